@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is the whole hot path for one layer: reshape_and_cache appends the new
+token of every sequence, paged_attention_decode attends each sequence's query
+over its paged K/V, and (when a partition size is set) the partition reduce
+merges split-K partials.  Inputs are seeded synthetic data with the shapes of
+the workload (workloads.py), resident in HBM before timing starts.  Several
+copies of the KV pool ("layers") are rotated so that consecutive steps never
+find their K/V in the 256 MB last-level cache.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  metric  achieved HBM bandwidth of the step (algorithmic bytes / step time)
+          and decode tokens/s/layer
+  roofline  the decode kernel alone, timed with HIP events on the stream it
+          runs on, against the MI355X HBM peak of 8 TB/s
+  cpu_baseline  the CPU oracle on this host, on a bounded sample of the same
+          workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "paged decode attention: achieved HBM TB/s (% of peak) + decode tokens/s/layer"
+PEAK_GBPS = 8000.0
+E = workloads.ELEM_BYTES
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(c, P: int) -> dict:
+    """Algorithmic bytes one decode launch (and its reduce) must move: each KV
+    head's rows once per group, Q in, O out, the table entries used, the
+    lengths, and for split-K the partials written once and read once."""
+    L = c.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * c.Hkv * c.D * E[c.cache_dtype] * 2
+    row = c.Hq * c.D * E[c.q_dtype]                  # one sequence's Q (or O)
+    table = 4 * int((-(-L // c.bs)).sum()) + 4 * c.S
+    n_multi, partials = 0, 0
+    if P > 0:
+        nparts = -(-L // P)
+        multi = nparts > 1
+        n_multi = int(multi.sum())
+        partials = int(nparts[multi].sum()) * c.Hq * (c.D + 2) * 4
+    # decode: K/V, Q, O of sequences it finishes, table, lengths, partials out
+    dec = kv + c.S * row + (c.S - n_multi) * row + table + partials
+    # reduce: partials in, O of the split sequences, lengths
+    red = partials + n_multi * row + 4 * c.S if P > 0 else 0
+    T = c.slot_mapping.size
+    append = T * c.Hkv * c.D * (E[c.src_dtype] + E[c.cache_dtype]) * 2 + 8 * T
+    return {"kv": kv, "decode_kernel": dec, "reduce_kernel": red,
+            "append": append, "step": dec + red + append}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_361_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launch_bytes: float):
+    """HBM bytes per decode launch from committed PMC summaries, if they were
+    taken from the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (ValueError, AttributeError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, budget_s: float = 15.0) -> dict:
+    """The CPU oracle (as it stands) on the first sequences of the workload:
+    a probe on a few sequences sizes a sample of about `budget_s`."""
+    import oracle
+    threads = oracle.max_threads()
+    kw = dict(q_dtype=c.q_dtype, cache_dtype=c.cache_dtype, scale=c.scale,
+              k_scale=c.k_scale, v_scale=c.v_scale, threads=threads)
+
+    def run(n):
+        sub_rows = np.arange(n * c.Hq, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                            rows=sub_rows, **kw)
+        return time.perf_counter() - t0
+
+    n = min(8, c.S)
+    t = run(n)
+    tok = int(c.seq_lens[:n].sum())
+    if t < budget_s / 4 and n < c.S:
+        per_tok = t / max(tok, 1)
+        target = budget_s / per_tok
+        cum = np.cumsum(c.seq_lens.astype(np.int64))
+        n = int(min(c.S, max(n, np.searchsorted(cum, target) + 1)))
+        t = run(n)
+        tok = int(c.seq_lens[:n].sum())
+    sub = c.copy()
+    sub.S = n
+    sub.seq_lens = c.seq_lens[:n]
+    sub.slot_mapping = c.slot_mapping[:0]
+    nbytes = decode_bytes(sub, 0)["decode_kernel"]
+    return {"value": round(nbytes / t / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle",
+            "tokens_per_s_per_layer": round(n / t, 2),
+            "seconds": round(t, 3),
+            "sample": "decode of the first %d of %d sequences (%d tokens, all %d query "
+                      "heads), gather + fp64 softmax attention, OpenMP over rows"
+                      % (n, c.S, tok, c.Hq)}
+
+
+def make_workload(args):
+    if args.config == 5:
+        c = workloads.config5(bs=args.bs)
+    else:
+        c = workloads.CONFIGS[args.config]()
+    P = c.partition_size if args.partition is None else args.partition
+    return c, P
+
+
+WORKLOAD_NAMES = {
+    1: "tiny fp32 paged decode: 4 seqs, L {7,16,33,100}, 4/4 heads, D 64, bs 16",
+    2: "Llama-2-13B-shaped MHA decode layer, fp16: 64 seqs, L~U[512,2048], 40/40 heads, "
+       "D 128, bs 16, +1 appended token/seq",
+    3: "Llama-3-8B-shaped GQA decode layer, bf16: 256 seqs, L~lognormal(median 1024, "
+       "sigma 1, cap 4096), 32 q / 8 kv heads, D 128, bs 16, +1 appended token/seq",
+    4: "long-context GQA decode, bf16, split-K: 8 seqs, L {32,48,64,64,96,96,128,128}K, "
+       "64 q / 8 kv heads, D 128, bs 32, partitions of 512",
+    5: "shared-prefix decode with fp8-e4m3 KV: 128 seqs, 1024-token shared prefix + "
+       "tails U[16,512], 32 q / 8 kv heads, D 128",
+}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--bs", type=int, default=16, help="block size for config 5")
+    ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-K partition size (default: the workload's)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="distinct KV pools rotated across steps")
+    ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU step "
+              "in this library (each GPU owns its sequences' blocks); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_361_amd as pkv
+
+    torch.cuda.set_device(0)
+    log("generating workload %d ..." % args.config)
+    t0 = time.perf_counter()
+    c, P = make_workload(args)
+    log("generated in %.1fs: %d seqs, %d tokens, pool %d blocks" %
+        (time.perf_counter() - t0, c.S, int(c.seq_lens.sum()), c.NB))
+
+    def dev(a, d):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    TD = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    query = dev(c.query, c.q_dtype)
+    tables = torch.from_numpy(c.block_tables).cuda()
+    lens = torch.from_numpy(c.seq_lens).cuda()
+    new_k = dev(c.new_key, c.src_dtype)
+    new_v = dev(c.new_value, c.src_dtype)
+    slots = torch.from_numpy(c.slot_mapping).cuda()
+    k0, v0 = dev(c.k_cache, c.cache_dtype), dev(c.v_cache, c.cache_dtype)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(1, args.layers) - 1)]
+    out = torch.empty(c.S, c.Hq, c.D, dtype=TD[c.q_dtype], device="cuda")
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.D, c.max_seq_len, P)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step(i, ev=None):
+        kc, vc = layers[i % len(layers)]
+        if c.slot_mapping.size:
+            if ev: ev[0].record(stream)
+            pkv.reshape_and_cache(new_k, new_v, kc, vc, slots, k_scale=c.k_scale,
+                                  v_scale=c.v_scale)
+        if ev: ev[1].record(stream)
+        pkv.paged_attention_decode(out, query, kc, vc, tables, lens, scale=c.scale,
+                                   max_seq_len=c.max_seq_len, k_scale=c.k_scale,
+                                   v_scale=c.v_scale, partition_size=P, workspace=ws,
+                                   algo=args.algo)
+        if ev: ev[2].record(stream)
+        if P > 0:
+            pkv.paged_attention_reduce(out, ws, lens, max_seq_len=c.max_seq_len,
+                                       partition_size=P)
+        if ev: ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log("warmup done (%d steps)" % args.warmup)
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    log("timed %d steps in %.3fs" % (K, t_total))
+
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    red_ms = np.array([e[2].elapsed_time(e[3]) for e in evs]) if P > 0 else np.zeros(K)
+    app_ms = (np.array([e[0].elapsed_time(e[1]) for e in evs]) if c.slot_mapping.size
+              else np.zeros(K))
+    nb = decode_bytes(c, P)
+    step_s = t_total / K
+    attn_s = float(np.mean(dec_ms + red_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    value = nb["step"] / step_s / 1e12
+    achieved = nb["decode_kernel"] / dec_s / 1e9
+    wl = WORKLOAD_NAMES[args.config]
+    if args.config == 5:
+        wl += ", bs %d" % c.bs
+    traffic = traffic_from_profiles("config%d" % args.config, nb["decode_kernel"])
+    res = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f16": "f16", "f32": "f32"}[c.q_dtype]
+                 + ("/fp8-kv" if c.cache_dtype == "fp8" else ""),
+        "data": "synthetic",
+        "config": {"workload": wl, "seqs": c.S, "tokens": int(c.seq_lens.sum()),
+                   "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.bs,
+                   "partition_size": P, "algo": args.algo, "kv_pools_rotated": len(layers)},
+        "pct_of_peak": round(100 * value * 1e3 / PEAK_GBPS, 2),
+        "tokens_per_s_per_layer": round(c.S / attn_s, 1),
+        "tokens_per_s_per_layer_with_append": round(c.S / step_s, 1),
+        "decode_us": round(dec_s * 1e6, 2),
+        "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                              round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
+        "reduce_us": round(float(np.mean(red_ms)) * 1e3, 2),
+        "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
+        "bytes_per_step": nb,
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_baseline == "on":
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(c)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+/*
+ * pagedkv.h - PagedAttention decode on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpagedkv.so.  Three operations, a workspace query and a status
+ * string.  All kernels are hand-written HIP for CDNA4.
+ *
+ * Sources (by page title and section):
+ *   [P4] "vLLM 推理引擎源码级拆解：PagedAttention 显存虚拟化、Continuous
+ *        Batching 调度与量化落地全指南" (chenxutan.com/d/5333)
+ *   [P2] "vLLM 深度实战" (chenxutan.com/d/3332)
+ *   [P1] "vLLM 0.5 深度拆解" (chenxutan.com/d/4924)
+ *   [P3] "vLLM 深度剖析：PagedAttention 与连续批处理如何撑起大模型推理"
+ *        (pgsm.cn/news/372185)
+ *
+ * Conventions for every call
+ *   - Pointers are device pointers owned by the caller, except where noted.
+ *     The library allocates, frees and synchronises nothing: each call
+ *     validates its arguments on the host, enqueues kernels on `stream` and
+ *     returns.  It keeps no state across calls, so calls are thread-safe.
+ *   - Tensors are dense, row-major (C order), with the shapes given below.
+ *     Device pointers must be 16-byte aligned.
+ *   - Argument errors are reported by a negative pkv_status before anything
+ *     is enqueued.  PKV_ERR_HIP means the kernel launch itself failed.
+ *   - Device-side contents (block ids, lengths, slots) are not validated on
+ *     the host; the kernels clamp them so that no access leaves the
+ *     buffers described here, and the documented preconditions say when the
+ *     result is meaningful.
+ *
+ * Pool layout ([P4] §2.3 declares [num_blocks, block_size, num_heads,
+ * head_dim]; the head axis is read as KV heads):
+ *   k_cache, v_cache : [num_blocks][block_size][num_kv_heads][head_dim]
+ *   element (b, o, h, d) sits at ((b*block_size + o)*num_kv_heads + h)*head_dim + d
+ *   Token t of sequence s lives in physical block block_tables[s][t / block_size]
+ *   at offset t % block_size ([P4] §2.2-2.3).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+    PKV_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    PKV_ERR_DTYPE = -3,       /* unknown dtype or an invalid dtype pairing */
+    PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel for this combination */
+    PKV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+    PKV_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
+    PKV_ERR_HIP = -7          /* the HIP runtime reported a launch error */
+} pkv_status;
+
+typedef enum {
+    PKV_F32 = 0,
+    PKV_F16 = 1,
+    PKV_BF16 = 2,
+    PKV_FP8_E4M3 = 3          /* OCP E4M3 (no inf, 0x7F/0xFF NaN, max 448) */
+} pkv_dtype;
+
+/* Kernel choice for pkv_paged_attention_decode. */
+typedef enum {
+    PKV_ALGO_AUTO = 0,        /* fastest kernel that supports the arguments */
+    PKV_ALGO_VALU = 1,        /* vector-ALU kernel: every supported combination */
+    PKV_ALGO_MFMA = 2         /* matrix-core kernel: f16/bf16 query, f16/bf16/fp8 cache */
+} pkv_algo;
+
+/*
+ * pkv_reshape_and_cache - store new tokens' K and V in their cache slots.
+ *
+ * [P4] §2.2: the next token goes into the free slot of the sequence's last
+ * block, or into a fresh block appended to its table; the caller's block
+ * bookkeeping turns that into one slot number per token,
+ * slot = physical_block * block_size + offset.  For every token i with
+ * 0 <= slot_mapping[i] < num_blocks*block_size and every KV head h:
+ *     k_cache[slot / block_size][slot % block_size][h][:] = conv(key[i][h][:])
+ *     v_cache[...same...]                                  = conv(value[i][h][:])
+ * Other slots are skipped.  conv is a bit copy when cache_dtype == src_dtype;
+ * for cache_dtype PKV_FP8_E4M3 it is e4m3(x / scale) with x the exact fp32
+ * value of the source element, an IEEE fp32 division, round to nearest even
+ * and saturation of finite overflow to +-448 (NaN stays NaN).  The pages give
+ * only an fp8 cache flag ([P1] §4.2, [P3] §6.1, [P4] §6.4); OCP E4M3 with
+ * one scale per tensor is this library's reading.
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim], src_dtype
+ *                 (PKV_F32, PKV_F16 or PKV_BF16)
+ *   k_cache, v_cache  pool as above, cache_dtype == src_dtype or PKV_FP8_E4M3
+ *   slot_mapping  [num_tokens] int64
+ *   k_scale, v_scale  fp8 scales (> 0, finite); ignored otherwise
+ * Precondition: slots are distinct (two tokens writing one slot race).
+ * num_tokens == 0 is a no-op.
+ */
+int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtype,
+                          void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                          const int64_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, float k_scale,
+                          float v_scale, hipStream_t stream);
+
+/*
+ * pkv_paged_attention_decode - one query token per sequence against its
+ * paged K/V ([P4] §2.3).
+ *
+ * For sequence s, query head hq and G = num_q_heads / num_kv_heads, with
+ * h = hq / G (consecutive query heads share a KV head; [P4] §2.3 names GQA
+ * and MQA) and L = seq_lens[s]:
+ *     z_t = scale * k_scale' * sum_d query[s][hq][d] * K[t][d],  t < L
+ *     out[s][hq][:] = sum_t softmax(z)_t * v_scale' * V[t][:]
+ * where K[t], V[t] are the stored rows of token t of (s, h), read through the
+ * block table, and k_scale' = k_scale, v_scale' = v_scale for an fp8 cache
+ * (1 otherwise).  Tokens t >= L never contribute, whatever the memory holds.
+ * The softmax is evaluated online (running max and running sum, as in the
+ * [P4] §2.3 kernel sketch), in fp32.  L <= 0 gives a zero row.
+ *
+ *   out           [num_seqs][num_q_heads][head_dim], dtype = q_dtype
+ *   query         [num_seqs][num_q_heads][head_dim], q_dtype
+ *   k_cache, v_cache  pool as above, cache_dtype
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
+ *                 only the first ceil(L / block_size) entries of a row are read
+ *   seq_lens      [num_seqs] int32
+ *   max_seq_len   host-side bound on seq_lens (sizes the split-K grid)
+ *
+ * Supported: (q_dtype, cache_dtype) in {(F32,F32), (F16,F16), (BF16,BF16),
+ * (F16,FP8), (BF16,FP8)}; head_dim 64 or 128; block_size 8, 16 or 32;
+ * num_q_heads % num_kv_heads == 0 with G <= 8 (PKV_ALGO_VALU) or G <= 16
+ * (PKV_ALGO_MFMA).
+ *
+ * Split-K (not on the pages; the merge follows from the running max/sum of
+ * the online softmax).  partition_size == 0: one pass, `out` is written and
+ * workspace may be NULL.  partition_size > 0 (a multiple of 16 and of
+ * block_size): the tokens of each sequence are cut into partitions
+ * [k*P, min(L, (k+1)*P)), P = partition_size; a sequence with at most one
+ * partition is finished here and its `out` rows written; for every other
+ * sequence the per-partition partials go to `workspace` and
+ * pkv_paged_attention_reduce must run next on the same stream.
+ *
+ * Workspace layout (bytes from pkv_decode_workspace_bytes), with
+ * P_max = ceil(max_seq_len / P) and n = num_seqs * num_q_heads * P_max:
+ *   offset 0             float max_logit[num_seqs][num_q_heads][P_max]
+ *                        m_k = max of z_t over partition k (natural-log units)
+ *   offset A = round_up(4n, 256)
+ *                        float exp_sum[num_seqs][num_q_heads][P_max]
+ *                        l_k = sum over partition k of exp(z_t - m_k)
+ *   offset 2A            float partial_out[num_seqs][num_q_heads][P_max][head_dim]
+ *                        o_k = sum over partition k of exp(z_t - m_k) * v_scale' * V[t]
+ *                        (not normalised by l_k)
+ * Entries of partitions k >= ceil(L/P), and of single-partition sequences,
+ * are not written.
+ *
+ * Preconditions for a meaningful result: 0 <= block ids < num_blocks and
+ * seq_lens[s] <= min(max_seq_len, max_blocks_per_seq * block_size).  Block
+ * ids outside the pool are clamped to num_blocks - 1 and lengths to that
+ * bound, so a bad table gives a wrong row but no stray access.
+ *
+ * algo selects the kernel (pkv_algo); an explicit choice that cannot serve
+ * the arguments returns PKV_ERR_UNSUPPORTED.
+ */
+int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
+                               const void* k_cache, const void* v_cache,
+                               pkv_dtype cache_dtype, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_seq_len, float scale, float k_scale,
+                               float v_scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t algo, hipStream_t stream);
+
+/*
+ * pkv_decode_workspace_bytes - bytes of workspace split-K decode needs
+ * (layout above); 0 when partition_size == 0 or a size is not positive.
+ * Host-only, touches no device.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t head_dim, int32_t max_seq_len,
+                                  int32_t partition_size);
+
+/*
+ * pkv_paged_attention_reduce - merge split-K partials (the second kernel of
+ * long-context decode).
+ *
+ * For every sequence s with K = ceil(L/P) >= 2 partitions and every query
+ * head hq, from the workspace written by pkv_paged_attention_decode (or any
+ * producer of the same layout):
+ *     M = max_k m_k
+ *     out[s][hq][:] = sum_k e^(m_k - M) o_k[:] / sum_k e^(m_k - M) l_k
+ * over k < K.  Rows of sequences with K <= 1 are left untouched (decode wrote
+ * them).  out_dtype is F32, F16 or BF16; the other arguments must match the
+ * decode call that produced the workspace.
+ */
+int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype,
+                               const void* workspace, size_t workspace_bytes,
+                               const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_seq_len, int32_t partition_size,
+                               hipStream_t stream);
+
+/* Static, human-readable name of a pkv_status value. */
+const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

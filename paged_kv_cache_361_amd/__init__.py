@@ -1,0 +1,170 @@
+"""PagedAttention decode for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libpagedkv.so, the C ABI declared in
+include/pagedkv.h.  The functions here only marshal torch tensors into
+pointers and sizes; every step of the computation runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.
+
+Operations (see include/pagedkv.h for the full contract):
+  reshape_and_cache       store new tokens' K/V in their pool slots
+  paged_attention_decode  one query token per sequence against the paged K/V
+  paged_attention_reduce  merge split-K partials (long contexts)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_build", "libpagedkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+ALGO = {"auto": 0, "valu": 1, "mfma": 2}
+
+_TORCH_DTYPE = {
+    torch.float32: PKV_F32,
+    torch.float16: PKV_F16,
+    torch.bfloat16: PKV_BF16,
+    torch.uint8: PKV_FP8_E4M3,
+    torch.float8_e4m3fn: PKV_FP8_E4M3,
+}
+
+
+class PagedKVError(RuntimeError):
+    """A libpagedkv call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (%d)" % (fn, status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libpagedkv.so is not built (%s); run `python -c \"import "
+            "__graft_entry__; __graft_entry__.build()\"` or "
+            "`python paged_kv_cache_361_amd/build.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    I = ctypes.c_int
+    lib.pkv_reshape_and_cache.argtypes = [P, P, I, P, P, I, P, I32, I32, I32, I32, I32,
+                                          F, F, P]
+    lib.pkv_reshape_and_cache.restype = I
+    lib.pkv_paged_attention_decode.argtypes = [P, P, I, P, P, I, P, I32, P, I32, I32, I32,
+                                               I32, I32, I32, I32, F, F, F, I32, P, SZ,
+                                               I32, P]
+    lib.pkv_paged_attention_decode.restype = I
+    lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.pkv_decode_workspace_bytes.restype = SZ
+    lib.pkv_paged_attention_reduce.argtypes = [P, I, P, SZ, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_paged_attention_reduce.restype = I
+    lib.pkv_status_string.argtypes = [I]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return _load().pkv_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _TORCH_DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported tensor dtype %s" % t.dtype) from None
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PagedKVError(fn, rc)
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, *,
+                      k_scale: float = 1.0, v_scale: float = 1.0,
+                      stream=None) -> None:
+    """key/value [T, Hkv, D]; caches [NB, bs, Hkv, D]; slot_mapping [T] int64."""
+    T, Hkv, D = key.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    rc = _load().pkv_reshape_and_cache(
+        _ptr(key), _ptr(value), _dtype_code(key), _ptr(k_cache), _ptr(v_cache),
+        _dtype_code(k_cache), _ptr(slot_mapping), T, Hkv, D, bs, NB,
+        float(k_scale), float(v_scale), _stream(stream))
+    _check("pkv_reshape_and_cache", rc)
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                           max_seq_len: int, partition_size: int) -> int:
+    return int(_load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                   max_seq_len, partition_size))
+
+
+def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, block_tables: torch.Tensor,
+                           seq_lens: torch.Tensor, *, scale: float, max_seq_len: int,
+                           k_scale: float = 1.0, v_scale: float = 1.0,
+                           partition_size: int = 0,
+                           workspace: Optional[torch.Tensor] = None,
+                           algo: str = "auto", stream=None) -> None:
+    """out, query [S, Hq, D]; caches [NB, bs, Hkv, D]; block_tables [S, max_blocks]
+    int32; seq_lens [S] int32.  With partition_size > 0, call
+    paged_attention_reduce next with the same workspace."""
+    S, Hq, D = query.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _load().pkv_paged_attention_decode(
+        _ptr(out), _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(v_cache),
+        _dtype_code(k_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        S, Hq, Hkv, D, bs, NB, int(max_seq_len), float(scale), float(k_scale),
+        float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, ALGO[algo],
+        _stream(stream))
+    _check("pkv_paged_attention_decode", rc)
+
+
+def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor,
+                           seq_lens: torch.Tensor, *, max_seq_len: int,
+                           partition_size: int, stream=None) -> None:
+    """Merges the split-K partials in `workspace` into out [S, Hq, D]."""
+    S, Hq, D = out.shape
+    rc = _load().pkv_paged_attention_reduce(
+        _ptr(out), _dtype_code(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(seq_lens), S, Hq, D,
+        int(max_seq_len), int(partition_size), _stream(stream))
+    _check("pkv_paged_attention_reduce", rc)
+
+
+def allocate_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
+                       partition_size: int, device="cuda") -> Optional[torch.Tensor]:
+    """A byte tensor large enough for split-K decode (None when not needed)."""
+    n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,221 @@
+// api.hip - the C ABI of libpagedkv (declared in include/pagedkv.h).
+//
+// Host-side argument validation, workspace layout and kernel dispatch.  No
+// call allocates, frees or synchronises; every error is returned before
+// anything is enqueued.
+#include "pagedkv.h"
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace pkv;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Partition count and workspace pieces for split-K.
+struct WsLayout {
+    int P_max = 0;
+    size_t off_l = 0, off_o = 0, bytes = 0;
+};
+
+inline bool ws_layout(int32_t S, int32_t Hq, int32_t D, int32_t max_seq_len,
+                      int32_t P, WsLayout* w) {
+    if (S <= 0 || Hq <= 0 || D <= 0 || max_seq_len <= 0 || P <= 0) return false;
+    w->P_max = (int)((max_seq_len + (int64_t)P - 1) / P);
+    const size_t n = (size_t)S * (size_t)Hq * (size_t)w->P_max;
+    w->off_l = round_up(n * 4, 256);
+    w->off_o = 2 * w->off_l;
+    w->bytes = w->off_o + n * (size_t)D * 4;
+    return true;
+}
+
+inline bool supported_block_size(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
+
+inline bool valid_decode_types(int qdt, int cdt) {
+    if (qdt == PKV_FP8_E4M3) return false;
+    if (cdt == PKV_FP8_E4M3) return qdt == PKV_F16 || qdt == PKV_BF16;
+    return qdt == cdt;
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+    switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case PKV_ERR_DTYPE: return "unknown dtype or invalid dtype pairing";
+    case PKV_ERR_UNSUPPORTED: return "no kernel for this combination";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case PKV_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtype,
+                          void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                          const int64_t* slot_mapping, int32_t num_tokens,
+                          int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, float k_scale,
+                          float v_scale, hipStream_t stream) {
+    if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+    if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+    if (cache_dtype != src_dtype && cache_dtype != PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+        num_blocks <= 0)
+        return PKV_ERR_SHAPE;
+    if (head_dim % 8 != 0) return PKV_ERR_UNSUPPORTED;
+    if (cache_dtype == PKV_FP8_E4M3 &&
+        !(k_scale > 0.0f && v_scale > 0.0f && k_scale < INFINITY && v_scale < INFINITY))
+        return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)slot_mapping & 7u))
+        return PKV_ERR_ALIGN;
+    WriteParams p;
+    p.key = key;
+    p.value = value;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.slot_mapping = slot_mapping;
+    p.num_slots = (int64_t)num_blocks * block_size;
+    p.T = num_tokens;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    p.src_bytes = src_dtype == PKV_F32 ? 4 : 2;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    return launch_status(launch_reshape_and_cache(src_dtype, cache_dtype, p, stream));
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition_size) {
+    WsLayout w;
+    if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w)) return 0;
+    return w.bytes;
+}
+
+int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
+                               const void* k_cache, const void* v_cache,
+                               pkv_dtype cache_dtype, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_seq_len, float scale, float k_scale,
+                               float v_scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t algo, hipStream_t stream) {
+    if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+    if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
+        partition_size < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PKV_ERR_SHAPE;
+    if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA) return PKV_ERR_UNSUPPORTED;
+    if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+    if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+        return PKV_ERR_SHAPE;
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u))
+        return PKV_ERR_ALIGN;
+
+    DecodeParams p;
+    p.out = out;
+    p.q = query;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.lens = seq_lens;
+    p.ws_m = p.ws_l = p.ws_o = nullptr;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    p.G = num_q_heads / num_kv_heads;
+    p.bs = block_size;
+    p.NB = num_blocks;
+    p.max_blocks = max_blocks_per_seq;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    p.len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
+    p.P = partition_size;
+    p.P_max = 1;
+    const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    p.scale_log2 = scale * ks * kLog2e;
+    p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    if (partition_size > 0) {
+        WsLayout w;
+        if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w))
+            return PKV_ERR_SHAPE;
+        if (!workspace) return PKV_ERR_WORKSPACE;
+        if (workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+        p.P_max = w.P_max;
+        p.ws_m = (float*)workspace;
+        p.ws_l = (float*)((char*)workspace + w.off_l);
+        p.ws_o = (float*)((char*)workspace + w.off_o);
+    }
+    const int64_t units = (int64_t)num_seqs * p.P_max * num_kv_heads;
+    if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
+
+    const bool mfma_ok = decode_mfma_supported(q_dtype, cache_dtype, head_dim, p.G);
+    const bool valu_ok = decode_valu_supported(q_dtype, cache_dtype, head_dim, p.G);
+    if (algo == PKV_ALGO_MFMA || (algo == PKV_ALGO_AUTO && mfma_ok)) {
+        if (!mfma_ok) return PKV_ERR_UNSUPPORTED;
+        return launch_status(launch_decode_mfma(q_dtype, cache_dtype, p, stream));
+    }
+    if (!valu_ok) return PKV_ERR_UNSUPPORTED;
+    return launch_status(launch_decode_valu(q_dtype, cache_dtype, p, stream));
+}
+
+int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* workspace,
+                               size_t workspace_bytes, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                               int32_t max_seq_len, int32_t partition_size,
+                               hipStream_t stream) {
+    if (!valid_dtype(out_dtype) || out_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
+    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 ||
+        partition_size <= 0)
+        return PKV_ERR_SHAPE;
+    if (partition_size % 16 != 0) return PKV_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    WsLayout w;
+    if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w))
+        return PKV_ERR_SHAPE;
+    if (!out || !seq_lens) return PKV_ERR_NULL;
+    if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
+    if (!aligned16(out) || !aligned16(workspace) || ((uintptr_t)seq_lens & 3u))
+        return PKV_ERR_ALIGN;
+    if ((int64_t)num_seqs * num_q_heads > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
+    ReduceParams p;
+    p.out = out;
+    p.ws_m = (const float*)workspace;
+    p.ws_l = (const float*)((const char*)workspace + w.off_l);
+    p.ws_o = (const float*)((const char*)workspace + w.off_o);
+    p.lens = seq_lens;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.D = head_dim;
+    p.P = partition_size;
+    p.P_max = w.P_max;
+    p.len_cap = max_seq_len;
+    return launch_status(launch_reduce(out_dtype, p, stream));
+}
+
+}  // extern "C"

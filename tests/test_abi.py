@@ -1,0 +1,126 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/pagedkv.h declares, and rejects bad arguments on the host before any
+launch.  The rejected calls pass fake (but aligned, non-null) device
+addresses; every one of them fails validation, so nothing is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_361_amd as pkv
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_cache_361_amd import build
+        build.build()
+    return pkv
+
+
+@pytest.fixture(scope="module")
+def lib(pkv):
+    return pkv._load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pkv_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_three_operations():
+    syms = declared_symbols()
+    for s in ("pkv_reshape_and_cache", "pkv_paged_attention_decode",
+              "pkv_paged_attention_reduce", "pkv_decode_workspace_bytes",
+              "pkv_status_string"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+
+
+def test_status_strings(pkv):
+    assert pkv.status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert pkv.status_string(code) != "unknown status"
+
+
+def test_workspace_bytes_layout(pkv):
+    S, Hq, D, L, P = 8, 64, 128, 131072, 512
+    P_max = -(-L // P)
+    n = S * Hq * P_max
+    a = -(-4 * n // 256) * 256
+    assert pkv.decode_workspace_bytes(S, Hq, D, L, P) == 2 * a + 4 * n * D
+    assert pkv.decode_workspace_bytes(S, Hq, D, L, 0) == 0
+    assert pkv.decode_workspace_bytes(0, Hq, D, L, P) == 0
+
+
+FAKE = 1 << 20     # aligned, non-null; never dereferenced (calls fail first)
+
+
+def decode_args(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=2, k=FAKE, v=FAKE, cdt=2, tables=FAKE,
+             max_blocks=16, lens=FAKE, S=4, Hq=32, Hkv=8, D=128, bs=16, NB=100,
+             max_len=256, scale=0.1, ks=1.0, vs=1.0, P=0, ws=None, ws_bytes=0,
+             algo=0, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "qdt", "k", "v", "cdt", "tables", "max_blocks",
+                           "lens", "S", "Hq", "Hkv", "D", "bs", "NB", "max_len", "scale",
+                           "ks", "vs", "P", "ws", "ws_bytes", "algo", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), -1), (dict(q=None), -1), (dict(tables=None), -1), (dict(lens=None), -1),
+    (dict(qdt=7), -3), (dict(qdt=3), -3), (dict(qdt=1, cdt=2), -3), (dict(qdt=0, cdt=3), -3),
+    (dict(S=0), -2), (dict(Hq=30), -2), (dict(Hkv=0), -2), (dict(max_len=0), -2),
+    (dict(max_blocks=0), -2), (dict(NB=0), -2), (dict(P=-16), -2),
+    (dict(P=24), -2), (dict(bs=32, P=48), -2),
+    (dict(bs=64), -4), (dict(bs=12), -4), (dict(D=96), -4), (dict(Hq=64, Hkv=2), -4),
+    (dict(algo=5), -4), (dict(algo=1, Hq=128, Hkv=8), -4),
+    (dict(out=FAKE + 8), -6), (dict(k=FAKE + 4), -6), (dict(lens=FAKE + 2), -6),
+    (dict(P=512), -5), (dict(P=512, ws=FAKE, ws_bytes=100), -5),
+    (dict(scale=float("nan")), -2),
+])
+def test_decode_rejects_bad_arguments(lib, kw, status):
+    assert lib.pkv_paged_attention_decode(*decode_args(**kw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=3), -3), (dict(src=1, cache=2), -3), (dict(src=9), -3),
+    (dict(T=-1), -2), (dict(Hkv=0), -2), (dict(bs=0), -2), (dict(NB=0), -2),
+    (dict(cache=3, ks=0.0), -2), (dict(cache=3, vs=float("inf")), -2),
+    (dict(key=None), -1), (dict(slots=None), -1), (dict(key=FAKE + 8), -6),
+    (dict(slots=FAKE + 4), -6), (dict(D=100), -4),
+])
+def test_cache_write_rejects_bad_arguments(lib, kw, status):
+    a = dict(key=FAKE, value=FAKE, src=2, kc=FAKE, vc=FAKE, cache=2, slots=FAKE, T=4,
+             Hkv=8, D=128, bs=16, NB=10, ks=1.0, vs=1.0, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("key", "value", "src", "kc", "vc", "cache", "slots", "T", "Hkv",
+                           "D", "bs", "NB", "ks", "vs", "stream")]
+    assert lib.pkv_reshape_and_cache(*args) == status
+
+
+def test_cache_write_zero_tokens_is_a_noop(lib):
+    assert lib.pkv_reshape_and_cache(None, None, 2, None, None, 2, None, 0, 8, 128, 16, 10,
+                                     1.0, 1.0, None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(odt=3), -3), (dict(odt=9), -3), (dict(S=0), -2), (dict(P=0), -2),
+    (dict(P=24), -2), (dict(D=96), -4), (dict(out=None), -1), (dict(lens=None), -1),
+    (dict(ws=None), -5), (dict(ws_bytes=10), -5), (dict(out=FAKE + 4), -6),
+])
+def test_reduce_rejects_bad_arguments(lib, pkv, kw, status):
+    a = dict(out=FAKE, odt=2, ws=FAKE, ws_bytes=1 << 40, lens=FAKE, S=8, Hq=64, D=128,
+             max_len=4096, P=512, stream=None)
+    a.update(kw)
+    args = [a[k] for k in ("out", "odt", "ws", "ws_bytes", "lens", "S", "Hq", "D",
+                           "max_len", "P", "stream")]
+    assert lib.pkv_paged_attention_reduce(*args) == status

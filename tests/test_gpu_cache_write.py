@@ -1,0 +1,86 @@
+"""reshape_and_cache on the GPU against the oracle writer: bit-exact.
+
+Covers the same-type bit copy for every cache type, the E4M3 quantiser over
+every bf16 and f16 bit pattern at three scales, skipped slots (negative, past
+the pool) and bytes outside the written slots (canary)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_361_amd as pkv
+import workloads
+from gpu_case import cache_bytes, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_both(key, value, src, cache, kc0, vc0, slots, ks=1.0, vs=1.0):
+    kd, vd = to_dev(kc0, cache), to_dev(vc0, cache)
+    pkv.reshape_and_cache(to_dev(key, src), to_dev(value, src), kd, vd,
+                          torch.from_numpy(slots).cuda(), k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ko, vo = kc0.copy(), vc0.copy()
+    oracle.reshape_and_cache(key, value, ko, vo, slots, src_dtype=src, cache_dtype=cache,
+                             k_scale=ks, v_scale=vs)
+    return cache_bytes(kd), cache_bytes(vd), ko.view(np.uint8), vo.view(np.uint8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("Hkv,D", [(8, 128), (40, 128), (4, 64), (1, 64)])
+def test_bit_copy_matches_oracle(dtype, Hkv, D):
+    rng = np.random.default_rng(Hkv * 1000 + D)
+    NB, bs, T = 37, 16, 50
+    key = workloads.draw(rng, (T, Hkv, D), dtype)
+    value = workloads.draw(rng, (T, Hkv, D), dtype)
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[5] = -1
+    slots[9] = NB * bs
+    slots[11] = -(1 << 40)
+    kc0 = workloads.draw(rng, (NB, bs, Hkv, D), dtype)    # canary: random bytes
+    vc0 = workloads.draw(rng, (NB, bs, Hkv, D), dtype)
+    kg, vg, ko, vo = _run_both(key, value, dtype, dtype, kc0, vc0, slots)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [1.0, 0.0103, 3.7])
+def test_fp8_quantiser_every_bit_pattern(src, scale):
+    """All 65536 source bit patterns (NaN and inf included) through the GPU
+    and the oracle writer; the E4M3 bytes must match exactly."""
+    Hkv, D = 8, 128
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    T = 65536 // (Hkv * D)
+    if src == "bf16":
+        x = bits.reshape(T, Hkv, D)
+    else:
+        x = bits.view(np.float16).reshape(T, Hkv, D)
+    y = np.ascontiguousarray(x[::-1])          # a different order for V
+    NB, bs = T, 1
+    slots = np.arange(T, dtype=np.int64)
+    kc0 = np.full((NB, bs, Hkv, D), 0x5A, np.uint8)
+    vc0 = np.full((NB, bs, Hkv, D), 0x5A, np.uint8)
+    kg, vg, ko, vo = _run_both(x, y, src, "fp8", kc0, vc0, slots, scale, scale * 0.5)
+    assert np.array_equal(kg, ko)
+    assert np.array_equal(vg, vo)
+
+
+def test_fp8_quantiser_f32_sample():
+    rng = np.random.default_rng(5)
+    T, Hkv, D = 300, 2, 64
+    x = (rng.standard_normal((T, Hkv, D)) * np.exp2(rng.integers(-20, 12, (T, Hkv, D)))).astype(np.float32)
+    x[0, 0, :4] = [np.inf, -np.inf, np.nan, 0.0]
+    y = -x
+    slots = rng.permutation(T).astype(np.int64)
+    kc0 = np.zeros((T, 1, Hkv, D), np.uint8)
+    vc0 = np.zeros((T, 1, Hkv, D), np.uint8)
+    kg, vg, ko, vo = _run_both(x, y, "f32", "fp8", kc0, vc0, slots, 0.37, 1.0)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_config_append_matches_oracle(cfg):
+    c = workloads.config5(bs=16) if cfg == 5 else workloads.CONFIGS[cfg]()
+    kg, vg, ko, vo = _run_both(c.new_key, c.new_value, c.src_dtype, c.cache_dtype,
+                               c.k_cache, c.v_cache, c.slot_mapping, c.k_scale, c.v_scale)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
