@@ -125,6 +125,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
         partition_size < 0)
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (num_kv_heads > 4096) return PKV_ERR_SHAPE;   // keeps in-block offsets 32-bit
     if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PKV_ERR_SHAPE;
     if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA) return PKV_ERR_UNSUPPORTED;
     if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;

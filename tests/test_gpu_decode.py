@@ -227,7 +227,6 @@ def test_identical_keys_give_mean_of_values(algo):
         k0 = c.k_cache[c.block_tables[s, 0], 0].copy()
         for j in range(-(-L // c.bs)):
             c.k_cache[c.block_tables[s, j]] = k0
-        c.new_key[s] = k0
     out = gpu_run(c, algo)
     kc, vc = oracle_caches(c)
     for s in range(c.S):
