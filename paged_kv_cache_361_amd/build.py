@@ -2,8 +2,9 @@
 
 Each .hip file under csrc/ is compiled with hipcc for gfx950 only, in
 parallel, then linked into paged_kv_cache_361_amd/_build/libpagedkv.so.
-Packed-fp32 instructions are disabled and fp32 division stays correctly
-rounded (the fp8 cache writer depends on it).
+Packed-fp32 instructions are disabled, fp32 division stays correctly
+rounded (the fp8 cache writer depends on it) and matrix-core results are
+kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -25,6 +26,9 @@ CFLAGS = [
     "-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-rdc",
+    # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+    # works on them in place instead of copying them out of AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]
