@@ -44,7 +44,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_bytes(c, P: int) -> dict:
+def balanced_split(lens: np.ndarray, Hkv: int, nW: int):
+    """The balanced split's pieces, replayed on the host: the streams
+    (sequence, KV head) of 16-token tiles laid end to end and cut into chunks
+    by the guided schedule (nW chunks of max(1, 3A/5) tiles, nW of
+    max(1, A/4), then max(4, A/10), A = T / nW).  Returns (number of streams
+    spread over several chunks, partial entries they write per query head)."""
+    nt = -(-np.maximum(lens.astype(np.int64), 0) // 16)
+    T = int(nt.sum()) * Hkv
+    if T == 0:
+        return 0, 0
+    A = T // nW
+    C1, C2, C3 = max(1, A * 3 // 5), max(1, A // 4), max(4, A // 10)
+    e1, e2 = min(nW * C1, T), min(nW * (C1 + C2), T)
+
+    def chunk_of(x):
+        return np.where(x < e1, x // C1,
+                        np.where(x < e2, nW + (x - e1) // C2, 2 * nW + (x - e2) // C3))
+
+    g0 = (np.repeat(np.cumsum(nt) - nt, Hkv) * Hkv
+          + np.tile(np.arange(Hkv), lens.size) * np.repeat(nt, Hkv))
+    g1 = g0 + np.repeat(nt, Hkv)
+    live = g1 > g0
+    c0 = chunk_of(g0)
+    c1 = chunk_of(np.maximum(g1 - 1, 0))
+    split = live & (c1 > c0)
+    return int(split.sum()), int((c1 - c0 + 1)[split].sum())
+
+
+def decode_bytes(c, P: int, nW: int = 0) -> dict:
     """Algorithmic bytes one decode launch (and its reduce) must move: each KV
     head's rows once per group, Q in, O out, the table entries used, the
     lengths, and for split-K the partials written once and read once."""
@@ -58,10 +86,17 @@ def decode_bytes(c, P: int) -> dict:
         multi = nparts > 1
         n_multi = int(multi.sum())
         partials = int(nparts[multi].sum()) * c.Hq * (c.D + 2) * 4
+    elif P < 0:
+        # a split (sequence, KV head) stream writes one entry per piece for each
+        # query head of its group; its G output rows come from the reduce
+        split_streams, entries = balanced_split(L, c.Hkv, nW)
+        n_multi = split_streams / c.Hkv          # in units of whole sequences
+        partials = entries * c.G * (c.D + 2) * 4
     # decode: K/V, Q, O of sequences it finishes, table, lengths, partials out
     dec = kv + c.S * row + (c.S - n_multi) * row + table + partials
     # reduce: partials in, O of the split sequences, lengths
-    red = partials + n_multi * row + 4 * c.S if P > 0 else 0
+    red = partials + int(n_multi * row) + 4 * c.S if P != 0 else 0
+    dec = int(dec)
     T = c.slot_mapping.size
     append = T * c.Hkv * c.D * (E[c.src_dtype] + E[c.cache_dtype]) * 2 + 8 * T
     return {"kv": kv, "decode_kernel": dec, "reduce_kernel": red,
@@ -166,7 +201,8 @@ def main() -> int:
     ap.add_argument("--bs", type=int, default=16, help="block size for config 5")
     ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition size (default: the workload's)")
+                    help="split-K partition size: 0 one pass, P > 0 fixed partitions, "
+                         "-1 the balanced split (default: the workload's)")
     ap.add_argument("--layers", type=int, default=4,
                     help="distinct KV pools rotated across steps")
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
@@ -206,7 +242,7 @@ def main() -> int:
     k0, v0 = dev(c.k_cache, c.cache_dtype), dev(c.v_cache, c.cache_dtype)
     layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(1, args.layers) - 1)]
     out = torch.empty(c.S, c.Hq, c.D, dtype=TD[c.q_dtype], device="cuda")
-    ws = pkv.allocate_workspace(c.S, c.Hq, c.D, c.max_seq_len, P)
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
     stream = torch.cuda.current_stream()
 
     if args.copy_calib_mib:
@@ -229,9 +265,9 @@ def main() -> int:
                                    v_scale=c.v_scale, partition_size=P, workspace=ws,
                                    algo=args.algo)
         if ev: ev[2].record(stream)
-        if P > 0:
-            pkv.paged_attention_reduce(out, ws, lens, max_seq_len=c.max_seq_len,
-                                       partition_size=P)
+        if P != 0:
+            pkv.paged_attention_reduce(out, ws, lens, num_kv_heads=c.Hkv,
+                                       max_seq_len=c.max_seq_len, partition_size=P)
         if ev: ev[3].record(stream)
 
     for i in range(args.warmup):
@@ -250,10 +286,13 @@ def main() -> int:
     log("timed %d steps in %.3fs" % (K, t_total))
 
     dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    red_ms = np.array([e[2].elapsed_time(e[3]) for e in evs]) if P > 0 else np.zeros(K)
+    red_ms = np.array([e[2].elapsed_time(e[3]) for e in evs]) if P != 0 else np.zeros(K)
     app_ms = (np.array([e[0].elapsed_time(e[1]) for e in evs]) if c.slot_mapping.size
               else np.zeros(K))
-    nb = decode_bytes(c, P)
+    nW = 0
+    if P < 0:     # the grid size the library chose, from the workspace header
+        nW = int(ws[:16].cpu().numpy().view(np.int32)[1])
+    nb = decode_bytes(c, P, nW)
     step_s = t_total / K
     attn_s = float(np.mean(dec_ms + red_ms)) / 1e3
     dec_s = float(np.mean(dec_ms)) / 1e3
@@ -279,7 +318,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl, "seqs": c.S, "tokens": int(c.seq_lens.sum()),
                    "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.bs,
-                   "partition_size": P, "algo": args.algo, "kv_pools_rotated": len(layers)},
+                   "partition_size": P if P >= 0 else "balanced", "algo": args.algo,
+                   "kv_pools_rotated": len(layers)},
         "pct_of_peak": round(100 * value * 1e3 / PEAK_GBPS, 2),
         "tokens_per_s_per_layer": round(c.S / attn_s, 1),
         "tokens_per_s_per_layer_with_append": round(c.S / step_s, 1),
@@ -287,6 +327,7 @@ def main() -> int:
         "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                               round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
         "reduce_us": round(float(np.mean(red_ms)) * 1e3, 2),
+        "balanced_grid_waves": nW if P < 0 else None,
         "append_us": round(float(np.mean(app_ms)) * 1e3, 2),
         "bytes_per_step": nb,
         "roofline": {"bound": "hbm", "kernel": "paged_attention_decode",

@@ -63,6 +63,10 @@ typedef enum {
     PKV_FP8_E4M3 = 3          /* OCP E4M3 (no inf, 0x7F/0xFF NaN, max 448) */
 } pkv_dtype;
 
+/* partition_size value selecting the balanced split (see
+ * pkv_paged_attention_decode). */
+#define PKV_PARTITION_BALANCED (-1)
+
 /* Kernel choice for pkv_paged_attention_decode. */
 typedef enum {
     PKV_ALGO_AUTO = 0,        /* fastest kernel that supports the arguments */
@@ -131,26 +135,50 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  * (PKV_ALGO_MFMA).
  *
  * Split-K (not on the pages; the merge follows from the running max/sum of
- * the online softmax).  partition_size == 0: one pass, `out` is written and
- * workspace may be NULL.  partition_size > 0 (a multiple of 16 and of
- * block_size): the tokens of each sequence are cut into partitions
- * [k*P, min(L, (k+1)*P)), P = partition_size; a sequence with at most one
- * partition is finished here and its `out` rows written; for every other
- * sequence the per-partition partials go to `workspace` and
- * pkv_paged_attention_reduce must run next on the same stream.
+ * the online softmax).  Three modes, chosen by partition_size:
  *
- * Workspace layout (bytes from pkv_decode_workspace_bytes), with
- * P_max = ceil(max_seq_len / P) and n = num_seqs * num_q_heads * P_max:
- *   offset 0             float max_logit[num_seqs][num_q_heads][P_max]
- *                        m_k = max of z_t over partition k (natural-log units)
- *   offset A = round_up(4n, 256)
- *                        float exp_sum[num_seqs][num_q_heads][P_max]
- *                        l_k = sum over partition k of exp(z_t - m_k)
- *   offset 2A            float partial_out[num_seqs][num_q_heads][P_max][head_dim]
- *                        o_k = sum over partition k of exp(z_t - m_k) * v_scale' * V[t]
- *                        (not normalised by l_k)
- * Entries of partitions k >= ceil(L/P), and of single-partition sequences,
- * are not written.
+ *   0      one pass: `out` is written and workspace may be NULL.
+ *
+ *   P > 0  fixed partitions (P a multiple of 16 and of block_size): the
+ *          tokens of each sequence are cut into partitions
+ *          [k*P, min(L, (k+1)*P)); a sequence with at most one partition is
+ *          finished here and its `out` rows written; for every other sequence
+ *          the per-partition partials go to `workspace` and
+ *          pkv_paged_attention_reduce must run next on the same stream.
+ *          Workspace layout, with P_max = ceil(max_seq_len / P) and
+ *          n = num_seqs * num_q_heads * P_max:
+ *            offset 0             float max_logit[num_seqs][num_q_heads][P_max]
+ *            offset A = round_up(4n, 256)
+ *                                 float exp_sum[num_seqs][num_q_heads][P_max]
+ *            offset 2A            float partial_out[num_seqs][num_q_heads][P_max][head_dim]
+ *          For partition k: m_k is a reference logit (natural-log units, at
+ *          most the partition's largest z_t and within 8 ln 2 of it),
+ *          l_k = sum over the partition of exp(z_t - m_k) and
+ *          o_k = sum of exp(z_t - m_k) * v_scale' * V[t] (not normalised).
+ *          Entries of partitions k >= ceil(L/P), and of single-partition
+ *          sequences, are not written.
+ *
+ *   PKV_PARTITION_BALANCED (-1)
+ *          balanced split (matrix-core kernel only, so f16/bf16 queries;
+ *          num_seqs <= 8192): the whole batch's work -- every (sequence, KV
+ *          head) pair's tokens in 16-token tiles, laid end to end -- is cut
+ *          into chunks by a guided schedule (large chunks first, small ones
+ *          last) and spread over a persistent grid of as many wavefronts as
+ *          the GPU holds at once (at most 2048), which take chunks in order
+ *          from a counter, so that ragged lengths and uneven wavefront speeds
+ *          cost no load balance.  Two kernels are enqueued: a small plan
+ *          kernel that prepares the workspace, then the decode kernel.  A
+ *          (sequence, KV head) pair that falls into one chunk is finished
+ *          here; for every other pair each chunk's piece leaves its partials
+ *          in `workspace` (layout private to the library: a header, the tile
+ *          prefix of the sequences, then (m, l, o) entries as above, two per
+ *          query head of the group per chunk), and pkv_paged_attention_reduce
+ *          must run next on the same stream with partition_size =
+ *          PKV_PARTITION_BALANCED; it also writes the zero rows of sequences
+ *          with L <= 0.  The workspace needs no initialisation.  Requires
+ *          num_seqs * num_kv_heads * ceil(max_seq_len / 16) < 2^31.
+ *
+ * pkv_decode_workspace_bytes gives the workspace size for either split mode.
  *
  * Preconditions for a meaningful result: 0 <= block ids < num_blocks and
  * seq_lens[s] <= min(max_seq_len, max_blocks_per_seq * block_size).  Block
@@ -174,32 +202,39 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
 
 /*
  * pkv_decode_workspace_bytes - bytes of workspace split-K decode needs
- * (layout above); 0 when partition_size == 0 or a size is not positive.
- * Host-only, touches no device.
+ * (layouts above) for partition_size > 0 or PKV_PARTITION_BALANCED; 0 when
+ * partition_size == 0, a size is not positive or num_q_heads is not a
+ * multiple of num_kv_heads.  The balanced size does not depend on the
+ * lengths: a header, num_seqs + 1 words, and 2 * (5 * 2048 + 8) entries of
+ * head_dim + 2 floats per query head of the group.  Host-only, touches no
+ * device.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                  int32_t head_dim, int32_t max_seq_len,
-                                  int32_t partition_size);
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition_size);
 
 /*
  * pkv_paged_attention_reduce - merge split-K partials (the second kernel of
  * long-context decode).
  *
- * For every sequence s with K = ceil(L/P) >= 2 partitions and every query
- * head hq, from the workspace written by pkv_paged_attention_decode (or any
- * producer of the same layout):
+ * For every row (sequence s, query head hq) whose work was split, from the
+ * workspace written by pkv_paged_attention_decode with the same
+ * partition_size, seq_lens and sizes:
  *     M = max_k m_k
- *     out[s][hq][:] = sum_k e^(m_k - M) o_k[:] / sum_k e^(m_k - M) l_k
- * over k < K.  Rows of sequences with K <= 1 are left untouched (decode wrote
- * them).  out_dtype is F32, F16 or BF16; the other arguments must match the
- * decode call that produced the workspace.
+ *     out[s][hq][:] = sum_k e^(m_k - M) o_k / sum_k e^(m_k - M) l_k
+ * over the row's entries k (fixed partitions: k < ceil(L/P); balanced: the
+ * pieces of the row's KV-head stream).  Rows that decode finished are left
+ * untouched.  Fixed partitions: the workspace may also come from any other
+ * producer of the documented layout.  Balanced: the workspace must hold what
+ * the decode call wrote (for the same num_kv_heads); if its header does not
+ * match, nothing is written.  out_dtype is F32, F16 or BF16.
  */
 int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype,
                                const void* workspace, size_t workspace_bytes,
                                const int32_t* seq_lens, int32_t num_seqs,
-                               int32_t num_q_heads, int32_t head_dim,
-                               int32_t max_seq_len, int32_t partition_size,
-                               hipStream_t stream);
+                               int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seq_len,
+                               int32_t partition_size, hipStream_t stream);
 
 /* Static, human-readable name of a pkv_status value. */
 const char* pkv_status_string(int status);

@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(_HERE, "_build", "libpagedkv.so")
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 ALGO = {"auto": 0, "valu": 1, "mfma": 2}
+# partition_size selecting the balanced split (the whole batch's work cut
+# evenly over a persistent grid; reduce must follow with the same value)
+PARTITION_BALANCED = -1
 
 _TORCH_DTYPE = {
     torch.float32: PKV_F32,
@@ -67,9 +70,9 @@ def _load():
                                                I32, I32, I32, I32, F, F, F, I32, P, SZ,
                                                I32, P]
     lib.pkv_paged_attention_decode.restype = I
-    lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_decode_workspace_bytes.restype = SZ
-    lib.pkv_paged_attention_reduce.argtypes = [P, I, P, SZ, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_paged_attention_reduce.argtypes = [P, I, P, SZ, P, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_paged_attention_reduce.restype = I
     lib.pkv_status_string.argtypes = [I]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -121,10 +124,10 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     _check("pkv_reshape_and_cache", rc)
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
-                           max_seq_len: int, partition_size: int) -> int:
-    return int(_load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
-                                                   max_seq_len, partition_size))
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                           head_dim: int, max_seq_len: int, partition_size: int) -> int:
+    return int(_load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                   head_dim, max_seq_len, partition_size))
 
 
 def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
@@ -135,8 +138,9 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
                            workspace: Optional[torch.Tensor] = None,
                            algo: str = "auto", stream=None) -> None:
     """out, query [S, Hq, D]; caches [NB, bs, Hkv, D]; block_tables [S, max_blocks]
-    int32; seq_lens [S] int32.  With partition_size > 0, call
-    paged_attention_reduce next with the same workspace."""
+    int32; seq_lens [S] int32.  partition_size: 0 one pass, P > 0 fixed
+    partitions of P tokens, PARTITION_BALANCED the balanced split; with a split,
+    call paged_attention_reduce next with the same workspace and value."""
     S, Hq, D = query.shape
     NB, bs, Hkv, _ = k_cache.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -150,21 +154,23 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
 
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor,
-                           seq_lens: torch.Tensor, *, max_seq_len: int,
+                           seq_lens: torch.Tensor, *, num_kv_heads: int, max_seq_len: int,
                            partition_size: int, stream=None) -> None:
     """Merges the split-K partials in `workspace` into out [S, Hq, D]."""
     S, Hq, D = out.shape
     rc = _load().pkv_paged_attention_reduce(
         _ptr(out), _dtype_code(out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(seq_lens), S, Hq, D,
-        int(max_seq_len), int(partition_size), _stream(stream))
+        workspace.numel() * workspace.element_size(), _ptr(seq_lens), S, Hq,
+        int(num_kv_heads), D, int(max_seq_len), int(partition_size), _stream(stream))
     _check("pkv_paged_attention_reduce", rc)
 
 
-def allocate_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_seq_len: int,
-                       partition_size: int, device="cuda") -> Optional[torch.Tensor]:
+def allocate_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                       max_seq_len: int, partition_size: int,
+                       device="cuda") -> Optional[torch.Tensor]:
     """A byte tensor large enough for split-K decode (None when not needed)."""
-    n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size)
+    n = decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                               partition_size)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device)

@@ -29,6 +29,9 @@ CFLAGS = [
     # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
     # works on them in place instead of copying them out of AGPRs
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # keep atomics as written: the optimizer's single-lane rewrite reads the
+    # result back at once, which would stall a pipelined loop
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
 ]

@@ -18,21 +18,50 @@ inline bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Partition count and workspace pieces for split-K.
+// Workspace pieces for split-K.  Fixed partitions: P_max entries per row,
+// m at 0, l at off_l, o at off_o.  Balanced: a 256-byte header, the tile
+// prefix of the sequences (S + 1 words) at off_pre, then m, l and o for two
+// entries per query head of the group per chunk of the guided schedule,
+// sized for the largest grid (kBalancedMaxWaves) and its chunk bound.
 struct WsLayout {
     int P_max = 0;
-    size_t off_l = 0, off_o = 0, bytes = 0;
+    size_t off_pre = 0, off_m = 0, off_l = 0, off_o = 0, bytes = 0;
 };
 
-inline bool ws_layout(int32_t S, int32_t Hq, int32_t D, int32_t max_seq_len,
+inline bool ws_layout(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_seq_len,
                       int32_t P, WsLayout* w) {
-    if (S <= 0 || Hq <= 0 || D <= 0 || max_seq_len <= 0 || P <= 0) return false;
-    w->P_max = (int)((max_seq_len + (int64_t)P - 1) / P);
-    const size_t n = (size_t)S * (size_t)Hq * (size_t)w->P_max;
-    w->off_l = round_up(n * 4, 256);
-    w->off_o = 2 * w->off_l;
+    if (S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_seq_len <= 0 || Hq % Hkv != 0)
+        return false;
+    size_t n;
+    if (P == PKV_PARTITION_BALANCED) {
+        w->P_max = 0;
+        w->off_pre = 256;
+        w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1), 256);
+        n = (size_t)2 * (size_t)max_chunks(kBalancedMaxWaves) * (size_t)(Hq / Hkv);
+    } else {
+        if (P <= 0) return false;
+        w->P_max = (int)((max_seq_len + (int64_t)P - 1) / P);
+        w->off_m = 0;
+        n = (size_t)S * (size_t)Hq * (size_t)w->P_max;
+    }
+    w->off_l = w->off_m + round_up(n * 4, 256);
+    w->off_o = w->off_l + round_up(n * 4, 256);
     w->bytes = w->off_o + n * (size_t)D * 4;
     return true;
+}
+
+// Resident wavefronts of the whole device for the balanced kernel serving
+// these types and shapes, capped at kBalancedMaxWaves.
+inline int balanced_grid_waves(int qdt, int cdt, int D, int bs, int S) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    int per_cu = decode_balanced_waves_per_cu(qdt, cdt, D, bs, S);
+    if (per_cu <= 0) per_cu = 8;
+    const long n = (long)cus * per_cu;
+    return (int)(n < kBalancedMaxWaves ? n : kBalancedMaxWaves);
 }
 
 inline bool supported_block_size(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
@@ -100,10 +129,13 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
     return launch_status(launch_reshape_and_cache(src_dtype, cache_dtype, p, stream));
 }
 
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition_size) {
     WsLayout w;
-    if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w)) return 0;
+    if (!ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
+                   &w))
+        return 0;
     return w.bytes;
 }
 
@@ -122,7 +154,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
-        partition_size < 0)
+        (partition_size < 0 && partition_size != PKV_PARTITION_BALANCED))
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
     if (num_kv_heads > 4096) return PKV_ERR_SHAPE;   // keeps in-block offsets 32-bit
@@ -145,6 +177,8 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     p.tables = block_tables;
     p.lens = seq_lens;
     p.ws_m = p.ws_l = p.ws_o = nullptr;
+    p.ws_hdr = p.ws_pre = nullptr;
+    p.nW = 0;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
@@ -160,15 +194,19 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
-    if (partition_size > 0) {
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    if (partition_size != 0) {
         WsLayout w;
-        if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w))
+        if (!ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                       partition_size, &w))
             return PKV_ERR_SHAPE;
         if (!workspace) return PKV_ERR_WORKSPACE;
         if (workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-        p.P_max = w.P_max;
-        p.ws_m = (float*)workspace;
+        p.P_max = balanced ? 1 : w.P_max;
+        p.ws_hdr = (int32_t*)workspace;
+        p.ws_pre = (int32_t*)((char*)workspace + w.off_pre);
+        p.ws_m = (float*)((char*)workspace + w.off_m);
         p.ws_l = (float*)((char*)workspace + w.off_l);
         p.ws_o = (float*)((char*)workspace + w.off_o);
     }
@@ -177,6 +215,16 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
 
     const bool mfma_ok = decode_mfma_supported(q_dtype, cache_dtype, head_dim, p.G);
     const bool valu_ok = decode_valu_supported(q_dtype, cache_dtype, head_dim, p.G);
+    if (balanced) {
+        // Tile counts are 32-bit on the device.
+        const int64_t tiles = (int64_t)num_seqs * num_kv_heads * ((p.len_cap + 15) / 16);
+        if (tiles > ((int64_t)1 << 31) - 1) return PKV_ERR_SHAPE;
+        if (algo == PKV_ALGO_VALU || !mfma_ok || num_seqs > kBalancedMaxSeqs)
+            return PKV_ERR_UNSUPPORTED;
+        p.P = 0;
+        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size, num_seqs);
+        return launch_status(launch_decode_balanced(q_dtype, cache_dtype, p, stream));
+    }
     if (algo == PKV_ALGO_MFMA || (algo == PKV_ALGO_AUTO && mfma_ok)) {
         if (!mfma_ok) return PKV_ERR_UNSUPPORTED;
         return launch_status(launch_decode_mfma(q_dtype, cache_dtype, p, stream));
@@ -187,17 +235,21 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
 
 int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* workspace,
                                size_t workspace_bytes, const int32_t* seq_lens,
-                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                               int32_t max_seq_len, int32_t partition_size,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seq_len, int32_t partition_size,
                                hipStream_t stream) {
     if (!valid_dtype(out_dtype) || out_dtype == PKV_FP8_E4M3) return PKV_ERR_DTYPE;
-    if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0 ||
-        partition_size <= 0)
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_seq_len <= 0 || (partition_size <= 0 && !balanced))
         return PKV_ERR_SHAPE;
-    if (partition_size % 16 != 0) return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (!balanced && partition_size % 16 != 0) return PKV_ERR_SHAPE;
     if (head_dim != 64 && head_dim != 128) return PKV_ERR_UNSUPPORTED;
+    if (balanced && num_seqs > kBalancedMaxSeqs) return PKV_ERR_UNSUPPORTED;
     WsLayout w;
-    if (!ws_layout(num_seqs, num_q_heads, head_dim, max_seq_len, partition_size, &w))
+    if (!ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_size,
+                   &w))
         return PKV_ERR_SHAPE;
     if (!out || !seq_lens) return PKV_ERR_NULL;
     if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
@@ -206,16 +258,20 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* works
     if ((int64_t)num_seqs * num_q_heads > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
     ReduceParams p;
     p.out = out;
-    p.ws_m = (const float*)workspace;
+    p.ws_hdr = (const int32_t*)workspace;
+    p.ws_pre = (const int32_t*)((const char*)workspace + w.off_pre);
+    p.ws_m = (const float*)((const char*)workspace + w.off_m);
     p.ws_l = (const float*)((const char*)workspace + w.off_l);
     p.ws_o = (const float*)((const char*)workspace + w.off_o);
     p.lens = seq_lens;
     p.S = num_seqs;
     p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
     p.D = head_dim;
-    p.P = partition_size;
+    p.P = balanced ? 0 : partition_size;
     p.P_max = w.P_max;
     p.len_cap = max_seq_len;
+    if (balanced) return launch_status(launch_reduce_balanced(out_dtype, p, stream));
     return launch_status(launch_reduce(out_dtype, p, stream));
 }
 

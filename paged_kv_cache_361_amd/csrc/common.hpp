@@ -100,6 +100,13 @@ __device__ inline float group_max(float x) {
     return x;
 }
 
+// Integer sum over the 64 lanes of a wavefront (every lane gets it).
+__device__ inline int group_sum_int(int x) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
 // Sum / max across lanes that differ only in bits >= log2(STRIDE): combines
 // the 64/STRIDE lanes {l, l+STRIDE, ...} that hold the same column.
 template <int STRIDE>

@@ -1,0 +1,468 @@
+// decode_balanced.hip - paged decode attention with the work of a whole
+// batch spread over a persistent grid of wavefronts by a guided dynamic
+// schedule ("balanced" split-K, partition_size = PKV_PARTITION_BALANCED).
+//
+// What is computed is the same single-query attention through the block
+// table as in "vLLM 推理引擎源码级拆解" §2.3; only the division of the work
+// differs.  Every (sequence, KV head) pair is a stream of 16-token tiles;
+// the streams are laid end to end (sequence-major, then KV head) and the
+// resulting T tiles are cut into chunks by the guided schedule of
+// kernels.hpp (large chunks first, small ones last).  The grid holds as many
+// wavefronts as the GPU runs at once; wave w starts on chunk w and then takes
+// chunks in order from a counter in the workspace.  Waves of one GPU do not
+// stream at one rate (waves of one CU finish a static even share tens of
+// microseconds apart), so the small chunks at the end keep every wave busy
+// until the batch is done.
+//
+// A piece of a stream inside one chunk is a segment.  A segment that is a
+// whole stream writes its output rows directly.  Any other segment is the
+// first or the last of its chunk and writes its partials (reference max,
+// sum, unnormalised output) to slot 0 (first) or 1 (last) of the chunk in the
+// workspace; pkv_paged_attention_reduce merges, for each stream spread over
+// chunks c0..c1, the entries of those chunks.
+//
+// Two kernels per call: a one-workgroup plan kernel writes the exclusive
+// tile prefix of the sequences, the schedule header and a zeroed chunk
+// counter into the workspace, then the decode kernel runs.  (A kernel rather
+// than a memset keeps the call safe to capture in a graph.)
+//
+// Pipeline.  The matrix-core tile of tile_mfma.hpp runs on a ring of DEPTH
+// tile buffers.  Segments are cut into spans of at most 64 blocks (one
+// block-table window, one entry per lane) and spans into rounds of DEPTH
+// tiles (the last round of a span padded with dead tiles).  The producer
+// issues round r + 1 while the consumer works through round r, slot by
+// slot, across span, segment and chunk boundaries: the table window of the
+// producer's next span, the query rows of a segment it enters and the index
+// of the chunk after its current one (the counter's atomic add) are all
+// requested one step ahead, and the lengths and tile prefix the walk needs
+// are held in LDS, so moving on never drains the ring.
+#include "tile_mfma.hpp"
+
+namespace pkv {
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 4;
+constexpr int kPlanThreads = 1024;
+
+// Atomic add on a buffer word, returning the old value; lanes whose offset
+// is past the descriptor's range do nothing (and read 0).  Used with only
+// lane 0 in range, so the wave adds once without a branch around the
+// instruction (a branch around a memory instruction would cost the loop a
+// full wait on every load in flight).
+__device__ int buffer_atomic_add_i32(int v, rsrc_t r, int off, int soff, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.atomic.add.i32");
+
+__device__ inline int seq_tiles(int L) { return L > 0 ? (L + 15) >> 4 : 0; }
+
+// ---- plan ----------------------------------------------------------------
+
+__global__ __launch_bounds__(kPlanThreads) void balanced_plan_kernel(DecodeParams p) {
+    __shared__ int wave_sum[kPlanThreads / 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int per = (p.S + kPlanThreads - 1) / kPlanThreads;   // sequences per thread
+    const int s0 = tid * per;
+    int n = 0;
+    for (int i = 0; i < per; i++) {
+        const int s = s0 + i;
+        if (s < p.S) n += seq_tiles(min(p.lens[s], p.len_cap)) * p.Hkv;
+    }
+    const int incl = wave_incl_scan(n);
+    if (lane == 63) wave_sum[wv] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanThreads / 64; k++) {
+        before += k < wv ? wave_sum[k] : 0;
+        total += wave_sum[k];
+    }
+    int run = before + incl - n;
+    for (int i = 0; i < per; i++) {
+        const int s = s0 + i;
+        if (s < p.S) {
+            p.ws_pre[s] = run;
+            run += seq_tiles(min(p.lens[s], p.len_cap)) * p.Hkv;
+        }
+    }
+    if (tid == 0) {
+        const Sched q = make_sched(total, p.nW);
+        p.ws_pre[p.S] = total;
+        int32_t* h = p.ws_hdr;
+        h[kHdrMagic] = kBalancedMagic;
+        h[kHdrNW] = p.nW;
+        h[kHdrHkv] = p.Hkv;
+        h[kHdrG] = p.G;
+        h[kHdrT] = total;
+        h[kHdrC1] = q.C1;
+        h[kHdrC2] = q.C2;
+        h[kHdrC3] = q.C3;
+        h[kHdrChunks] = q.chunks;
+        h[kHdrCounter] = 0;
+    }
+}
+
+// ---- decode ----------------------------------------------------------------
+
+// Span flags.
+enum : int { kFirst = 1, kLast = 2, kComplete = 4, kSlot1 = 8 };
+
+// A span: tiles [t0, t1) of stream (s, h) (packed in `key`), within one table
+// window starting at block wb, inside chunk `chunk`.  Wave-uniform; kept
+// small because three of them live in scalar registers.
+struct Span {
+    int key;           // s << 12 | h
+    int L, t0, t1, wb, chunk;
+    int flags;         // kFirst: first span of its segment; kLast: last;
+                       // kComplete: the segment is the whole stream;
+                       // kSlot1: not the first segment of its chunk
+    __device__ int s() const { return key >> 12; }
+    __device__ int h() const { return key & 4095; }
+};
+
+// Wave-uniform walk over one chunk, span by span.  pre and len are the LDS
+// copies of the tile prefix and of the clamped lengths.
+struct Walk {
+    int s, h, tile;    // next tile: stream (s, h), tile index
+    int L;             // clamped length of sequence s
+    int rem;           // tiles of the chunk not yet walked
+    int chunk;
+    int wf;            // 1: the current segment continues in the next span;
+                       // 2: it started at tile 0; 4: a segment already ended
+                       // in this chunk
+
+    __device__ inline void start(const int* pre, const int* len, int S, int c, int x0,
+                                 int x1) {
+        // the sequence whose streams hold tile x0: pre[s] <= x0 < pre[s + 1]
+        int lo = 0, hi = S;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (__builtin_amdgcn_readfirstlane(pre[mid]) <= x0) lo = mid;
+            else hi = mid;
+        }
+        s = lo;
+        L = __builtin_amdgcn_readfirstlane(len[s]);
+        const int nt = seq_tiles(L);
+        const int off = x0 - __builtin_amdgcn_readfirstlane(pre[s]);
+        h = off / nt;
+        tile = off % nt;
+        rem = x1 - x0;
+        chunk = c;
+        wf = 0;
+    }
+
+    __device__ inline bool next(const int* len, int S, int Hkv, int bs_shift, Span& o) {
+        if (rem <= 0) return false;
+        int nt = seq_tiles(L);
+        while (tile >= nt) {               // stream exhausted: move on
+            tile = 0;
+            wf &= ~1;
+            if (++h == Hkv) {
+                h = 0;
+                do {
+                    if (++s >= S) return false;    // not reached while rem > 0
+                    L = __builtin_amdgcn_readfirstlane(len[s]);
+                    nt = seq_tiles(L);
+                } while (nt == 0);
+            }
+        }
+        int f = 0;
+        if (!(wf & 1)) {                   // a new segment starts here
+            f |= kFirst;
+            wf = (wf & 4) | (tile == 0 ? 2 : 0);
+        }
+        if (wf & 4) f |= kSlot1;
+        o.key = (s << 12) | h;
+        o.L = L;
+        o.t0 = tile;
+        o.wb = (tile << 4) >> bs_shift;
+        const int wend = ((o.wb + 64) << bs_shift) >> 4;   // first tile past the window
+        int t1 = min(nt, tile + rem);
+        t1 = min(t1, wend);
+        o.t1 = t1;
+        o.chunk = chunk;
+        rem -= t1 - tile;
+        tile = t1;
+        const bool last = (tile >= nt) || rem <= 0;
+        if (last) {
+            f |= kLast;
+            if ((wf & 2) && tile >= nt) f |= kComplete;
+            wf = 4;                        // closed; later segments use slot 1
+        } else {
+            wf |= 1;
+        }
+        o.flags = f;
+        return true;
+    }
+};
+
+template <class Q, class C, int D, bool PAIR, int DEPTH>
+__global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodeParams p) {
+    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef typename TM::T T;
+    typedef typename TM::v8 v8;
+    extern __shared__ int lds[];
+    int* pre = lds;                        // [S + 1] tile prefix
+    int* len = lds + p.S + 1;              // [S] clamped lengths
+    for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) {
+        pre[i] = p.ws_pre[i];
+        if (i < p.S) len[i] = min(p.lens[i], p.len_cap);
+    }
+    __syncthreads();
+
+    const TM tm;
+    const int lane = tm.lane;
+    const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const Sched q = make_sched(__builtin_amdgcn_readfirstlane(pre[p.S]), p.nW);
+    if (w >= q.chunks) return;
+    const int G = p.G;
+    const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
+    int* counter = p.ws_hdr + kHdrCounter;
+
+    // ---- requests made one round ahead ---------------------------------
+    // The index of the wave's next chunk (the counter's atomic add), the
+    // table window of the producer's next span and the query rows of a
+    // segment the producer enters are requested once per round, at the end
+    // of the round, by instructions that run every round (out of range, so
+    // touching nothing, when nothing is wanted), and taken one round later,
+    // after the consumer has waited for the tiles issued before them.  A
+    // result still in flight is never copied or branched around, which would
+    // make the loop wait for every load in flight.
+    const rsrc_t ctr = make_rsrc((const char*)counter, 4);
+    int got = buffer_atomic_add_i32(1, ctr, lane == 0 ? 0 : (int)kOOB, 0, 0);
+    bool issued = true;                    // `got` is a chunk request in flight
+    bool have = false;                     // `pend` holds an unused chunk index
+    int pend = 0;
+    bool chunks_left = true;
+    auto take_chunk = [&]() {
+        int k;
+        if (have) k = pend;
+        else if (issued) k = __builtin_amdgcn_readfirstlane(got);
+        else k = __builtin_amdgcn_readfirstlane(
+                 buffer_atomic_add_i32(1, ctr, lane == 0 ? 0 : (int)kOOB, 0, 0));
+        have = issued = false;
+        return q.nW + k;
+    };
+
+    // ---- producer: walks the wave's chunks one span ahead of the issue ----
+    Walk pw;
+    pw.start(pre, len, p.S, w, chunk_begin(q, w), chunk_begin(q, w + 1));
+    auto next_span = [&](Span& o) {
+        while (!pw.next(len, p.S, p.Hkv, bs_shift, o)) {
+            if (!chunks_left) return false;
+            const int c = take_chunk();
+            if (c >= q.chunks) {
+                chunks_left = false;
+                return false;
+            }
+            pw.start(pre, len, p.S, c, chunk_begin(q, c), chunk_begin(q, c + 1));
+        }
+        return true;
+    };
+    // Window of 64 block-table entries from block sp.wb; entries at or past
+    // ceil(L / bs) are outside the descriptor and read 0 (never touched).
+    auto load_window = [&](const Span& sp, bool want) {
+        const int nblk = want ? (sp.L + p.bs - 1) >> bs_shift : 0;
+        const rsrc_t r = make_rsrc((const char*)(p.tables + (size_t)sp.s() * p.max_blocks),
+                                   (uint32_t)nblk * 4u);
+        return (int)Buf<4>::load(r, (uint32_t)(sp.wb + lane) * 4u);
+    };
+    // Query rows of the span's group as the B operand (heads past G read 0).
+    auto load_query = [&](const Span& sp, bool want, v8 (&qv)[TM::KS]) {
+        const char* base = (const char*)p.q + ((size_t)sp.s() * p.Hq + (size_t)sp.h() * G) * D * sizeof(T);
+        const rsrc_t r = make_rsrc(base, want ? (uint32_t)(G * D * sizeof(T)) : 0u);
+        const uint32_t row = (uint32_t)(tm.j16 * D * sizeof(T));
+#pragma unroll
+        for (int kk = 0; kk < TM::KS; kk++) {
+            const int d0 = TM::kFp8 ? (kk >> 1) * 64 + 16 * tm.g4 + (kk & 1) * 8 : 32 * kk + 8 * tm.g4;
+            qv[kk] = __builtin_bit_cast(v8, Buf<16>::load(r, row + (uint32_t)(d0 * sizeof(T))));
+        }
+    };
+
+    Span ps, pn;
+    next_span(ps);                         // chunk w is not empty
+    v8 qb[TM::KS];                         // query of the consumer's segment
+    load_query(ps, true, qb);
+    int win = load_window(ps, true);
+    bool has_ps = true;
+    bool has_pn = next_span(pn);
+    int win_n = load_window(pn, has_pn);   // window of pn
+    Head hd = make_head<C, D>(p, ps.h());
+    int prt = ps.t0;
+
+    bool want_win = false, want_q = false;  // set when pn / ps change
+    // Producer's step to the round after the one just issued.
+    auto producer_advance = [&]() {
+        prt += DEPTH;
+        if (has_ps && prt >= ps.t1) {
+            has_ps = has_pn;
+            if (has_ps) {
+                ps = pn;
+                win = win_n;
+                prt = ps.t0;
+                hd = make_head<C, D>(p, ps.h());
+                want_q = (ps.flags & kFirst) != 0;
+                has_pn = next_span(pn);
+                want_win = has_pn;
+            }
+        }
+    };
+    int wload;                              // window requested this round
+    v8 qload[TM::KS];                       // query requested this round
+    // End of a round: the requests.
+    auto request = [&]() {
+        const bool want = !have && !issued && chunks_left;
+        got = buffer_atomic_add_i32(1, ctr, lane == 0 && want ? 0 : (int)kOOB, 0, 0);
+        issued = want;
+        wload = load_window(pn, want_win);
+        load_query(ps, want_q, qload);
+    };
+    // One round later: take them.  `got` must be taken before the next
+    // request, which reuses it.
+    auto take_chunk_index = [&]() {
+        if (issued) {
+            pend = __builtin_amdgcn_readfirstlane(got);
+            have = true;
+            issued = false;
+        }
+    };
+    auto take = [&]() {
+        take_chunk_index();
+        if (want_win) {
+            win_n = wload;
+            want_win = false;
+        }
+    };
+
+    // ---- consumer: one round behind, on the producer's previous span ------
+    typename TM::Tile tl[DEPTH];
+#pragma unroll
+    for (int j = 0; j < DEPTH; j++) {
+        const int tp = prt + j;
+        tm.issue(hd, tp << 4, tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1, ps.wb, win, tl[j]);
+    }
+    // consumer's span: its stream, length, end tile, chunk and flags
+    int c_key = ps.key, c_L = ps.L, c_t1 = ps.t1, c_chunk = ps.chunk, c_flags = ps.flags;
+    int crt = ps.t0;
+    typename TM::Acc acc;
+    tm.reset(acc);
+    producer_advance();
+    take_chunk_index();                    // the request made at the start
+    request();
+
+    while (true) {
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++) {
+            const int tc = crt + j;
+            if (j == 0 || tc < c_t1) tm.consume(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j]);
+            const int tp = prt + j;
+            const int plim = has_ps && tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1;
+            tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j]);
+        }
+        take();
+        // Consumer first: finish its span and take the producer's current
+        // one (the span of the round just issued) before the producer moves.
+        crt += DEPTH;
+        if (crt >= c_t1) {
+            if (c_flags & kLast) {
+                const size_t row0 = (size_t)(c_key >> 12) * p.Hq + (size_t)(c_key & 4095) * G;
+                const size_t e0 = ((size_t)c_chunk * 2 + ((c_flags & kSlot1) ? 1 : 0)) * G;
+                tm.finish(
+                    acc, G, (c_flags & kComplete) != 0, p.v_scale,
+                    [&](int head) { return (T*)p.out + (row0 + head) * D; },
+                    [&](int head) { return p.ws_m + e0 + head; },
+                    [&](int head) { return p.ws_l + e0 + head; },
+                    [&](int head) { return p.ws_o + (e0 + head) * D; });
+            }
+            if (!has_ps) break;
+            c_key = ps.key;
+            c_L = ps.L;
+            c_t1 = ps.t1;
+            c_chunk = ps.chunk;
+            c_flags = ps.flags;
+            crt = ps.t0;
+            if (c_flags & kFirst) {
+                // requested when the producer entered this segment
+#pragma unroll
+                for (int k = 0; k < TM::KS; k++) qb[k] = qload[k];
+                tm.reset(acc);
+            }
+        }
+        want_q = false;
+        producer_advance();
+        request();
+    }
+}
+
+// Tiles in flight per wavefront: two 16-token tiles (one of them in flight
+// during the arithmetic) keep the kernel at two waves per SIMD with the walk
+// state and the prefetched query of the next segment held in registers.
+template <bool PAIR>
+constexpr int pipeline_depth() {
+    return 2;
+}
+
+inline size_t lds_bytes(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
+
+template <class Q, class C, int D, bool PAIR>
+hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
+    const dim3 grid((unsigned)((p.nW + kWaves - 1) / kWaves)), block(64 * kWaves);
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>()>),
+        grid, block, args, lds_bytes(p.S), st);
+}
+
+template <class Q, class C, int D, bool PAIR>
+int resident_k(int S) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>()>,
+            64 * kWaves, lds_bytes(S)) != hipSuccess)
+        return 0;
+    return blocks * kWaves;
+}
+
+template <class Q, class C>
+hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
+    const bool pair = p.bs == 8;
+    if (p.D == 64) return pair ? launch_k<Q, C, 64, true>(p, st) : launch_k<Q, C, 64, false>(p, st);
+    if (p.D == 128)
+        return pair ? launch_k<Q, C, 128, true>(p, st) : launch_k<Q, C, 128, false>(p, st);
+    return hipErrorInvalidValue;
+}
+
+template <class Q, class C>
+int resident_d(int D, int bs, int S) {
+    const bool pair = bs == 8;
+    if (D == 64) return pair ? resident_k<Q, C, 64, true>(S) : resident_k<Q, C, 64, false>(S);
+    if (D == 128) return pair ? resident_k<Q, C, 128, true>(S) : resident_k<Q, C, 128, false>(S);
+    return 0;
+}
+
+}  // namespace
+
+int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S) {
+    if (qdt == kBF16)
+        return cdt == kFP8 ? resident_d<BF16, FP8>(D, bs, S) : resident_d<BF16, BF16>(D, bs, S);
+    if (qdt == kF16)
+        return cdt == kFP8 ? resident_d<F16, FP8>(D, bs, S) : resident_d<F16, F16>(D, bs, S);
+    return 0;
+}
+
+hipError_t launch_decode_balanced(int qdt, int cdt, const DecodeParams& p, hipStream_t st) {
+    if (!decode_mfma_supported(qdt, cdt, p.D, p.G)) return hipErrorInvalidValue;
+    if (p.S > kBalancedMaxSeqs || p.nW < 1 || p.nW > kBalancedMaxWaves) return hipErrorInvalidValue;
+    hipError_t e = launch_kernel(balanced_plan_kernel, dim3(1), dim3(kPlanThreads), st, p);
+    if (e != hipSuccess) return e;
+    if (qdt == kBF16) {
+        if (cdt == kFP8) return launch_d<BF16, FP8>(p, st);
+        return launch_d<BF16, BF16>(p, st);
+    }
+    if (cdt == kFP8) return launch_d<F16, FP8>(p, st);
+    return launch_d<F16, F16>(p, st);
+}
+
+}  // namespace pkv

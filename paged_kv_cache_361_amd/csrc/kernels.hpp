@@ -32,6 +32,9 @@ struct DecodeParams {
     float* ws_m;           // split-K partials (nullptr in one-pass mode)
     float* ws_l;
     float* ws_o;
+    int32_t* ws_hdr;       // balanced mode: header of the workspace
+    int32_t* ws_pre;       // balanced mode: tile prefix of the sequences [S + 1]
+    int nW;                // balanced mode: wavefronts of the persistent grid
     int S, Hq, Hkv, D, G, bs, NB, max_blocks;
     int len_cap;           // min(max_seq_len, max_blocks * bs)
     int P;                 // partition size, 0 = one pass
@@ -45,9 +48,83 @@ struct ReduceParams {
     const float* ws_m;
     const float* ws_l;
     const float* ws_o;
+    const int32_t* ws_hdr; // balanced mode: header written by the decode call
+    const int32_t* ws_pre; // balanced mode: tile prefix of the sequences [S + 1]
     const int32_t* lens;
-    int S, Hq, D, P, P_max, len_cap;
+    int S, Hq, Hkv, D, P, P_max, len_cap;
 };
+
+// ---- balanced split-K ------------------------------------------------------
+//
+// The T tiles of a batch (16 tokens of one (sequence, KV head) stream each,
+// streams laid end to end) are cut into chunks by a guided schedule that
+// depends only on T and the grid size nW: nW chunks of C1 tiles (about 60%
+// of an even share A = T / nW), then nW chunks of C2 (about 25%), then chunks
+// of C3 = max(4, A / 10) up to T.  Chunk c starts at tile
+// chunk_begin(c); the decode grid takes chunks 0..nW-1 statically and the
+// rest from a counter, and the reduce finds a stream's chunks with
+// chunk_of().
+//
+// Workspace: a 256-byte header (words below; the chunk counter alone in
+// word 32), the exclusive tile prefix of the sequences (S + 1 words) from
+// byte 256, then (m, l, o) entries, two per query head of the group per
+// chunk.
+constexpr int32_t kBalancedMagic = 0x504B5642;
+enum BalancedHeader : int {
+    kHdrMagic = 0, kHdrNW = 1, kHdrHkv = 2, kHdrG = 3, kHdrT = 4, kHdrC1 = 5, kHdrC2 = 6,
+    kHdrC3 = 7, kHdrChunks = 8, kHdrCounter = 32
+};
+// Upper bound on the persistent grid of the balanced kernel (wavefronts).
+constexpr int kBalancedMaxWaves = 2048;
+// Upper bound on the batch size of the balanced kernel (the tile prefix of
+// the sequences is held in LDS).
+constexpr int kBalancedMaxSeqs = 8192;
+
+struct Sched {
+    int T, nW, C1, C2, C3, chunks;
+    int e1, e2;            // first tiles of the second and third phases (capped at T)
+};
+
+__host__ __device__ inline Sched make_sched(int T, int nW) {
+    Sched q;
+    q.T = T;
+    q.nW = nW;
+    const int A = nW > 0 ? T / nW : 0;
+    q.C1 = A * 3 / 5 > 1 ? A * 3 / 5 : 1;
+    q.C2 = A / 4 > 1 ? A / 4 : 1;
+    q.C3 = A / 10 > 4 ? A / 10 : 4;
+    const int64_t e1 = (int64_t)nW * q.C1;
+    const int64_t e2 = e1 + (int64_t)nW * q.C2;
+    q.e1 = (int)(e1 < T ? e1 : T);
+    q.e2 = (int)(e2 < T ? e2 : T);
+    if (T <= 0) q.chunks = 0;
+    else if (e1 >= T) q.chunks = (T + q.C1 - 1) / q.C1;
+    else if (e2 >= T) q.chunks = nW + (int)((T - e1 + q.C2 - 1) / q.C2);
+    else q.chunks = 2 * nW + (int)((T - e2 + q.C3 - 1) / q.C3);
+    return q;
+}
+
+// First tile of chunk c (c <= chunks; chunk_begin(chunks) == T).
+__host__ __device__ inline int chunk_begin(const Sched& q, int c) {
+    int64_t b;
+    if (c <= q.nW) b = (int64_t)c * q.C1;
+    else if (c <= 2 * q.nW) b = (int64_t)q.nW * q.C1 + (int64_t)(c - q.nW) * q.C2;
+    else b = (int64_t)q.nW * (q.C1 + q.C2) + (int64_t)(c - 2 * q.nW) * q.C3;
+    return (int)(b < q.T ? b : q.T);
+}
+
+// Chunk holding tile x (0 <= x < T).
+__host__ __device__ inline int chunk_of(const Sched& q, int x) {
+    if (x < q.e1) return x / q.C1;
+    if (x < q.e2) return q.nW + (x - q.e1) / q.C2;
+    return 2 * q.nW + (x - q.e2) / q.C3;
+}
+
+// Most chunks any batch can produce on a grid of nW waves (the workspace
+// bound): phases one and two hold 2 nW chunks; the third covers fewer than
+// (0.15 A + 2.6) nW tiles in chunks of max(4, A/10), fewer than 2.5 nW + 1
+// chunks for every A.
+__host__ __device__ inline int64_t max_chunks(int nW) { return 5 * (int64_t)nW + 8; }
 
 // Launches a kernel whose only parameter is a parameter struct and returns
 // that launch's own status.
@@ -65,6 +142,11 @@ bool decode_valu_supported(int qdt, int cdt, int D, int G);
 hipError_t launch_decode_valu(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 bool decode_mfma_supported(int qdt, int cdt, int D, int G);
 hipError_t launch_decode_mfma(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
+// Balanced mode (matrix-core kernel): resident wavefronts per CU of the
+// kernel that would serve these types and shapes (0 if unknown), and launch.
+int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S);
+hipError_t launch_decode_balanced(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 hipError_t launch_reduce(int out_dt, const ReduceParams& p, hipStream_t st);
+hipError_t launch_reduce_balanced(int out_dt, const ReduceParams& p, hipStream_t st);
 
 }  // namespace pkv

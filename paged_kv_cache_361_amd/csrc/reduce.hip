@@ -1,19 +1,26 @@
-// reduce.hip - the second kernel of split-K decode: merges per-partition
-// partials (m_k, l_k, o_k) into the output row
+// reduce.hip - the second kernel of split-K decode: merges partials
+// (m_k, l_k, o_k) into the output row
 //     out = sum_k e^(m_k - M) o_k / sum_k e^(m_k - M) l_k,  M = max_k m_k.
 // The pages do not describe partitioned decode; the merge is the running
 // max / running sum update of the online softmax in the kernel sketch of
-// "vLLM 推理引擎源码级拆解" §2.3, applied once per partition instead of once
-// per token.
+// "vLLM 推理引擎源码级拆解" §2.3, applied once per piece instead of once per
+// token.
 //
-// Work layout.  A row (sequence, query head) is served by WPR wavefronts
-// (WPR = 1 for short rows, 4 when rows have many partitions).  Lane
-// (kg = lane / 16, c = lane % 16) of wave `sub` owns output columns
-// [c*CW, c*CW + CW) and the partitions k = j, j + 4*WPR, j + 8*WPR, ... with
-// slot j = 4*sub + kg; each partition's CW columns are one contiguous load,
-// and the loads of four partitions are issued together.  M and the
-// denominator are computed by every wave from the m_k and l_k arrays (tiny);
-// the per-slot sums meet through lane shuffles and, for WPR = 4, through LDS.
+// Where the entries of a row live depends on the split:
+//   fixed partitions  entry k of row (s, hq) is partition k, k < ceil(L/P);
+//   balanced          the row's KV-head stream was cut over chunks c0..c1 of
+//                     the guided schedule (kernels.hpp); entry e is slot 0 or
+//                     1 of chunk c0 + e (see decode_balanced.hip), found from
+//                     the tile prefix and the header the decode call wrote.
+//
+// Work layout.  A row is served by WPR wavefronts (WPR = 1 for short rows, 4
+// when rows have many entries).  Lane (kg = lane / 16, c = lane % 16) of wave
+// `sub` owns output columns [c*CW, c*CW + CW) and the entries e = j, j + 4*WPR,
+// j + 8*WPR, ... with slot j = 4*sub + kg; each entry's CW columns are one
+// contiguous load, and the loads of four entries are issued together, the
+// first four before M is known.  M and the denominator are computed by every
+// wave from the m and l values (tiny); the per-slot sums meet through lane
+// shuffles and, for WPR = 4, through LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,67 +30,74 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kUnroll = 4;
 
-template <class O, int D, int WPR>
-__global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
+// Merges n >= 2 entries into one output row.  idx(e) maps entry e to its
+// index in the m/l arrays (o rows at idx * D).
+template <class O, int D, int WPR, class Idx>
+__device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t row,
+                                 int wave, int sub) {
     constexpr int CW = D / 16;                 // columns per lane
-    constexpr int SLOTS = 4 * WPR;             // partition slots per row
-    constexpr int RPB = kWaves / WPR;          // rows per workgroup
+    constexpr int SLOTS = 4 * WPR;             // entry slots per row
     typedef float colv __attribute__((ext_vector_type(CW)));
     __shared__ colv part_sum[WPR > 1 ? kWaves : 1][16];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int sub = wave % WPR;
-    const int row = blockIdx.x * RPB + wave / WPR;   // s * Hq + hq
-    const int rows = p.S * p.Hq;
-    // With WPR > 1 a workgroup is one row, so these exits are workgroup-uniform.
-    if (row >= rows) return;
-    const int s = row / p.Hq;
-    int L = p.lens[s];
-    L = L < p.len_cap ? L : p.len_cap;
-    const int nparts = L > 0 ? (L + p.P - 1) / p.P : 0;
-    if (nparts <= 1) return;
-
-    const size_t base = (size_t)row * p.P_max;
-    const float* ms = p.ws_m + base;
-    const float* ls = p.ws_l + base;
-
-    // M and the denominator, over all partitions (lanes stride by 64).
-    float M = -INFINITY;
-    for (int k = lane; k < nparts; k += 64) M = fmaxf(M, ms[k]);
-    M = group_max<64>(M);
-    const float Ml = M * kLog2e;
-    float den = 0.0f;
-    for (int k = lane; k < nparts; k += 64) den += exp2f(fmaf(ms[k], kLog2e, -Ml)) * ls[k];
-    den = group_sum<64>(den);
-
-    // Weighted sum of this lane's slot over its columns.
     const int kg = lane >> 4;
     const int c = lane & 15;
     const int j = 4 * sub + kg;
-    const float* ob = p.ws_o + base * D + c * CW;
-    colv acc = colv{};
-    for (int k0 = j; k0 < nparts; k0 += SLOTS * kUnroll) {
-        colv o[kUnroll];
-        float m[kUnroll];
+
+    // Everything a short row needs is requested before anything waits: the
+    // first 64 (m, l) pairs and the first round of this lane's partial
+    // outputs (which do not depend on M).  Out-of-range slots read entry 0
+    // and get weight 0.
+    const size_t i0 = lane < n ? idx(lane) : 0;
+    const float m0 = lane < n ? p.ws_m[i0] : -INFINITY;
+    const float l0 = lane < n ? p.ws_l[i0] : 0.0f;
+    colv o[kUnroll];
+    float mo[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int k = k0 + u * SLOTS;
-            const int kk = k < nparts ? k : j;             // in range; weight zeroed below
-            o[u] = *(const colv*)(ob + (size_t)kk * D);
-            m[u] = ms[kk];
+    for (int u = 0; u < kUnroll; u++) {
+        const int e = j + u * SLOTS;
+        const size_t ie = idx(e < n ? e : 0);
+        o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+        mo[u] = p.ws_m[ie];
+    }
+
+    // M and the denominator over all entries (lanes stride by 64).
+    float M = m0;
+    for (int e = lane + 64; e < n; e += 64) M = fmaxf(M, p.ws_m[idx(e)]);
+    M = group_max<64>(M);
+    const float Ml = M * kLog2e;
+    float den = lane < n ? exp2f(fmaf(m0, kLog2e, -Ml)) * l0 : 0.0f;
+    for (int e = lane + 64; e < n; e += 64) {
+        const size_t ie = idx(e);
+        den += exp2f(fmaf(p.ws_m[ie], kLog2e, -Ml)) * p.ws_l[ie];
+    }
+    den = group_sum<64>(den);
+
+    // Weighted sum of this lane's slot over its columns, kUnroll entries per
+    // round.
+    colv acc = colv{};
+    for (int e0 = j; e0 < n; e0 += SLOTS * kUnroll) {
+        if (e0 != j) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++) {
+                const int e = e0 + u * SLOTS;
+                const size_t ie = idx(e < n ? e : 0);
+                o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+                mo[u] = p.ws_m[ie];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
-            const int k = k0 + u * SLOTS;
-            const float w = k < nparts ? exp2f(fmaf(m[u], kLog2e, -Ml)) : 0.0f;
+            const int e = e0 + u * SLOTS;
+            const float w = e < n ? exp2f(fmaf(mo[u], kLog2e, -Ml)) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < CW; e++) acc[e] = fmaf(w, o[u][e], acc[e]);
+            for (int q = 0; q < CW; q++) acc[q] = fmaf(w, o[u][q], acc[q]);
         }
     }
     // Combine the four slots of this wave (lanes c, c+16, c+32, c+48).
 #pragma unroll
-    for (int e = 0; e < CW; e++) acc[e] = strided_sum<16>(acc[e]);
+    for (int q = 0; q < CW; q++) acc[q] = strided_sum<16>(acc[q]);
     if constexpr (WPR > 1) {
         if (kg == 0) part_sum[wave][c] = acc;
         __syncthreads();
@@ -92,7 +106,7 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
         for (int w = 1; w < WPR; w++) {
             const colv x = part_sum[w][c];
 #pragma unroll
-            for (int e = 0; e < CW; e++) acc[e] += x[e];
+            for (int q = 0; q < CW; q++) acc[q] += x[q];
         }
     } else {
         if (kg != 0) return;
@@ -102,38 +116,120 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
     typedef OT ovec __attribute__((ext_vector_type(CW)));
     ovec r;
 #pragma unroll
-    for (int e = 0; e < CW; e++) r[e] = O::narrow(acc[e] * inv);
-    *(ovec*)((OT*)p.out + (size_t)row * D + c * CW) = r;
+    for (int q = 0; q < CW; q++) r[q] = O::narrow(acc[q] * inv);
+    *(ovec*)((OT*)p.out + row * D + c * CW) = r;
 }
 
-template <class O, int D>
-hipError_t launch_w(const ReduceParams& p, hipStream_t st) {
+// ---- fixed partitions -------------------------------------------------------
+
+template <class O, int D, int WPR>
+__global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
+    constexpr int RPB = kWaves / WPR;          // rows per workgroup
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = wave % WPR;
+    const int row = blockIdx.x * RPB + wave / WPR;   // s * Hq + hq
+    // With WPR > 1 a workgroup is one row, so these exits are workgroup-uniform.
+    if (row >= p.S * p.Hq) return;
+    const int s = row / p.Hq;
+    int L = p.lens[s];
+    L = L < p.len_cap ? L : p.len_cap;
+    const int nparts = L > 0 ? (L + p.P - 1) / p.P : 0;
+    if (nparts <= 1) return;
+    const size_t base = (size_t)row * p.P_max;
+    merge_row<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, wave,
+                         sub);
+}
+
+// ---- balanced split ---------------------------------------------------------
+
+template <class O, int D, int WPR>
+__global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReduceParams p) {
+    constexpr int RPB = kWaves / WPR;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = wave % WPR;
+    const int row = blockIdx.x * RPB + wave / WPR;
+    if (row >= p.S * p.Hq) return;
+    const int32_t* hdr = p.ws_hdr;
+    const int nW = hdr[kHdrNW];
+    const int Hkv = hdr[kHdrHkv];
+    const int G = hdr[kHdrG];
+    const int T = hdr[kHdrT];
+    // A workspace not written by a balanced decode of this shape: write
+    // nothing rather than follow its indices.
+    if (hdr[kHdrMagic] != kBalancedMagic || nW < 1 || nW > kBalancedMaxWaves || G < 1 ||
+        Hkv != p.Hkv || Hkv * G != p.Hq || T < 0 || p.ws_pre[p.S] != T)
+        return;
+    const Sched q = make_sched(T, nW);
+    const int s = row / p.Hq;
+    const int hq = row % p.Hq;
+    const int h = hq / G;
+    const int g = hq % G;
+    const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
+    if (p0 < 0 || p1 < p0 || p1 > T || (p1 - p0) % Hkv != 0) return;
+    const int nt = (p1 - p0) / Hkv;
+    if (nt == 0) {                              // no tokens: a zero row
+        if (sub == 0) {
+            typedef typename O::T OT;
+            for (int d = lane; d < D; d += 64) ((OT*)p.out)[(size_t)row * D + d] = O::narrow(0.0f);
+        }
+        return;
+    }
+    const int g0 = p0 + h * nt;                 // first tile of stream (s, h)
+    const int c0 = chunk_of(q, g0);
+    const int c1 = chunk_of(q, g0 + nt - 1);
+    if (c0 == c1) return;                       // one chunk held it: decode wrote the row
+    const int slot0 = chunk_begin(q, c0) < g0 ? 1 : 0;
+    merge_row<O, D, WPR>(
+        p, c1 - c0 + 1,
+        [&](int e) {
+            const int slot = e == 0 ? slot0 : 0;
+            return ((size_t)(c0 + e) * 2 + slot) * G + g;
+        },
+        (size_t)row, wave, sub);
+}
+
+template <class O, int D, bool BAL>
+hipError_t launch_w(const ReduceParams& p, bool wide, hipStream_t st) {
     const long rows = (long)p.S * p.Hq;
     const dim3 block(64 * kWaves);
-    if (p.P_max > 32) {
+    if (wide) {
         const dim3 grid((unsigned)rows);
+        if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 4>, grid, block, st, p);
         return launch_kernel(reduce_kernel<O, D, 4>, grid, block, st, p);
     }
     const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
+    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 1>, grid, block, st, p);
     return launch_kernel(reduce_kernel<O, D, 1>, grid, block, st, p);
 }
 
-template <class O>
-hipError_t launch_d(const ReduceParams& p, hipStream_t st) {
-    if (p.D == 64) return launch_w<O, 64>(p, st);
-    if (p.D == 128) return launch_w<O, 128>(p, st);
+template <class O, bool BAL>
+hipError_t launch_d(const ReduceParams& p, bool wide, hipStream_t st) {
+    if (p.D == 64) return launch_w<O, 64, BAL>(p, wide, st);
+    if (p.D == 128) return launch_w<O, 128, BAL>(p, wide, st);
     return hipErrorInvalidValue;
+}
+
+template <bool BAL>
+hipError_t launch_o(int out_dt, const ReduceParams& p, bool wide, hipStream_t st) {
+    switch (out_dt) {
+    case kF32: return launch_d<F32, BAL>(p, wide, st);
+    case kF16: return launch_d<F16, BAL>(p, wide, st);
+    case kBF16: return launch_d<BF16, BAL>(p, wide, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_reduce(int out_dt, const ReduceParams& p, hipStream_t st) {
-    switch (out_dt) {
-    case kF32: return launch_d<F32>(p, st);
-    case kF16: return launch_d<F16>(p, st);
-    case kBF16: return launch_d<BF16>(p, st);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_o<false>(out_dt, p, p.P_max > 32, st);
+}
+
+hipError_t launch_reduce_balanced(int out_dt, const ReduceParams& p, hipStream_t st) {
+    // Few rows (long contexts, each row split over many waves): four waves
+    // per row.
+    return launch_o<true>(out_dt, p, (long)p.S * p.Hq <= 2048, st);
 }
 
 }  // namespace pkv

@@ -1,0 +1,404 @@
+// tile_mfma.hpp - the matrix-core tile of paged decode attention, shared by
+// the per-unit kernel (decode_mfma.hip) and the balanced persistent kernel
+// (decode_balanced.hip).
+//
+// One wavefront serves the G <= 16 query heads of one KV head, 16 tokens at
+// a time ("vLLM 推理引擎源码级拆解" §2.3: single-query attention through the block
+// table with a running max / running sum softmax):
+//
+//   scores  S^T[token][head] = K_tile[16 x D] * Q^T[D x 16]
+//           v_mfma_f32_16x16x32_{bf16,f16}: A = K rows (lane%16 = token, the
+//           lane's 8 contraction elements are a 16-byte slice of the row), B =
+//           the query heads (lane%16 = head, zero past G).  The result lands
+//           with lane%16 = head and register r = token 4*(lane/16) + r.
+//   output  O[head][d] += P[head][token] * V_tile[16 x D]
+//           v_mfma_f32_16x16x16_{bf16,f16}, one per 16 output columns.  The
+//           score layout above is exactly the A layout of this instruction
+//           (lane%16 = head, 4 consecutive tokens per lane), so the softmax
+//           weights feed it without any data movement.  For B each lane loads
+//           the rows of its 4 tokens restricted to 8 contiguous columns and the
+//           columns are assigned as d = 8*(lane%16) + n for tile n, which turns
+//           the transpose the instruction needs into register permutes.
+//
+// Memory side.  Every K/V access is a buffer load whose 128-bit descriptor
+// holds the 64-bit base of one physical block (plus the head offset) in
+// scalar registers, with 32-bit per-lane offsets inside the block.  Rows past
+// the end of a sequence get an offset beyond the descriptor's range: the
+// hardware returns zeros without touching memory, so masked tokens cost no
+// bandwidth and whatever the pool holds there (NaN poison included) never
+// reaches the arithmetic.  Block ids come from a 64-entry window of the block
+// table held one entry per lane and broadcast with readlane.
+//
+// Softmax bookkeeping.  Scores are kept in base-2 units (log2(e) and the
+// scale folded into one multiplier).  The running reference maximum of a
+// head is raised only when a tile's maximum exceeds it by more than kTau, so
+// the accumulator rescale is rare; weights are then bounded by 2^kTau, which
+// fp32 sums absorb without loss.
+//
+// E4M3 caches are widened to the query's 16-bit type with the gfx950 packed
+// conversion (exact: every E4M3 value is a bf16 and an f16 value); the K and
+// V scales are folded into the score scale and the output scale.
+//
+// With a bf16 query the softmax weights are fed as a bf16 pair hi + lo
+// (hi = bf16(p), lo = bf16(p - hi)), i.e. ~16 significant bits, so the only
+// 8-bit rounding left in the kernel is the stored output itself.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pkv {
+namespace mfma {
+
+constexpr float kTau = 8.0f;            // lazy-rescale threshold (base-2 units)
+constexpr uint32_t kOOB = 0x80000000u;  // past any descriptor range: reads 0
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes): stride 0, 32-bit format
+// word of the gfx9 family.
+__device__ inline rsrc_t make_rsrc(const char* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, (int)bytes,
+                                             0x00020000);
+}
+
+template <int BYTES>
+struct Buf;
+template <>
+struct Buf<16> {
+    typedef u32x4 T;
+    __device__ static inline T load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+};
+template <>
+struct Buf<8> {
+    typedef u32x2 T;
+    __device__ static inline T load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    }
+};
+template <>
+struct Buf<4> {
+    typedef uint32_t T;
+    __device__ static inline T load(rsrc_t r, uint32_t off) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+};
+
+template <class Q>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+    typedef __bf16 T;
+    typedef bf16x8 v8;
+    typedef bf16x4 v4;
+    static constexpr bool kSplitP = true;
+    __device__ static inline f32x4 qk(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 pv(v4 a, v4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+    }
+    // 4 E4M3 codes (one dword) -> 4 bf16.
+    __device__ static inline v4 from_fp8x4(uint32_t w) {
+        const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+        const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+        return v4{lo[0], lo[1], hi[0], hi[1]};
+    }
+};
+
+template <>
+struct Mfma<F16> {
+    typedef _Float16 T;
+    typedef f16x8 v8;
+    typedef f16x4 v4;
+    static constexpr bool kSplitP = false;
+    __device__ static inline f32x4 qk(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline f32x4 pv(v4 a, v4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static inline v4 from_fp8x4(uint32_t w) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        const f16x2 lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+        const f16x2 hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+        return v4{lo[0], lo[1], hi[0], hi[1]};
+    }
+};
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ inline int wave_incl_scan(int x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Wave-uniform addressing of one KV head's rows in the pool.
+struct Head {
+    const char* kbase;     // k_cache + head offset
+    const char* vbase;     // v_cache + head offset
+    uint32_t row_bytes;    // bytes between consecutive slots
+    uint32_t blk_bytes;    // bytes per block
+    uint32_t rec_bytes;    // descriptor range from a block base
+    uint32_t nb_last;      // last valid block id
+    int bs_shift;          // log2(block_size)
+};
+
+template <class C, int D>
+__device__ inline Head make_head(const DecodeParams& p, int h) {
+    constexpr int EB = C::kBytes;
+    Head hd;
+    const uint32_t head_off = (uint32_t)(h * D * EB);
+    hd.row_bytes = (uint32_t)(p.Hkv * D * EB);
+    hd.blk_bytes = (uint32_t)p.bs * hd.row_bytes;
+    hd.rec_bytes = hd.blk_bytes - head_off;
+    hd.kbase = (const char*)p.k + head_off;
+    hd.vbase = (const char*)p.v + head_off;
+    hd.nb_last = (uint32_t)p.NB - 1u;
+    hd.bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
+    return hd;
+}
+
+// PAIR: block size 8, so a 16-token tile spans two blocks.
+template <class Q, class C, int D, bool PAIR>
+struct TileMath {
+    typedef Mfma<Q> M;
+    typedef typename M::T T;
+    typedef typename M::v8 v8;
+    typedef typename M::v4 v4;
+    static constexpr bool kFp8 = std::is_same<C, FP8>::value;
+    static constexpr int EB = C::kBytes;           // cache bytes per element
+    static constexpr int KS = D / 32;              // QK contraction steps
+    static constexpr int NT = D / 16;              // PV column tiles = columns per lane
+    static constexpr int KL = kFp8 ? D / 64 : KS;  // 16-byte K loads per lane per tile
+    static constexpr int VB = NT * EB;             // bytes of one V row slice per lane
+    typedef T vrow __attribute__((ext_vector_type(NT)));
+    typedef typename Buf<VB>::T vraw;
+
+    struct Tile {
+        u32x4 k[KL];
+        vraw v[4];
+    };
+    // Running state of one (sequence piece, KV head): reference max and this
+    // lane's share of the sum for head lane%16, accumulator rows 4*(lane/16)+r.
+    struct Acc {
+        f32x4 o[NT];
+        float m;
+        float l;
+    };
+
+    int lane, g4, j16;
+    uint32_t kcol[KL];     // lane-constant byte offsets inside a slot row
+    uint32_t vcol;
+
+    __device__ TileMath() {
+        lane = threadIdx.x & 63;
+        g4 = lane >> 4;
+        j16 = lane & 15;
+#pragma unroll
+        for (int i = 0; i < KL; i++)
+            kcol[i] = kFp8 ? (uint32_t)(64 * i + 16 * g4) : (uint32_t)((32 * i + 8 * g4) * EB);
+        vcol = (uint32_t)(NT * j16 * EB);
+    }
+
+    // Query heads of the group as the B operand of the score product; `q`
+    // is row 0 of the group ([G][D]), heads past G read as zeros.
+    __device__ inline void load_q(const T* q, int G, v8 (&qb)[KS]) const {
+        const T* qrow = q + (size_t)j16 * D;
+#pragma unroll
+        for (int kk = 0; kk < KS; kk++) {
+            const int d0 = kFp8 ? (kk >> 1) * 64 + 16 * g4 + (kk & 1) * 8 : 32 * kk + 8 * g4;
+            if (j16 < G) qb[kk] = *(const v8*)(qrow + d0);
+            else qb[kk] = v8{};
+        }
+    }
+
+    __device__ inline void reset(Acc& a) const {
+#pragma unroll
+        for (int n = 0; n < NT; n++) a.o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        a.m = -INFINITY;
+        a.l = 0.0f;
+    }
+
+    // Issues the loads of the 16-token tile starting at token t0 (no wait).
+    // lim = index within the tile of its last live row (< 0: the whole tile
+    // is dead and reads zeros).  Block ids come from `win`, the table entries
+    // from block wb on (t0's block and, with PAIR, the next one must lie in
+    // the window when live).
+    __device__ inline void issue(const Head& hd, int t0, int lim, int wb, int win,
+                                 Tile& tl) const {
+        uint32_t pa = 0, pb = 0;
+        if (lim >= 0) {
+            const int blk = (t0 >> hd.bs_shift) - wb;
+            pa = (uint32_t)__builtin_amdgcn_readlane(win, blk);
+            pa = pa < hd.nb_last ? pa : hd.nb_last;
+            if (PAIR && lim >= 8) {
+                pb = (uint32_t)__builtin_amdgcn_readlane(win, blk + 1);
+                pb = pb < hd.nb_last ? pb : hd.nb_last;
+            }
+        }
+        const rsrc_t ka = make_rsrc(hd.kbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
+        const rsrc_t va = make_rsrc(hd.vbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
+        if constexpr (!PAIR) {
+            const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
+            const uint32_t krow = j16 <= lim ? (in_blk + (uint32_t)j16) * hd.row_bytes : kOOB;
+#pragma unroll
+            for (int i = 0; i < KL; i++) tl.k[i] = Buf<16>::load(ka, krow + kcol[i]);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int tv = 4 * g4 + r;
+                const uint32_t voff = tv <= lim ? (in_blk + (uint32_t)tv) * hd.row_bytes : kOOB;
+                tl.v[r] = Buf<VB>::load(va, voff + vcol);
+            }
+        } else {
+            // Each access is issued against both blocks' descriptors; the one
+            // not holding the row gets an out-of-range offset and reads 0.
+            const rsrc_t kb = make_rsrc(hd.kbase + (size_t)pb * hd.blk_bytes, hd.rec_bytes);
+            const rsrc_t vb = make_rsrc(hd.vbase + (size_t)pb * hd.blk_bytes, hd.rec_bytes);
+            const bool live_k = j16 <= lim;
+            const uint32_t ko = (uint32_t)(j16 & 7) * hd.row_bytes;
+            const uint32_t koa = live_k && j16 < 8 ? ko : kOOB;
+            const uint32_t kob = live_k && j16 >= 8 ? ko : kOOB;
+#pragma unroll
+            for (int i = 0; i < KL; i++)
+                tl.k[i] = Buf<16>::load(ka, koa + kcol[i]) | Buf<16>::load(kb, kob + kcol[i]);
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int tv = 4 * g4 + r;
+                const uint32_t vo = (uint32_t)(tv & 7) * hd.row_bytes;
+                const uint32_t voa = tv <= lim && tv < 8 ? vo : kOOB;
+                const uint32_t vob = tv <= lim && tv >= 8 ? vo : kOOB;
+                tl.v[r] = Buf<VB>::load(va, voa + vcol) | Buf<VB>::load(vb, vob + vcol);
+            }
+        }
+    }
+
+    // Consumes one tile: scores, online softmax update, PV accumulate.  lim
+    // as for issue(); rows past it get no weight.
+    __device__ inline void consume(Acc& a, const v8 (&qb)[KS], float scale_log2, int lim,
+                                   const Tile& cur) const {
+        f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < KL; i++) {
+            if constexpr (kFp8) {
+                const v4 a0 = M::from_fp8x4(cur.k[i][0]);
+                const v4 a1 = M::from_fp8x4(cur.k[i][1]);
+                const v4 a2 = M::from_fp8x4(cur.k[i][2]);
+                const v4 a3 = M::from_fp8x4(cur.k[i][3]);
+                const v8 k0 = v8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+                const v8 k1 = v8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+                sc = M::qk(k0, qb[2 * i], sc);
+                sc = M::qk(k1, qb[2 * i + 1], sc);
+            } else {
+                sc = M::qk(__builtin_bit_cast(v8, cur.k[i]), qb[i], sc);
+            }
+        }
+        float z[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const float x = sc[r] * scale_log2;
+            z[r] = (4 * g4 + r <= lim) ? x : -INFINITY;
+        }
+
+        // ---- online softmax: tile max over the 16 tokens of each head ----
+        float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        mx = strided_max<16>(mx);
+        const float m_new = mx > a.m + kTau ? mx : a.m;
+        if (__any(m_new != a.m)) {
+            const float alpha = m_new == a.m ? 1.0f : exp2f(a.m - m_new);  // 0 at first
+            a.l *= alpha;
+            // accumulator rows are heads 4*g4 + r; their alpha lives in lane 4*g4 + r
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float ar = __shfl(alpha, 4 * g4 + r, 64);
+#pragma unroll
+                for (int n = 0; n < NT; n++) a.o[n][r] *= ar;
+            }
+            a.m = m_new;
+        }
+        float pz[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) pz[r] = exp2f(z[r] - a.m);
+        a.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
+
+        // ---- weights as the A operand, value rows as the B operand ----
+        v4 p_hi, p_lo;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            p_hi[r] = (T)pz[r];
+            if constexpr (M::kSplitP) p_lo[r] = (T)(pz[r] - (float)p_hi[r]);
+        }
+        vrow vr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            if constexpr (kFp8) {
+                const uint32_t* w = (const uint32_t*)&cur.v[r];
+#pragma unroll
+                for (int q = 0; q < NT / 4; q++) {
+                    const v4 x = M::from_fp8x4(w[q]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) vr[r][4 * q + e] = x[e];
+                }
+            } else {
+                vr[r] = __builtin_bit_cast(vrow, cur.v[r]);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NT; n++) {
+            const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
+            a.o[n] = M::pv(p_hi, b, a.o[n]);
+        }
+        if constexpr (M::kSplitP) {
+#pragma unroll
+            for (int n = 0; n < NT; n++) {
+                const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
+                a.o[n] = M::pv(p_lo, b, a.o[n]);
+            }
+        }
+    }
+
+    // Epilogue.  Lane (g4, j16) holds accumulator rows head = 4*g4 + r and
+    // columns NT*j16 + n.  For every head < G, `out_row(head)` (when final)
+    // receives the normalised row in the query type; otherwise `m_at(head)`,
+    // `l_at(head)` and `o_at(head)` receive the partials (reference max in
+    // natural-log units, sum, unnormalised output times v_scale).
+    template <class OutRow, class MAt, class LAt, class OAt>
+    __device__ inline void finish(const Acc& a, int G, bool final_out, float v_scale,
+                                  OutRow out_row, MAt m_at, LAt l_at, OAt o_at) const {
+        const float l_tot = strided_sum<16>(a.l);     // head j16, over all tokens
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const int head = 4 * g4 + r;
+            const float lh = __shfl(l_tot, head, 64);
+            const float mh = __shfl(a.m, head, 64);
+            if (head >= G) continue;
+            if (final_out) {
+                const float inv = v_scale / lh;
+                vrow o;
+#pragma unroll
+                for (int n = 0; n < NT; n++) o[n] = (T)(a.o[n][r] * inv);
+                *(vrow*)(out_row(head) + NT * j16) = o;
+            } else {
+                if (j16 == 0) {
+                    *m_at(head) = mh * kLn2;
+                    *l_at(head) = lh;
+                }
+                float* o = o_at(head) + NT * j16;
+#pragma unroll
+                for (int n = 0; n < NT; n++) o[n] = a.o[n][r] * v_scale;
+            }
+        }
+    }
+};
+
+}  // namespace mfma
+}  // namespace pkv

@@ -58,16 +58,16 @@ class DevCase:
         c = self.c
         P = c.partition_size if partition_size is None else partition_size
         ws = workspace
-        if P > 0 and ws is None:
-            ws = pkv.allocate_workspace(c.S, c.Hq, c.D, c.max_seq_len, P)
+        if P != 0 and ws is None:
+            ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
         pkv.paged_attention_decode(self.out, self.query, self.k_cache, self.v_cache,
                                    self.tables, self.lens, scale=c.scale,
                                    max_seq_len=c.max_seq_len, k_scale=c.k_scale,
                                    v_scale=c.v_scale, partition_size=P, workspace=ws,
                                    algo=algo)
-        if P > 0:
-            pkv.paged_attention_reduce(self.out, ws, self.lens, max_seq_len=c.max_seq_len,
-                                       partition_size=P)
+        if P != 0:
+            pkv.paged_attention_reduce(self.out, ws, self.lens, num_kv_heads=c.Hkv,
+                                       max_seq_len=c.max_seq_len, partition_size=P)
         return self.out
 
 

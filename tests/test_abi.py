@@ -52,13 +52,30 @@ def test_status_strings(pkv):
 
 
 def test_workspace_bytes_layout(pkv):
-    S, Hq, D, L, P = 8, 64, 128, 131072, 512
+    S, Hq, Hkv, D, L, P = 8, 64, 8, 128, 131072, 512
     P_max = -(-L // P)
     n = S * Hq * P_max
     a = -(-4 * n // 256) * 256
-    assert pkv.decode_workspace_bytes(S, Hq, D, L, P) == 2 * a + 4 * n * D
-    assert pkv.decode_workspace_bytes(S, Hq, D, L, 0) == 0
-    assert pkv.decode_workspace_bytes(0, Hq, D, L, P) == 0
+    assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, L, P) == 2 * a + 4 * n * D
+    assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, L, 0) == 0
+    assert pkv.decode_workspace_bytes(0, Hq, Hkv, D, L, P) == 0
+    assert pkv.decode_workspace_bytes(S, Hq, 7, D, L, P) == 0      # Hq % Hkv != 0
+
+
+def test_balanced_workspace_bytes(pkv):
+    """Balanced split: a 256-byte header, the tile prefix of the sequences
+    (S + 1 words, padded to 256 bytes), then (m, l, o) entries for two pieces
+    per query head of the group per chunk, for the chunk bound 5 * 2048 + 8
+    of the largest grid; the lengths do not enter."""
+    Hq, Hkv, D, S = 32, 8, 128, 256
+    n = 2 * (5 * 2048 + 8) * (Hq // Hkv)
+    a = -(-4 * n // 256) * 256
+    off_m = -(-(256 + 4 * (S + 1)) // 256) * 256
+    expect = off_m + 2 * a + 4 * n * D
+    B = pkv.PARTITION_BALANCED
+    assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, 4096, B) == expect
+    assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, 131072, B) == expect
+    assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, 4096, -2) == 0
 
 
 FAKE = 1 << 20     # aligned, non-null; never dereferenced (calls fail first)
@@ -86,6 +103,11 @@ def decode_args(**kw):
     (dict(out=FAKE + 8), -6), (dict(k=FAKE + 4), -6), (dict(lens=FAKE + 2), -6),
     (dict(P=512), -5), (dict(P=512, ws=FAKE, ws_bytes=100), -5),
     (dict(scale=float("nan")), -2),
+    (dict(P=-2), -2), (dict(P=-1), -5), (dict(P=-1, ws=FAKE, ws_bytes=1000), -5),
+    (dict(P=-1, ws=FAKE, ws_bytes=1 << 40, qdt=0, cdt=0), -4),
+    (dict(P=-1, ws=FAKE, ws_bytes=1 << 40, algo=1), -4),
+    (dict(P=-1, ws=FAKE + 8, ws_bytes=1 << 40), -6),
+    (dict(P=-1, ws=FAKE, ws_bytes=1 << 40, S=8193, max_len=16), -4),
 ])
 def test_decode_rejects_bad_arguments(lib, kw, status):
     assert lib.pkv_paged_attention_decode(*decode_args(**kw)) == status
@@ -116,11 +138,13 @@ def test_cache_write_zero_tokens_is_a_noop(lib):
     (dict(odt=3), -3), (dict(odt=9), -3), (dict(S=0), -2), (dict(P=0), -2),
     (dict(P=24), -2), (dict(D=96), -4), (dict(out=None), -1), (dict(lens=None), -1),
     (dict(ws=None), -5), (dict(ws_bytes=10), -5), (dict(out=FAKE + 4), -6),
+    (dict(P=-2), -2), (dict(P=-1, ws=None), -5), (dict(P=-1, ws_bytes=4096), -5),
+    (dict(Hkv=0), -2), (dict(Hkv=7), -2), (dict(P=-1, S=8193), -4),
 ])
 def test_reduce_rejects_bad_arguments(lib, pkv, kw, status):
-    a = dict(out=FAKE, odt=2, ws=FAKE, ws_bytes=1 << 40, lens=FAKE, S=8, Hq=64, D=128,
-             max_len=4096, P=512, stream=None)
+    a = dict(out=FAKE, odt=2, ws=FAKE, ws_bytes=1 << 40, lens=FAKE, S=8, Hq=64, Hkv=8,
+             D=128, max_len=4096, P=512, stream=None)
     a.update(kw)
-    args = [a[k] for k in ("out", "odt", "ws", "ws_bytes", "lens", "S", "Hq", "D",
+    args = [a[k] for k in ("out", "odt", "ws", "ws_bytes", "lens", "S", "Hq", "Hkv", "D",
                            "max_len", "P", "stream")]
     assert lib.pkv_paged_attention_reduce(*args) == status

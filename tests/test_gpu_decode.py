@@ -134,7 +134,7 @@ def test_reduce_on_oracle_partials(dtype):
     o32 = np.nan_to_num(o).astype(np.float32)
     ref = oracle.partition_reduce(m32.astype(np.float64), l32.astype(np.float64),
                                   o32.astype(np.float64), c.seq_lens, partition_size=P)
-    nbytes = pkv.decode_workspace_bytes(c.S, c.Hq, c.D, c.max_seq_len, P)
+    nbytes = pkv.decode_workspace_bytes(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
     n = c.S * c.Hq * P_max
     a = -(-4 * n // 256) * 256
     ws = np.zeros(nbytes, np.uint8)
@@ -143,7 +143,7 @@ def test_reduce_on_oracle_partials(dtype):
     ws[2 * a:] = o32.reshape(-1).view(np.uint8)
     out = torch.full((c.S, c.Hq, c.D), 7.0, dtype=gpu_torch(dtype), device="cuda")
     pkv.paged_attention_reduce(out, torch.from_numpy(ws).cuda(), torch.from_numpy(c.seq_lens).cuda(),
-                               max_seq_len=c.max_seq_len, partition_size=P)
+                               num_kv_heads=c.Hkv, max_seq_len=c.max_seq_len, partition_size=P)
     got = from_dev(out)
     multi = c.seq_lens > P
     tol = {"f32": 1e-6, "f16": 1e-3, "bf16": 4e-3}[dtype]
@@ -330,3 +330,99 @@ def test_fuzz(algo, case):
     assert np.isfinite(out).all()
     bound = TOL[cd] + half_ulp(ref, qd)
     assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) - bound))
+
+
+# --- balanced split (persistent grid, whole-batch work cut evenly) ----------
+
+BAL = pkv.PARTITION_BALANCED
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_balanced_configs_full(cfg):
+    c = config(cfg)
+    check(c, gpu_run(c, "mfma", BAL), oracle_run(c))
+
+
+@pytest.mark.timeout(600)
+def test_balanced_config4_long_full():
+    c = config(4)
+    rows = [s * c.Hq + hq for s in range(c.S) for hq in (0, 7, 8, 33, 63)]
+    check(c, gpu_run(c, "mfma", BAL), oracle_run(c, rows), rows)
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_balanced_config5_fp8(bs):
+    c = config(5, bs)
+    check(c, gpu_run(c, "auto", BAL), oracle_run(c))
+
+
+def test_balanced_f32_is_unsupported():
+    c = config(1)
+    with pytest.raises(pkv.PagedKVError) as e:
+        gpu_run(c, "auto", BAL)
+    assert e.value.status == -4
+
+
+@pytest.mark.parametrize("lens", [[1], [3, 0, 17], [1, 1, 1, 0, 2], [16, 32, 48], [5000],
+                                  [0, 0, 700]])
+def test_balanced_small_batches(lens):
+    """Far fewer tiles than waves (most waves idle), zero-length rows written by
+    the reduce, one-token and tile-multiple lengths."""
+    c = workloads.make_case("bal-small", 80 + len(lens), [max(1, L) for L in lens], 16, 4, 128,
+                            16, q_dtype="bf16", cache_dtype="bf16",
+                            max_seq_len=max(max(lens), 1) + 5)
+    c.seq_lens = np.asarray(lens, np.int32)
+    out = gpu_run(c, "mfma", BAL)
+    ref = oracle_run(c)
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[s] == 0.0)
+    # few tokens: |out| can exceed 1, where the bf16 output's own rounding grows
+    bound = TOL["bf16"] + half_ulp(ref, "bf16")
+    excess = np.abs(out - ref) - bound
+    assert np.isfinite(out).all() and np.all(excess <= 0), float(np.max(excess))
+
+
+@pytest.mark.parametrize("case", list(fuzz_cases()), ids=lambda t: "fuzz%d" % t[0])
+@_skip_unsupported
+def test_balanced_fuzz(case):
+    i, qd, cd, G, Hkv, D, bs, lens, _ = case
+    c = workloads.make_case("bfuzz%d" % i, 5000 + i, lens, Hkv * G, Hkv, D, bs,
+                            q_dtype=qd, cache_dtype=cd, src_dtype=qd if cd == "fp8" else None,
+                            max_seq_len=int(max(lens)) + 37,
+                            append_last=(cd != "fp8" and i % 2 == 0))
+    out = gpu_run(c, "mfma", BAL)
+    ref = oracle_run(c)
+    bound = TOL[cd] + half_ulp(ref, qd)
+    assert np.all(np.abs(out - ref) <= bound), float(np.max(np.abs(out - ref) - bound))
+
+
+def test_balanced_block_relabelling_is_bit_exact():
+    c = small_gqa(seed=90)
+    a = gpu_run(c, "mfma", BAL)
+    rng = np.random.default_rng(91)
+    c2 = c.copy()
+    pi = rng.permutation(c.NB).astype(np.int32)
+    c2.k_cache = np.empty_like(c.k_cache)
+    c2.v_cache = np.empty_like(c.v_cache)
+    c2.k_cache[pi] = c.k_cache
+    c2.v_cache[pi] = c.v_cache
+    c2.block_tables = pi[c.block_tables]
+    c2.slot_mapping = (pi[c.slot_mapping // c.bs].astype(np.int64) * c.bs
+                       + c.slot_mapping % c.bs)
+    assert np.array_equal(a, gpu_run(c2, "mfma", BAL))
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_balanced_shared_prefix_equals_duplicated_bit_exact(bs):
+    c = workloads.config5(bs=bs, S=12)
+    a = gpu_run(c, "mfma", BAL)
+    assert np.array_equal(a, gpu_run(duplicate_prefix(c), "mfma", BAL))
+    check(c, a, oracle_run(c))
+
+
+def test_balanced_agrees_with_fixed_partitions():
+    c = small_gqa(seed=92, S=40)
+    a = gpu_run(c, "mfma", BAL)
+    b = gpu_run(c, "mfma", 256)
+    assert np.max(np.abs(a - b)) <= 4e-3
