@@ -7,12 +7,16 @@
 // differs.  Every (sequence, KV head) pair is a stream of 16-token tiles;
 // the streams are laid end to end (sequence-major, then KV head) and the
 // resulting T tiles are cut into chunks by the guided schedule of
-// kernels.hpp (large chunks first, small ones last).  The grid holds as many
-// wavefronts as the GPU runs at once; wave w starts on chunk w and then takes
-// chunks in order from a counter in the workspace.  Waves of one GPU do not
-// stream at one rate (waves of one CU finish a static even share tens of
-// microseconds apart), so the small chunks at the end keep every wave busy
-// until the batch is done.
+// kernels.hpp: nW chunks of the first size, nW of the second, then small
+// ones.  The grid holds as many wavefronts as the GPU runs at once (nW);
+// wave w works on chunk w, then takes chunks in order from a counter in the
+// workspace.  Waves of one GPU do not stream at one rate (on a loaded GPU
+// some take nearly twice as long as others over the same tiles), so the
+// smaller chunks that follow keep every wave busy until the batch is done.
+// Adds to the one counter are serialised (about 12 ns each), so a wave asks
+// for its next chunk only when a few rounds of its current one are left:
+// requests from all waves at once would delay the last by tens of
+// microseconds.
 //
 // A piece of a stream inside one chunk is a segment.  A segment that is a
 // whole stream writes its output rows directly.  Any other segment is the
@@ -45,6 +49,11 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 constexpr int kPlanThreads = 1024;
+// Tiles before the end of its chunk at which a wave asks for its next one.
+// Stepping into the next chunk without a stall needs about three rounds
+// (the index, then the table window of its first span); a request's latency
+// is about one round when requests are spread out.
+constexpr int kRequestAhead = 12;
 
 // Atomic add on a buffer word, returning the old value; lanes whose offset
 // is past the descriptor's range do nothing (and read 0).  Used with only
@@ -231,8 +240,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     // result still in flight is never copied or branched around, which would
     // make the loop wait for every load in flight.
     const rsrc_t ctr = make_rsrc((const char*)counter, 4);
-    int got = buffer_atomic_add_i32(1, ctr, lane == 0 ? 0 : (int)kOOB, 0, 0);
-    bool issued = true;                    // `got` is a chunk request in flight
+    int got = 0;
+    bool issued = false;                   // `got` is a chunk request in flight
     bool have = false;                     // `pend` holds an unused chunk index
     int pend = 0;
     bool chunks_left = true;
@@ -247,19 +256,19 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     };
 
     // ---- producer: walks the wave's chunks one span ahead of the issue ----
+    // Within a chunk the walk looks one span ahead; it steps into the next
+    // chunk only once that chunk's index is at hand.
     Walk pw;
     pw.start(pre, len, p.S, w, chunk_begin(q, w), chunk_begin(q, w + 1));
-    auto next_span = [&](Span& o) {
-        while (!pw.next(len, p.S, p.Hkv, bs_shift, o)) {
-            if (!chunks_left) return false;
-            const int c = take_chunk();
-            if (c >= q.chunks) {
-                chunks_left = false;
-                return false;
-            }
-            pw.start(pre, len, p.S, c, chunk_begin(q, c), chunk_begin(q, c + 1));
+    auto walk_next = [&](Span& o) { return pw.next(len, p.S, p.Hkv, bs_shift, o); };
+    auto chunk_next = [&](Span& o) {       // first span of the next chunk
+        const int c = take_chunk();
+        if (c >= q.chunks) {
+            chunks_left = false;
+            return false;
         }
-        return true;
+        pw.start(pre, len, p.S, c, chunk_begin(q, c), chunk_begin(q, c + 1));
+        return walk_next(o);               // chunks are never empty
     };
     // Window of 64 block-table entries from block sp.wb; entries at or past
     // ceil(L / bs) are outside the descriptor and read 0 (never touched).
@@ -282,12 +291,12 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     };
 
     Span ps, pn;
-    next_span(ps);                         // chunk w is not empty
+    walk_next(ps);                         // chunk w is not empty
     v8 qb[TM::KS];                         // query of the consumer's segment
     load_query(ps, true, qb);
     int win = load_window(ps, true);
     bool has_ps = true;
-    bool has_pn = next_span(pn);
+    bool has_pn = walk_next(pn);
     int win_n = load_window(pn, has_pn);   // window of pn
     Head hd = make_head<C, D>(p, ps.h());
     int prt = ps.t0;
@@ -297,6 +306,11 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     auto producer_advance = [&]() {
         prt += DEPTH;
         if (has_ps && prt >= ps.t1) {
+            if (!has_pn && chunks_left) {
+                // the next chunk's index is late: wait for it and its window
+                has_pn = chunk_next(pn);
+                if (has_pn) win_n = load_window(pn, true);
+            }
             has_ps = has_pn;
             if (has_ps) {
                 ps = pn;
@@ -304,16 +318,26 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
                 prt = ps.t0;
                 hd = make_head<C, D>(p, ps.h());
                 want_q = (ps.flags & kFirst) != 0;
-                has_pn = next_span(pn);
+                has_pn = walk_next(pn);
                 want_win = has_pn;
             }
+        }
+        if (has_ps && !has_pn && have) {   // look ahead into the next chunk
+            has_pn = chunk_next(pn);
+            want_win = has_pn;
         }
     };
     int wload;                              // window requested this round
     v8 qload[TM::KS];                       // query requested this round
     // End of a round: the requests.
     auto request = [&]() {
-        const bool want = !have && !issued && chunks_left;
+        // The next chunk's index is requested when the walk has reached the
+        // end of the current chunk and fewer than kRequestAhead of its tiles
+        // are left to issue: early enough to arrive in time, late enough
+        // that waves (which start together) ask at different times.
+        const int left = (ps.t1 - prt) + (has_pn ? pn.t1 - pn.t0 : 0);
+        const bool want = !have && !issued && chunks_left && has_ps && pw.rem <= 0 &&
+                          left < kRequestAhead;
         got = buffer_atomic_add_i32(1, ctr, lane == 0 && want ? 0 : (int)kOOB, 0, 0);
         issued = want;
         wload = load_window(pn, want_win);
@@ -349,7 +373,6 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     typename TM::Acc acc;
     tm.reset(acc);
     producer_advance();
-    take_chunk_index();                    // the request made at the start
     request();
 
     while (true) {
@@ -396,12 +419,14 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     }
 }
 
-// Tiles in flight per wavefront: two 16-token tiles (one of them in flight
-// during the arithmetic) keep the kernel at two waves per SIMD with the walk
-// state and the prefetched query of the next segment held in registers.
-template <bool PAIR>
+// Tiles in flight per wavefront, as many as fit beside the walk state and
+// the query rows at two waves per SIMD (at most 256 VGPRs): the loop is
+// bound by the latency of HBM, so the bytes a wave has in flight set its
+// rate.  An fp8 tile takes half the registers of a 16-bit one.
+template <class C, int D, bool PAIR>
 constexpr int pipeline_depth() {
-    return 2;
+    if (C::kBytes == 1) return PAIR ? 3 : 6;
+    return PAIR ? 2 : (D == 64 ? 4 : 3);
 }
 
 inline size_t lds_bytes(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
@@ -411,7 +436,7 @@ hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
     const dim3 grid((unsigned)((p.nW + kWaves - 1) / kWaves)), block(64 * kWaves);
     void* args[] = {const_cast<DecodeParams*>(&p)};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>()>),
+        reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>()>),
         grid, block, args, lds_bytes(p.S), st);
 }
 
@@ -419,7 +444,7 @@ template <class Q, class C, int D, bool PAIR>
 int resident_k(int S) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>()>,
+            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>()>,
             64 * kWaves, lds_bytes(S)) != hipSuccess)
         return 0;
     return blocks * kWaves;
