@@ -173,27 +173,28 @@ def cpu_baseline(c, budget_s: float = 20.0) -> dict:
 # Split used when --partition is not given: the fastest measured on MI355X
 # for each workload (the balanced split for the batch workloads; for the
 # shared-prefix fp8 workload, whose run is short, fixed 512-token partitions).
-DEFAULT_PARTITION = {1: 0, 2: -1, 3: -1, 4: -1, 5: 512}
+DEFAULT_PARTITION = {"tiny-f32": 0, "llama2-13b-mha": -1, "llama3-8b-gqa": -1,
+                     "long-context-gqa": -1, "shared-prefix-fp8": 512}
 
 
 def make_workload(args):
-    if args.config == 5:
-        c = workloads.config5(bs=args.bs)
+    if args.workload == "shared-prefix-fp8":
+        c = workloads.shared_prefix_fp8(bs=args.bs)
     else:
-        c = workloads.CONFIGS[args.config]()
-    P = DEFAULT_PARTITION[args.config] if args.partition is None else args.partition
+        c = workloads.WORKLOADS[args.workload]()
+    P = DEFAULT_PARTITION[args.workload] if args.partition is None else args.partition
     return c, P
 
 
 WORKLOAD_NAMES = {
-    1: "tiny fp32 paged decode: 4 seqs, L {7,16,33,100}, 4/4 heads, D 64, bs 16",
-    2: "Llama-2-13B-shaped MHA decode layer, fp16: 64 seqs, L~U[512,2048], 40/40 heads, "
+    "tiny-f32": "tiny fp32 paged decode: 4 seqs, L {7,16,33,100}, 4/4 heads, D 64, bs 16",
+    "llama2-13b-mha": "Llama-2-13B-shaped MHA decode layer, fp16: 64 seqs, L~U[512,2048], 40/40 heads, "
        "D 128, bs 16, +1 appended token/seq",
-    3: "Llama-3-8B-shaped GQA decode layer, bf16: 256 seqs, L~lognormal(median 1024, "
+    "llama3-8b-gqa": "Llama-3-8B-shaped GQA decode layer, bf16: 256 seqs, L~lognormal(median 1024, "
        "sigma 1, cap 4096), 32 q / 8 kv heads, D 128, bs 16, +1 appended token/seq",
-    4: "long-context GQA decode, bf16, split-K: 8 seqs, L {32,48,64,64,96,96,128,128}K, "
+    "long-context-gqa": "long-context GQA decode, bf16, split-K: 8 seqs, L {32,48,64,64,96,96,128,128}K, "
        "64 q / 8 kv heads, D 128, bs 32, partitions of 512",
-    5: "shared-prefix decode with fp8-e4m3 KV: 128 seqs, 1024-token shared prefix + "
+    "shared-prefix-fp8": "shared-prefix decode with fp8-e4m3 KV: 128 seqs, 1024-token shared prefix + "
        "tails U[16,512], 32 q / 8 kv heads, D 128",
 }
 
@@ -203,8 +204,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--bs", type=int, default=16, help="block size for config 5")
+    ap.add_argument("--workload", default="llama3-8b-gqa", choices=list(workloads.WORKLOADS))
+    ap.add_argument("--bs", type=int, default=16, help="block size of shared-prefix-fp8")
     ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition size: 0 one pass, P > 0 fixed partitions, "
@@ -227,7 +228,7 @@ def main() -> int:
     import paged_kv_cache_361_amd as pkv
 
     torch.cuda.set_device(0)
-    log("generating workload %d ..." % args.config)
+    log("generating workload %s ..." % args.workload)
     t0 = time.perf_counter()
     c, P = make_workload(args)
     log("generated in %.1fs: %d seqs, %d tokens, pool %d blocks" %
@@ -304,10 +305,14 @@ def main() -> int:
     dec_s = float(np.mean(dec_ms)) / 1e3
     value = nb["step"] / step_s / 1e12
     achieved = nb["decode_kernel"] / dec_s / 1e9
-    wl = WORKLOAD_NAMES[args.config]
-    if args.config == 5:
+    wl = WORKLOAD_NAMES[args.workload]
+    key = args.workload
+    if args.workload == "shared-prefix-fp8":
         wl += ", bs %d" % c.bs
-    traffic = traffic_from_profiles("config%d" % args.config, nb["decode_kernel"])
+        key += "-bs%d" % c.bs
+    if args.partition is not None:
+        key += "-P%d" % P
+    traffic = traffic_from_profiles(key, nb["decode_kernel"])
     res = {
         "metric": METRIC,
         "value": round(value, 4),

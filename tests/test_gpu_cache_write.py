@@ -78,9 +78,9 @@ def test_fp8_quantiser_f32_sample():
     assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 5])
-def test_config_append_matches_oracle(cfg):
-    c = workloads.config5(bs=16) if cfg == 5 else workloads.CONFIGS[cfg]()
+@pytest.mark.parametrize("cfg", ["llama2-13b-mha", "llama3-8b-gqa", "shared-prefix-fp8"])
+def test_workload_append_matches_oracle(cfg):
+    c = workloads.WORKLOADS[cfg]()
     kg, vg, ko, vo = _run_both(c.new_key, c.new_value, c.src_dtype, c.cache_dtype,
                                c.k_cache, c.v_cache, c.slot_mapping, c.k_scale, c.v_scale)
     assert np.array_equal(kg, ko) and np.array_equal(vg, vo)

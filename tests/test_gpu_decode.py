@@ -26,8 +26,8 @@ ALGOS = ["valu", "mfma"]
 
 
 @functools.lru_cache(maxsize=None)
-def config(n, *args):
-    return workloads.CONFIGS[n](*args)
+def workload(name, *args):
+    return workloads.WORKLOADS[name](*args)
 
 
 def _skip_unsupported(fn):
@@ -53,33 +53,33 @@ def check(c, out, ref, rows=None, tol=None):
 
 @pytest.mark.parametrize("algo", ALGOS)
 @_skip_unsupported
-def test_config1_tiny_fp32(algo):
-    c = config(1)
+def test_tiny_fp32(algo):
+    c = workload("tiny-f32")
     check(c, gpu_run(c, algo), oracle_run(c))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
 @_skip_unsupported
-def test_config2_mha_fp16_full(algo):
-    c = config(2)
+def test_llama2_13b_mha_fp16_full(algo):
+    c = workload("llama2-13b-mha")
     check(c, gpu_run(c, algo), oracle_run(c))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("P", [0, 512])
 @_skip_unsupported
-def test_config3_gqa_bf16_full(algo, P):
-    c = config(3)
+def test_llama3_8b_gqa_bf16_full(algo, P):
+    c = workload("llama3-8b-gqa")
     check(c, gpu_run(c, algo, P), oracle_run(c))
 
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("algo", ALGOS)
 @_skip_unsupported
-def test_config4_long_splitk_full(algo):
+def test_long_context_splitk_full(algo):
     """Full 32K-128K lengths, partitions of 512, reduced by the second kernel.
     The oracle computes a sample of rows, every sequence represented."""
-    c = config(4)
+    c = workload("long-context-gqa")
     rows = [s * c.Hq + hq for s in range(c.S) for hq in (0, 7, 8, 33, 63)]
     check(c, gpu_run(c, algo), oracle_run(c, rows), rows)
 
@@ -87,15 +87,15 @@ def test_config4_long_splitk_full(algo):
 @pytest.mark.parametrize("algo", ALGOS)
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @_skip_unsupported
-def test_config5_shared_prefix_fp8(algo, bs):
-    c = config(5, bs)
+def test_shared_prefix_fp8(algo, bs):
+    c = workload("shared-prefix-fp8", bs)
     check(c, gpu_run(c, algo), oracle_run(c))
 
 
 # --- split-K ---------------------------------------------------------------
 
 def small_gqa(seed=3, S=24, dtype="bf16", **kw):
-    return workloads.make_case("small-gqa", seed, lambda r: workloads.config3_lens(r, S),
+    return workloads.make_case("small-gqa", seed, lambda r: workloads.llama3_8b_gqa_lens(r, S),
                                32, 8, 128, kw.pop("bs", 16), q_dtype=dtype,
                                cache_dtype=dtype, max_seq_len=4096, **kw)
 
@@ -210,7 +210,7 @@ def duplicate_prefix(c):
 @pytest.mark.parametrize("bs", [8, 32])
 @_skip_unsupported
 def test_shared_prefix_equals_duplicated_bit_exact(algo, bs):
-    c = workloads.config5(bs=bs, S=12)
+    c = workloads.shared_prefix_fp8(bs=bs, S=12)
     t = duplicate_prefix(c)
     a = gpu_run(c, algo)
     b = gpu_run(t, algo)
@@ -337,27 +337,27 @@ def test_fuzz(algo, case):
 BAL = pkv.PARTITION_BALANCED
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
-def test_balanced_configs_full(cfg):
-    c = config(cfg)
+@pytest.mark.parametrize("cfg", ["llama2-13b-mha", "llama3-8b-gqa"])
+def test_balanced_batch_workloads_full(cfg):
+    c = workload(cfg)
     check(c, gpu_run(c, "mfma", BAL), oracle_run(c))
 
 
 @pytest.mark.timeout(600)
-def test_balanced_config4_long_full():
-    c = config(4)
+def test_balanced_long_context_full():
+    c = workload("long-context-gqa")
     rows = [s * c.Hq + hq for s in range(c.S) for hq in (0, 7, 8, 33, 63)]
     check(c, gpu_run(c, "mfma", BAL), oracle_run(c, rows), rows)
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
-def test_balanced_config5_fp8(bs):
-    c = config(5, bs)
+def test_balanced_shared_prefix_fp8(bs):
+    c = workload("shared-prefix-fp8", bs)
     check(c, gpu_run(c, "auto", BAL), oracle_run(c))
 
 
 def test_balanced_f32_is_unsupported():
-    c = config(1)
+    c = workload("tiny-f32")
     with pytest.raises(pkv.PagedKVError) as e:
         gpu_run(c, "auto", BAL)
     assert e.value.status == -4
@@ -415,7 +415,7 @@ def test_balanced_block_relabelling_is_bit_exact():
 
 @pytest.mark.parametrize("bs", [8, 32])
 def test_balanced_shared_prefix_equals_duplicated_bit_exact(bs):
-    c = workloads.config5(bs=bs, S=12)
+    c = workloads.shared_prefix_fp8(bs=bs, S=12)
     a = gpu_run(c, "mfma", BAL)
     assert np.array_equal(a, gpu_run(duplicate_prefix(c), "mfma", BAL))
     check(c, a, oracle_run(c))

@@ -172,7 +172,7 @@ def test_writer_then_gather_roundtrip(orc):
 def test_fp8_decode_uses_scaled_codes(orc):
     """fp8 cache: the oracle attends over decode(code) * scale; pinned by
     building the same K/V in f32 from torch-decoded codes."""
-    c = workloads.config5(bs=16, S=4)
+    c = workloads.shared_prefix_fp8(bs=16, S=4)
     kc, vc = c.k_cache.copy(), c.v_cache.copy()
     orc.reshape_and_cache(c.new_key, c.new_value, kc, vc, c.slot_mapping,
                           src_dtype="bf16", cache_dtype="fp8",

@@ -66,10 +66,10 @@ def test_decode_matches_dense_softmax_on_tiny_inputs(orc, seed):
             np.testing.assert_allclose(out[s, hq], ref, rtol=0, atol=1e-12)
 
 
-def test_config1_matches_dense_softmax(orc):
+def test_tiny_workload_matches_dense_softmax(orc):
     """Config 1 (tiny fp32): every row against the library brute force on the
     K/V the test reads back block by block through its own indexing."""
-    c = workloads.config1()
+    c = workloads.tiny_f32()
     out = orc.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables,
                            c.seq_lens, q_dtype="f32", cache_dtype="f32",
                            scale=c.scale)
@@ -143,7 +143,7 @@ def test_two_tokens_closed_form(orc):
 
 
 def test_zero_length_gives_zeros(orc):
-    c = workloads.config1()
+    c = workloads.tiny_f32()
     sl = c.seq_lens.copy()
     sl[1] = 0
     out = orc.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables, sl,
@@ -155,7 +155,7 @@ def test_zero_length_gives_zeros(orc):
 # --- paging invariants (bit-exact) ---------------------------------------
 
 def test_block_permutation_is_bit_invariant(orc):
-    c = workloads.config1()
+    c = workloads.tiny_f32()
     base = orc.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables,
                             c.seq_lens, q_dtype="f32", cache_dtype="f32", scale=c.scale)
     rng = np.random.default_rng(11)
@@ -220,7 +220,7 @@ def test_gqa_equals_mha_with_repeated_kv_heads(orc):
 def test_masked_tokens_never_contribute(orc):
     """Tokens at or past L hold NaN in every workload pool (tail of the last
     block, padding block); a finite output shows the oracle reads none."""
-    for c in (workloads.config1(), workloads.make_case(
+    for c in (workloads.tiny_f32(), workloads.make_case(
             "t", 5, [1, 8, 9, 31, 32, 33], 4, 2, 64, 8, q_dtype="bf16", cache_dtype="bf16")):
         assert np.isnan(workloads.bf16_values(c.k_cache) if c.cache_dtype == "bf16"
                         else c.k_cache).any()

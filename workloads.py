@@ -246,54 +246,56 @@ def make_case(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, *,
                 notes={"prefix_len": prefix_len, "append_last": append_last})
 
 
-# --- the five configurations --------------------------------------------
+# --- the five workloads ------------------------------------------------
 
-def config1() -> Case:
+def tiny_f32() -> Case:
     return make_case("tiny-fp32", 1, [7, 16, 33, 100], 4, 4, 64, 16,
                      q_dtype="f32", cache_dtype="f32", NB=64)
 
 
-def config2_lens(rng):
+def llama2_13b_mha_lens(rng):
     return rng.integers(512, 2048, size=64, endpoint=True)
 
 
-def config2() -> Case:
-    return make_case("llama2-13b-mha-fp16", 2, config2_lens, 40, 40, 128, 16,
+def llama2_13b_mha() -> Case:
+    return make_case("llama2-13b-mha-fp16", 2, llama2_13b_mha_lens, 40, 40, 128, 16,
                      q_dtype="f16", cache_dtype="f16", max_seq_len=2048,
                      append_last=True)
 
 
-def config3_lens(rng, S: int = 256):
+def llama3_8b_gqa_lens(rng, S: int = 256):
     x = rng.lognormal(mean=math.log(1024.0), sigma=1.0, size=S)
     return np.clip(np.rint(x), 1, 4096).astype(np.int64)
 
 
-def config3() -> Case:
-    return make_case("llama3-8b-gqa-bf16", 3, config3_lens, 32, 8, 128, 16,
+def llama3_8b_gqa() -> Case:
+    return make_case("llama3-8b-gqa-bf16", 3, llama3_8b_gqa_lens, 32, 8, 128, 16,
                      q_dtype="bf16", cache_dtype="bf16", max_seq_len=4096,
                      append_last=True)
 
 
-CONFIG4_LENS = [32, 48, 64, 64, 96, 96, 128, 128]
+LONG_CONTEXT_KTOKENS = [32, 48, 64, 64, 96, 96, 128, 128]
 
 
-def config4(scale_down: int = 1) -> Case:
+def long_context_gqa(scale_down: int = 1) -> Case:
     """Long-context split-K.  scale_down > 1 divides every length (for tests
     that keep the shape family but need the oracle to finish quickly)."""
-    lens = [k * 1024 // scale_down for k in CONFIG4_LENS]
+    lens = [k * 1024 // scale_down for k in LONG_CONTEXT_KTOKENS]
     return make_case("long-gqa-bf16-splitk", 4, lens, 64, 8, 128, 32,
                      q_dtype="bf16", cache_dtype="bf16",
                      max_seq_len=max(lens), partition_size=512)
 
 
-def config5_lens(rng, S: int = 128, prefix: int = 1024):
+def shared_prefix_lens(rng, S: int = 128, prefix: int = 1024):
     return prefix + rng.integers(16, 512, size=S, endpoint=True)
 
 
-def config5(bs: int = 16, S: int = 128) -> Case:
-    return make_case("shared-prefix-fp8-bs%d" % bs, 5, lambda r: config5_lens(r, S),
+def shared_prefix_fp8(bs: int = 16, S: int = 128) -> Case:
+    return make_case("shared-prefix-fp8-bs%d" % bs, 5, lambda r: shared_prefix_lens(r, S),
                      32, 8, 128, bs, q_dtype="bf16", cache_dtype="fp8",
                      src_dtype="bf16", max_seq_len=1536, prefix_len=1024)
 
 
-CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+WORKLOADS = {"tiny-f32": tiny_f32, "llama2-13b-mha": llama2_13b_mha,
+             "llama3-8b-gqa": llama3_8b_gqa, "long-context-gqa": long_context_gqa,
+             "shared-prefix-fp8": shared_prefix_fp8}
