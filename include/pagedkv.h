@@ -164,9 +164,10 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          head) pair's tokens in 16-token tiles, laid end to end -- is cut
  *          into chunks by a guided schedule (large chunks first, small ones
  *          last) and spread over a persistent grid of as many wavefronts as
- *          the GPU holds at once (at most 2048), which take chunks in order
- *          from a counter, so that ragged lengths and uneven wavefront speeds
- *          cost no load balance.  Two kernels are enqueued: a small plan
+ *          the GPU holds at once (at most 2048); each wavefront starts on a
+ *          chunk of its own and then takes chunks in order from a counter,
+ *          so that ragged lengths and uneven wavefront speeds cost no load
+ *          balance.  Two kernels are enqueued: a small plan
  *          kernel that prepares the workspace, then the decode kernel.  A
  *          (sequence, KV head) pair that falls into one chunk is finished
  *          here; for every other pair each chunk's piece leaves its partials
