@@ -20,7 +20,7 @@
 //           columns are assigned as d = 8*(lane%16) + n for tile n, which turns
 //           the transpose the instruction needs into register permutes.
 //
-// Memory side.  Every K/V access is a buffer load whose 128-bit descriptor
+// Memory side.  Every K/V access is a non-temporal buffer load whose 128-bit descriptor
 // holds the 64-bit base of one physical block (plus the head offset) in
 // scalar registers, with 32-bit per-lane offsets inside the block.  Rows past
 // the end of a sequence get an offset beyond the descriptor's range: the
@@ -54,6 +54,11 @@ namespace mfma {
 
 constexpr float kTau = 8.0f;            // lazy-rescale threshold (base-2 units)
 constexpr uint32_t kOOB = 0x80000000u;  // past any descriptor range: reads 0
+// Cache policy of the K/V loads: non-temporal.  Every K/V byte is read once
+// per call, so keeping it out of the caches' replacement costs nothing, and
+// on MI355X random 4 KiB block slices stream about 14% faster this way
+// (6.9 against 6.06 TB/s in a read-only probe of the same pattern).
+constexpr int kStream = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -72,6 +77,9 @@ struct Buf<16> {
     __device__ static inline T load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     }
+    __device__ static inline T stream(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream));
+    }
 };
 template <>
 struct Buf<8> {
@@ -79,12 +87,18 @@ struct Buf<8> {
     __device__ static inline T load(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
     }
+    __device__ static inline T stream(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kStream));
+    }
 };
 template <>
 struct Buf<4> {
     typedef uint32_t T;
     __device__ static inline T load(rsrc_t r, uint32_t off) {
         return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+    __device__ static inline T stream(rsrc_t r, uint32_t off) {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kStream);
     }
 };
 
@@ -252,12 +266,12 @@ struct TileMath {
             const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
             const uint32_t krow = j16 <= lim ? (in_blk + (uint32_t)j16) * hd.row_bytes : kOOB;
 #pragma unroll
-            for (int i = 0; i < KL; i++) tl.k[i] = Buf<16>::load(ka, krow + kcol[i]);
+            for (int i = 0; i < KL; i++) tl.k[i] = Buf<16>::stream(ka, krow + kcol[i]);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int tv = 4 * g4 + r;
                 const uint32_t voff = tv <= lim ? (in_blk + (uint32_t)tv) * hd.row_bytes : kOOB;
-                tl.v[r] = Buf<VB>::load(va, voff + vcol);
+                tl.v[r] = Buf<VB>::stream(va, voff + vcol);
             }
         } else {
             // Each access is issued against both blocks' descriptors; the one
@@ -270,14 +284,14 @@ struct TileMath {
             const uint32_t kob = live_k && j16 >= 8 ? ko : kOOB;
 #pragma unroll
             for (int i = 0; i < KL; i++)
-                tl.k[i] = Buf<16>::load(ka, koa + kcol[i]) | Buf<16>::load(kb, kob + kcol[i]);
+                tl.k[i] = Buf<16>::stream(ka, koa + kcol[i]) | Buf<16>::stream(kb, kob + kcol[i]);
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int tv = 4 * g4 + r;
                 const uint32_t vo = (uint32_t)(tv & 7) * hd.row_bytes;
                 const uint32_t voa = tv <= lim && tv < 8 ? vo : kOOB;
                 const uint32_t vob = tv <= lim && tv >= 8 ? vo : kOOB;
-                tl.v[r] = Buf<VB>::load(va, voa + vcol) | Buf<VB>::load(vb, vob + vcol);
+                tl.v[r] = Buf<VB>::stream(va, voa + vcol) | Buf<VB>::stream(vb, vob + vcol);
             }
         }
     }
