@@ -167,8 +167,7 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          the GPU holds at once (at most 2048); each wavefront starts on a
  *          chunk of its own and then takes chunks in order from a counter,
  *          so that ragged lengths and uneven wavefront speeds cost no load
- *          balance.  Two kernels are enqueued: a small plan
- *          kernel that prepares the workspace, then the decode kernel.  A
+ *          balance.  One kernel is enqueued.  A
  *          (sequence, KV head) pair that falls into one chunk is finished
  *          here; for every other pair each chunk's piece leaves its partials
  *          in `workspace` (layout private to the library: a header, the tile
@@ -176,7 +175,11 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          query head of the group per chunk), and pkv_paged_attention_reduce
  *          must run next on the same stream with partition_size =
  *          PKV_PARTITION_BALANCED; it also writes the zero rows of sequences
- *          with L <= 0.  The workspace needs no initialisation.  Requires
+ *          with L <= 0.  The workspace needs no initialisation: its chunk
+ *          counter carries the number of the call that last used it, and
+ *          each call takes it over at its first request, whatever it held.
+ *          Calls sharing one workspace must not overlap in time (use one
+ *          stream).  Requires
  *          num_seqs * num_kv_heads * ceil(max_seq_len / 16) < 2^31.
  *
  * pkv_decode_workspace_bytes gives the workspace size for either split mode.

@@ -5,12 +5,25 @@
 // anything is enqueued.
 #include "pagedkv.h"
 
+#include <atomic>
+#include <chrono>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace {
 
 using namespace pkv;
+
+// Numbers the balanced decode calls of the process.  A call tells the
+// chunk-counter state left in its workspace by an earlier call from its own
+// by this number (kernels.hpp), so numbers must not repeat for a long time:
+// a 32-bit sequence, started from the clock.
+uint32_t next_call_number() {
+    static std::atomic<uint32_t> next{
+        (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count()};
+    return next.fetch_add(1, std::memory_order_relaxed);
+}
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -223,6 +236,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
             return PKV_ERR_UNSUPPORTED;
         p.P = 0;
         p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size, num_seqs);
+        p.epoch = next_call_number();
         return launch_status(launch_decode_balanced(q_dtype, cache_dtype, p, stream));
     }
     if (algo == PKV_ALGO_MFMA || (algo == PKV_ALGO_AUTO && mfma_ok)) {

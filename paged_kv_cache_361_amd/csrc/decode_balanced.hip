@@ -25,10 +25,12 @@
 // workspace; pkv_paged_attention_reduce merges, for each stream spread over
 // chunks c0..c1, the entries of those chunks.
 //
-// Two kernels per call: a one-workgroup plan kernel writes the exclusive
-// tile prefix of the sequences, the schedule header and a zeroed chunk
-// counter into the workspace, then the decode kernel runs.  (A kernel rather
-// than a memset keeps the call safe to capture in a graph.)
+// One kernel per call.  Every workgroup computes the tile prefix of the
+// sequences in LDS; workgroup 0 also writes it and the schedule into the
+// workspace for the reduce.  The chunk counter needs no reset before the
+// call (no memset, so the call can be captured in a graph): it carries the
+// number of the call that owns it, and the call's first request takes it
+// over (kernels.hpp).
 //
 // Pipeline.  The matrix-core tile of tile_mfma.hpp runs on a ring of DEPTH
 // tile buffers.  Segments are cut into spans of at most 64 blocks (one
@@ -48,7 +50,6 @@ namespace {
 using namespace mfma;
 
 constexpr int kWaves = 4;
-constexpr int kPlanThreads = 1024;
 // Tiles before the end of its chunk at which a wave asks for its next one.
 // Stepping into the next chunk without a stall needs about three rounds
 // (the index, then the table window of its first span), and a request's
@@ -62,31 +63,79 @@ constexpr int kRequestAhead = 8;
 // lane 0 in range, so the wave adds once without a branch around the
 // instruction (a branch around a memory instruction would cost the loop a
 // full wait on every load in flight).
-__device__ int buffer_atomic_add_i32(int v, rsrc_t r, int off, int soff, int aux)
-    __asm("llvm.amdgcn.raw.ptr.buffer.atomic.add.i32");
+__device__ long long buffer_atomic_add_i64(long long v, rsrc_t r, int off, int soff, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.atomic.add.i64");
+
+// The chunk counter (kernels.hpp): whether a value read from it belongs to
+// call `epoch`.
+__device__ inline bool counter_live(uint64_t v, uint32_t epoch) {
+    return (uint32_t)(v >> 32) == epoch && ((uint32_t)v & ~kCountMask) == kCountTag;
+}
+
+// A request found the counter not yet this call's.  Call numbers increase,
+// so the call's range of values, (epoch << 32 | kCountTag) and up, lies
+// above whatever an earlier call left: a 64-bit max installs the call's base
+// whoever gets there first (and undoes any stale adds), then an add takes an
+// index as usual.  A word above the call's range (memory never written by a
+// call, another mode's data, or call numbers wrapping round) is replaced by
+// an exchange that takes index 0.  At most three atomics and no retry loop,
+// so no number of wavefronts arriving together can keep one waiting.  Two
+// exchanges in one call can hand out some indices twice; a chunk computed
+// twice writes the same values twice, and no index is ever skipped.
+__device__ inline int counter_rebase(unsigned long long* ctr, uint32_t epoch) {
+    int k = 0;
+    if ((threadIdx.x & 63) == 0) {
+        const unsigned long long base = ((unsigned long long)epoch << 32) | kCountTag;
+        atomicMax(ctr, base);
+        const unsigned long long old = atomicAdd(ctr, 1ull);
+        if (counter_live(old, epoch)) k = (int)((uint32_t)old & kCountMask);
+        else atomicExch(ctr, base | 1u);          // k = 0
+    }
+    return __builtin_amdgcn_readfirstlane(k);
+}
 
 __device__ inline int seq_tiles(int L) { return L > 0 ? (L + 15) >> 4 : 0; }
 
-// ---- plan ----------------------------------------------------------------
+// A copy of a loaded value made by an instruction the compiler cannot see
+// through, so that it waits for that one load here.  Used on rare paths
+// whose loaded registers merge into the main loop: without it the compiler
+// would treat the register as possibly in flight on the common path too and
+// wait there for every load issued.
+__device__ inline int settled(int x) {
+    int y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
 
-__global__ __launch_bounds__(kPlanThreads) void balanced_plan_kernel(DecodeParams p) {
-    __shared__ int wave_sum[kPlanThreads / 64];
+// ---- tile prefix ----------------------------------------------------------
+
+// Every workgroup computes the batch's tile prefix in LDS from the lengths:
+// len[s] = clamped length of sequence s, pre[s] = tiles of the streams of
+// all sequences before s (pre[S] = T).
+__device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
+    __shared__ int wave_sum[kWaves];
+    constexpr int NT = 64 * kWaves;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
-    const int per = (p.S + kPlanThreads - 1) / kPlanThreads;   // sequences per thread
+    // lengths into LDS with coalesced loads, then a scan over contiguous
+    // ranges of `per` sequences per thread
+#pragma unroll 4
+    for (int s = tid; s < p.S; s += NT) len[s] = min(p.lens[s], p.len_cap);
+    __syncthreads();
+    const int per = (p.S + NT - 1) / NT;
     const int s0 = tid * per;
     int n = 0;
     for (int i = 0; i < per; i++) {
         const int s = s0 + i;
-        if (s < p.S) n += seq_tiles(min(p.lens[s], p.len_cap)) * p.Hkv;
+        if (s < p.S) n += seq_tiles(len[s]) * p.Hkv;
     }
     const int incl = wave_incl_scan(n);
     if (lane == 63) wave_sum[wv] = incl;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
-    for (int k = 0; k < kPlanThreads / 64; k++) {
+    for (int k = 0; k < kWaves; k++) {
         before += k < wv ? wave_sum[k] : 0;
         total += wave_sum[k];
     }
@@ -94,25 +143,12 @@ __global__ __launch_bounds__(kPlanThreads) void balanced_plan_kernel(DecodeParam
     for (int i = 0; i < per; i++) {
         const int s = s0 + i;
         if (s < p.S) {
-            p.ws_pre[s] = run;
-            run += seq_tiles(min(p.lens[s], p.len_cap)) * p.Hkv;
+            pre[s] = run;
+            run += seq_tiles(len[s]) * p.Hkv;
         }
     }
-    if (tid == 0) {
-        const Sched q = make_sched(total, p.nW);
-        p.ws_pre[p.S] = total;
-        int32_t* h = p.ws_hdr;
-        h[kHdrMagic] = kBalancedMagic;
-        h[kHdrNW] = p.nW;
-        h[kHdrHkv] = p.Hkv;
-        h[kHdrG] = p.G;
-        h[kHdrT] = total;
-        h[kHdrC1] = q.C1;
-        h[kHdrC2] = q.C2;
-        h[kHdrC3] = q.C3;
-        h[kHdrChunks] = q.chunks;
-        h[kHdrCounter] = 0;
-    }
+    if (tid == 0) pre[p.S] = total;
+    __syncthreads();
 }
 
 // ---- decode ----------------------------------------------------------------
@@ -217,20 +253,32 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     extern __shared__ int lds[];
     int* pre = lds;                        // [S + 1] tile prefix
     int* len = lds + p.S + 1;              // [S] clamped lengths
-    for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) {
-        pre[i] = p.ws_pre[i];
-        if (i < p.S) len[i] = min(p.lens[i], p.len_cap);
-    }
-    __syncthreads();
+    int32_t* hdr = p.ws_hdr;
+    wg_prefix(p, pre, len);
 
     const TM tm;
     const int lane = tm.lane;
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Sched q = make_sched(__builtin_amdgcn_readfirstlane(pre[p.S]), p.nW);
-    if (w >= q.chunks) return;
+    if (blockIdx.x == 0) {
+        // what the reduce needs: the prefix and the schedule
+        for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) p.ws_pre[i] = pre[i];
+        if (threadIdx.x == 0) {
+            hdr[kHdrMagic] = kBalancedMagic;
+            hdr[kHdrNW] = p.nW;
+            hdr[kHdrHkv] = p.Hkv;
+            hdr[kHdrG] = p.G;
+            hdr[kHdrT] = q.T;
+            hdr[kHdrC1] = q.C1;
+            hdr[kHdrC2] = q.C2;
+            hdr[kHdrC3] = q.C3;
+            hdr[kHdrChunks] = q.chunks;
+        }
+    }
+    if (w >= q.chunks || w >= p.nW) return;
     const int G = p.G;
     const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
-    int* counter = p.ws_hdr + kHdrCounter;
+    unsigned long long* counter = (unsigned long long*)(hdr + kHdrCounter);
 
     // ---- requests made one round ahead ---------------------------------
     // The index of the wave's next chunk (the counter's atomic add), the
@@ -241,18 +289,25 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     // after the consumer has waited for the tiles issued before them.  A
     // result still in flight is never copied or branched around, which would
     // make the loop wait for every load in flight.
-    const rsrc_t ctr = make_rsrc((const char*)counter, 4);
-    int got = 0;
+    const rsrc_t ctr = make_rsrc((const char*)counter, 8);
+    long long got = 0;
     bool issued = false;                   // `got` is a chunk request in flight
     bool have = false;                     // `pend` holds an unused chunk index
     int pend = 0;
     bool chunks_left = true;
+    // chunk index (counter-relative) from a value an add returned
+    auto index_of = [&](long long v) {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        const uint64_t u = ((uint64_t)hi << 32) | lo;
+        if (counter_live(u, p.epoch)) return (int)(lo & kCountMask);
+        return counter_rebase(counter, p.epoch);
+    };
     auto take_chunk = [&]() {
         int k;
         if (have) k = pend;
-        else if (issued) k = __builtin_amdgcn_readfirstlane(got);
-        else k = __builtin_amdgcn_readfirstlane(
-                 buffer_atomic_add_i32(1, ctr, lane == 0 ? 0 : (int)kOOB, 0, 0));
+        else if (issued) k = index_of(got);
+        else k = index_of(buffer_atomic_add_i64(1, ctr, lane == 0 ? 0 : (int)kOOB, 0, 0));
         have = issued = false;
         return q.nW + k;
     };
@@ -311,7 +366,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
             if (!has_pn && chunks_left) {
                 // the next chunk's index is late: wait for it and its window
                 has_pn = chunk_next(pn);
-                if (has_pn) win_n = load_window(pn, true);
+                if (has_pn) win_n = settled(load_window(pn, true));
             }
             has_ps = has_pn;
             if (has_ps) {
@@ -340,7 +395,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
         const int left = (ps.t1 - prt) + (has_pn ? pn.t1 - pn.t0 : 0);
         const bool want = !have && !issued && chunks_left && has_ps && pw.rem <= 0 &&
                           left < kRequestAhead;
-        got = buffer_atomic_add_i32(1, ctr, lane == 0 && want ? 0 : (int)kOOB, 0, 0);
+        got = buffer_atomic_add_i64(1, ctr, lane == 0 && want ? 0 : (int)kOOB, 0, 0);
         issued = want;
         wload = load_window(pn, want_win);
         load_query(ps, want_q, qload);
@@ -349,7 +404,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodePara
     // request, which reuses it.
     auto take_chunk_index = [&]() {
         if (issued) {
-            pend = __builtin_amdgcn_readfirstlane(got);
+            pend = index_of(got);
             have = true;
             issued = false;
         }
@@ -482,8 +537,6 @@ int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S) {
 hipError_t launch_decode_balanced(int qdt, int cdt, const DecodeParams& p, hipStream_t st) {
     if (!decode_mfma_supported(qdt, cdt, p.D, p.G)) return hipErrorInvalidValue;
     if (p.S > kBalancedMaxSeqs || p.nW < 1 || p.nW > kBalancedMaxWaves) return hipErrorInvalidValue;
-    hipError_t e = launch_kernel(balanced_plan_kernel, dim3(1), dim3(kPlanThreads), st, p);
-    if (e != hipSuccess) return e;
     if (qdt == kBF16) {
         if (cdt == kFP8) return launch_d<BF16, FP8>(p, st);
         return launch_d<BF16, BF16>(p, st);

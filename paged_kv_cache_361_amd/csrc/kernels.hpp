@@ -35,6 +35,7 @@ struct DecodeParams {
     int32_t* ws_hdr;       // balanced mode: header of the workspace
     int32_t* ws_pre;       // balanced mode: tile prefix of the sequences [S + 1]
     int nW;                // balanced mode: wavefronts of the persistent grid
+    uint32_t epoch;        // balanced mode: this call's number (never repeats soon)
     int S, Hq, Hkv, D, G, bs, NB, max_blocks;
     int len_cap;           // min(max_seq_len, max_blocks * bs)
     int P;                 // partition size, 0 = one pass
@@ -67,11 +68,21 @@ struct ReduceParams {
 // rest from a counter, and the reduce finds a stream's chunks with
 // chunk_of().
 //
-// Workspace: a 256-byte header (words below; the chunk counter alone in
-// word 32), the exclusive tile prefix of the sequences (S + 1 words) from
-// byte 256, then (m, l, o) entries, two per query head of the group per
-// chunk.
+// Workspace: a 256-byte header, the exclusive tile prefix of the sequences
+// (S + 1 words) from byte 256, then (m, l, o) entries, two per query head of
+// the group per chunk.  Header words 0-8 describe the split for the reduce
+// (written by each decode call).  Words 32-33 (their own 128-byte line) hold
+// the chunk counter, a 64-bit word: high half the number of the call that
+// owns it, low half kCountTag | count.  Nothing resets it between calls: a
+// call's first requests find another call's number (or whatever the memory
+// held) and raise the word to the call's own base by a 64-bit max (call
+// numbers increase; a word above the call's range is replaced by an
+// exchange); every later request of the call adds one.  A stale word
+// passes for live only if it carries the call's own 32-bit number and the
+// 8-bit tag.
 constexpr int32_t kBalancedMagic = 0x504B5642;
+constexpr uint32_t kCountTag = 0xA5000000u;
+constexpr uint32_t kCountMask = 0x00FFFFFFu;
 enum BalancedHeader : int {
     kHdrMagic = 0, kHdrNW = 1, kHdrHkv = 2, kHdrG = 3, kHdrT = 4, kHdrC1 = 5, kHdrC2 = 6,
     kHdrC3 = 7, kHdrChunks = 8, kHdrCounter = 32

@@ -72,11 +72,30 @@ class DevCase:
 
 
 def gpu_run(c: workloads.Case, algo="auto", partition_size=None) -> np.ndarray:
+    """One decode (and reduce) of the case.  For the balanced split the call
+    runs three times on one workspace: the first finds it fresh and assigns
+    chunks statically, the next two take them from the workspace counter
+    (the second also checks that the first counter call left the counter
+    reset).  All three must agree bit for bit: they cut the batch into the
+    same chunks."""
     d = DevCase(c)
     d.write()
-    d.decode(algo, partition_size)
-    torch.cuda.synchronize()
-    return from_dev(d.out)
+    P = c.partition_size if partition_size is None else partition_size
+    if P != pkv.PARTITION_BALANCED:
+        d.decode(algo, partition_size)
+        torch.cuda.synchronize()
+        return from_dev(d.out)
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
+    runs = []
+    for _ in range(3):
+        d.out.fill_(float("nan"))
+        d.decode(algo, P, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append(d.out.clone())
+    for r in runs[1:]:
+        assert torch.equal(r.view(torch.uint8), runs[0].view(torch.uint8)), \
+            "balanced split: calls on one workspace disagree"
+    return from_dev(runs[0])
 
 
 def oracle_caches(c: workloads.Case):

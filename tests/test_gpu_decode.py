@@ -421,6 +421,53 @@ def test_balanced_shared_prefix_equals_duplicated_bit_exact(bs):
     check(c, a, oracle_run(c))
 
 
+def test_balanced_workspace_shared_with_fixed_partitions():
+    """A fixed-partition call that writes over the balanced header (its
+    partials start at byte 0) must leave the next balanced call correct: it
+    finds the counter state broken, assigns chunks statically and readies the
+    counter; the call after it uses the counter again.  All balanced calls
+    agree bit for bit."""
+    c = small_gqa(seed=93, S=40)
+    d = DevCase(c)
+    d.write()
+    nb = max(pkv.decode_workspace_bytes(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
+             for P in (BAL, 256))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for P in (BAL, BAL, 256, BAL, BAL, 256, BAL):
+        d.out.fill_(float("nan"))
+        d.decode("mfma", P, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((P, d.out.clone()))
+    bal = [o for P, o in outs if P == BAL]
+    for o in bal[1:]:
+        assert torch.equal(o.view(torch.uint8), bal[0].view(torch.uint8))
+    ref = oracle_run(c)
+    check(c, from_dev(bal[0]), ref)
+    check(c, from_dev(outs[2][1]), ref)
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, 0x5A])
+def test_balanced_workspace_contents_do_not_matter(fill):
+    """The chunk counter in a fresh workspace holds whatever the memory held:
+    zeros (below any call's range), all ones (above it) or another pattern.
+    Each must give the right result, on the first call and the next ones."""
+    c = small_gqa(seed=94, S=64)
+    d = DevCase(c)
+    d.write()
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, BAL)
+    ws.fill_(fill)
+    outs = []
+    for _ in range(3):
+        d.out.fill_(float("nan"))
+        d.decode("mfma", BAL, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(d.out.clone())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.uint8), outs[0].view(torch.uint8))
+    check(c, from_dev(outs[0]), oracle_run(c))
+
+
 def test_balanced_agrees_with_fixed_partitions():
     c = small_gqa(seed=92, S=40)
     a = gpu_run(c, "mfma", BAL)
