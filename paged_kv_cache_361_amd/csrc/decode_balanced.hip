@@ -246,7 +246,7 @@ struct Walk {
 };
 
 template <class Q, class C, int D, bool PAIR, int DEPTH>
-__global__ __launch_bounds__(64 * kWaves) void decode_balanced_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kWaves, 2) void decode_balanced_kernel(DecodeParams p) {
     typedef TileMath<Q, C, D, PAIR> TM;
     typedef typename TM::T T;
     typedef typename TM::v8 v8;
