@@ -49,6 +49,9 @@ def _load():
     lib.orc_paged_decode.argtypes = [P, P, I, P, P, I, P, I, P, I, I, I, I, I, I,
                                      D, D, D, P, I, I]
     lib.orc_paged_decode.restype = I
+    lib.orc_paged_multi.argtypes = [P, P, I, P, P, I, P, I, P, P, I, I, I, I, I, I,
+                                    D, D, D, P, I, I]
+    lib.orc_paged_multi.restype = I
     lib.orc_paged_partials.argtypes = [P, P, P, P, I, P, P, I, P, I, P, I, I, I, I,
                                        I, I, D, D, D, I, I, I]
     lib.orc_paged_partials.restype = I
@@ -152,6 +155,40 @@ def paged_decode(query, k_cache, v_cache, block_tables, seq_lens, *,
         _ptr(seq_lens), S, Hq, Hkv, D, bs, NB, float(scale), float(k_scale),
         float(v_scale), _ptr(r), 0 if r is None else r.size, int(threads))
     _check(rc, "paged_decode")
+    return out
+
+
+def paged_multi(query, k_cache, v_cache, block_tables, seq_lens, query_start, *,
+                q_dtype: str, cache_dtype: str, scale: float,
+                k_scale: float = 1.0, v_scale: float = 1.0,
+                rows: Optional[Sequence[int]] = None,
+                threads: int = 0) -> np.ndarray:
+    """Several new query tokens per sequence (chunked prefill, speculative
+    verification).  query [total_q, Hq, D]; query_start [S + 1] (exclusive
+    prefix of the per-sequence query counts Qn).  Query token i of sequence
+    s sits at position seq_lens[s] - Qn + i and sees tokens up to it.
+    Returns float64 [total_q, Hq, D]; ``rows`` (flat qtok*Hq + hq) restricts
+    the work, the others are NaN."""
+    query = _c(query, _NP[q_dtype])
+    k_cache = _c(k_cache, _NP[cache_dtype])
+    v_cache = _c(v_cache, _NP[cache_dtype])
+    block_tables = _c(block_tables, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    query_start = _c(query_start, np.int32)
+    TQ, Hq, D = query.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    S = seq_lens.shape[0]
+    assert D2 == D and block_tables.shape[0] == S and query_start.shape == (S + 1,)
+    assert int(query_start[-1]) == TQ
+    out = np.full((TQ, Hq, D), np.nan, np.float64)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    rc = _load().orc_paged_multi(
+        _ptr(out), _ptr(query), _DT[q_dtype], _ptr(k_cache), _ptr(v_cache),
+        _DT[cache_dtype], _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), _ptr(query_start), S, Hq, Hkv, D, bs, NB, float(scale),
+        float(k_scale), float(v_scale), _ptr(r), 0 if r is None else r.size,
+        int(threads))
+    _check(rc, "paged_multi")
     return out
 
 

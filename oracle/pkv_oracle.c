@@ -332,53 +332,63 @@ static int orc_check(const orc_problem* p)
     return ORC_OK;
 }
 
-/* One output row out[D] for (s, hq): steps 1-4 of the definition. */
-static int orc_decode_row(const orc_problem* p, int s, int hq, double* out)
+/* One output row out[D]: query vector q[D] of a head reading KV head h of
+ * sequence s, attending to tokens [0, n) of the sequence -- steps 1-4 of
+ * the definition.  n <= 0 gives a zero row. */
+static int orc_attend_row(const orc_problem* p, int s, int h, const double* q, int n,
+                          double* out)
 {
-    int G = p->Hq / p->Hkv;
-    int h = hq / G;
-    int L = p->seq_lens[s];
-    if (L <= 0) {
+    if (n <= 0) {
         for (int d = 0; d < p->D; d++)
             out[d] = 0.0;
         return ORC_OK;
     }
-    double* q = (double*)malloc(sizeof(double) * p->D);
-    double* K = (double*)malloc(sizeof(double) * (size_t)L * p->D);
-    double* V = (double*)malloc(sizeof(double) * (size_t)L * p->D);
-    double* z = (double*)malloc(sizeof(double) * (size_t)L);
+    double* K = (double*)malloc(sizeof(double) * (size_t)n * p->D);
+    double* V = (double*)malloc(sizeof(double) * (size_t)n * p->D);
+    double* z = (double*)malloc(sizeof(double) * (size_t)n);
     int rc = ORC_OK;
-    if (!q || !K || !V || !z) {
+    if (!K || !V || !z) {
         rc = ORC_ENOMEM;
         goto done;
     }
-    orc_query_row(p, s, hq, q);
-    rc = orc_gather(p, s, h, 0, L, K, V);
+    rc = orc_gather(p, s, h, 0, n, K, V);
     if (rc != ORC_OK)
         goto done;
-    orc_scores(p, q, K, L, z);
+    orc_scores(p, q, K, n, z);
     /* Step 3: softmax, two passes. */
     double m = -INFINITY;
-    for (int t = 0; t < L; t++)
+    for (int t = 0; t < n; t++)
         if (z[t] > m)
             m = z[t];
     double l = 0.0;
-    for (int t = 0; t < L; t++) {
+    for (int t = 0; t < n; t++) {
         z[t] = exp(z[t] - m);
         l += z[t];
     }
     /* Step 4: weighted sum of V rows, normalised. */
     for (int d = 0; d < p->D; d++) {
         double acc = 0.0;
-        for (int t = 0; t < L; t++)
+        for (int t = 0; t < n; t++)
             acc += z[t] * V[(size_t)t * p->D + d];
         out[d] = acc / l;
     }
 done:
-    free(q);
     free(K);
     free(V);
     free(z);
+    return rc;
+}
+
+/* Decode row (s, hq): the sequence's query against all its L tokens. */
+static int orc_decode_row(const orc_problem* p, int s, int hq, double* out)
+{
+    int G = p->Hq / p->Hkv;
+    double* q = (double*)malloc(sizeof(double) * p->D);
+    if (!q)
+        return ORC_ENOMEM;
+    orc_query_row(p, s, hq, q);
+    int rc = orc_attend_row(p, s, hq / G, q, p->seq_lens[s], out);
+    free(q);
     return rc;
 }
 
@@ -542,6 +552,77 @@ int orc_partition_reduce(double* out, const double* m_in, const double* l_in,
         }
     }
     return ORC_OK;
+}
+
+/* Several new query tokens per sequence, as chunked prefill and speculative
+ * verification use them ([P4] §6.3, §6.5; [P1] §2.3).  The Qn new tokens of
+ * sequence s, Qn = query_start[s+1] - query_start[s], are the last Qn of its
+ * L cached tokens (appended before attention, as in decode), so query token
+ * i sits at position L - Qn + i and attends to tokens 0 .. L - Qn + i
+ * (causal among the new tokens; all earlier tokens visible).  A query token
+ * whose position is negative (Qn > L) gets a zero row.
+ * query and out are [total_q][Hq][D] with total_q = query_start[S]; rows:
+ * optional flat indices qtok * Hq + hq, NULL computes every row. */
+int orc_paged_multi(double* out, const void* query, int q_dt,
+                    const void* k_cache, const void* v_cache, int cache_dt,
+                    const int32_t* block_tables, int max_blocks,
+                    const int32_t* seq_lens, const int32_t* query_start, int S,
+                    int Hq, int Hkv, int D, int bs, int NB, double scale,
+                    double k_scale, double v_scale, const int32_t* rows,
+                    int n_rows, int nthreads)
+{
+    orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
+                     max_blocks, seq_lens, S, Hq, Hkv, D, bs, NB, scale,
+                     k_scale, v_scale};
+    int rc = orc_check(&p);
+    if (rc != ORC_OK || !out || !query_start)
+        return rc != ORC_OK ? rc : ORC_EARG;
+    if (query_start[0] != 0)
+        return ORC_EARG;
+    for (int s = 0; s < S; s++)
+        if (query_start[s + 1] < query_start[s])
+            return ORC_EARG;
+    int total_q = query_start[S];
+    int* owner = (int*)malloc(sizeof(int) * (size_t)(total_q > 0 ? total_q : 1));
+    if (!owner)
+        return ORC_ENOMEM;
+    for (int s = 0; s < S; s++)
+        for (int i = query_start[s]; i < query_start[s + 1]; i++)
+            owner[i] = s;
+    int G = Hq / Hkv;
+    int n = rows ? n_rows : total_q * Hq;
+    int err = ORC_OK;
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int i = 0; i < n; i++) {
+        int r = rows ? rows[i] : i;
+        if (r < 0 || r >= total_q * Hq) {
+            err = ORC_EARG;
+            continue;
+        }
+        int qt = r / Hq, hq = r % Hq;
+        int s = owner[qt];
+        int Qn = query_start[s + 1] - query_start[s];
+        int pos = seq_lens[s] - Qn + (qt - query_start[s]);
+        double* q = (double*)malloc(sizeof(double) * D);
+        if (!q) {
+            err = ORC_ENOMEM;
+            continue;
+        }
+        size_t base = ((size_t)qt * Hq + hq) * D;
+        for (int d = 0; d < D; d++)
+            q[d] = orc_load(query, base + d, q_dt);
+        int e = orc_attend_row(&p, s, hq / G, q, pos + 1, out + (size_t)r * D);
+        free(q);
+        if (e != ORC_OK)
+            err = e;
+    }
+    (void)nthreads;
+    free(owner);
+    return err;
 }
 
 /* Gather only (step 1), exposed so tests can pin address translation:

@@ -326,3 +326,86 @@ def test_partition_ranges_by_brute_force(orc):
                 assert l[s, hq, p] == pytest.approx(w.sum(), abs=1e-12)
                 np.testing.assert_allclose(o[s, hq, p], w @ V[p * P:(p + 1) * P], atol=1e-12)
             assert np.isnan(m[s, hq, -(-L // P):]).all()   # untouched beyond ceil(L/P)
+
+
+# --- several query tokens per sequence (chunked prefill, verification) -----
+# [P4] §6.3 (chunked prefill) and §6.5 (speculative verification): the new
+# tokens of a sequence are its last Qn cached tokens; token i attends to
+# every token up to its own position.
+
+def _multi_case(rng, lens, qlens, Hkv, G, D, bs, dtype):
+    Ks, Vs = rand_logical(rng, lens, Hkv, D, dtype)
+    kc, vc, tables, sl = build_pool(Ks, Vs, bs, dtype=dtype, rng=rng)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = workloads.draw(rng, (int(qs[-1]), Hkv * G, D), dtype)
+    return Ks, Vs, kc, vc, tables, sl, qs, q
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_multi_matches_dense_causal_softmax(orc, seed):
+    """Library brute force: for query token i of sequence s at position
+    p = L - Qn + i, softmax(scale * K[:p+1] q) V[:p+1] in float64."""
+    rng = np.random.default_rng(400 + seed)
+    dtype = ["f32", "bf16", "f16", "bf16"][seed]
+    bs, Hkv, G, D = [16, 8, 32, 16][seed], [1, 2, 4, 2][seed], [4, 2, 1, 8][seed], [64, 128][seed % 2]
+    S = 3
+    lens = rng.integers(5, 70, size=S)
+    qlens = np.minimum(lens, rng.integers(1, 9, size=S))
+    Ks, Vs, kc, vc, tables, sl, qs, q = _multi_case(rng, lens, qlens, Hkv, G, D, bs, dtype)
+    scale = 1.0 / math.sqrt(D)
+    out = orc.paged_multi(q, kc, vc, tables, sl, qs, q_dtype=dtype, cache_dtype=dtype,
+                          scale=scale)
+    assert np.isfinite(out).all()
+    for s in range(S):
+        for i in range(int(qlens[s])):
+            pos = int(lens[s]) - int(qlens[s]) + i
+            for hq in range(Hkv * G):
+                h = hq // G
+                ref = dense_attention_fp64(widen(q[qs[s] + i, hq], dtype, orc),
+                                           widen(Ks[s][:pos + 1, h], dtype, orc),
+                                           widen(Vs[s][:pos + 1, h], dtype, orc), scale)
+                np.testing.assert_allclose(out[qs[s] + i, hq], ref, rtol=0, atol=1e-12)
+
+
+def test_multi_single_token_equals_decode(orc):
+    """Qn = 1 for every sequence is decode: bit-identical rows."""
+    rng = np.random.default_rng(410)
+    lens = rng.integers(1, 120, size=5)
+    Ks, Vs, kc, vc, tables, sl, qs, q = _multi_case(rng, lens, np.ones(5, int), 2, 4, 64, 16,
+                                                     "bf16")
+    a = orc.paged_multi(q, kc, vc, tables, sl, qs, q_dtype="bf16", cache_dtype="bf16",
+                        scale=0.125)
+    b = orc.paged_decode(q, kc, vc, tables, sl, q_dtype="bf16", cache_dtype="bf16",
+                         scale=0.125)
+    assert np.array_equal(a, b)
+
+
+def test_multi_token_equals_decode_of_its_prefix(orc):
+    """Query token i of a sequence equals decode of the same query against
+    the sequence cut after position L - Qn + i: bit-identical."""
+    rng = np.random.default_rng(411)
+    lens = np.array([40, 17, 64])
+    qlens = np.array([6, 17, 3])
+    Ks, Vs, kc, vc, tables, sl, qs, q = _multi_case(rng, lens, qlens, 2, 2, 64, 8, "f16")
+    out = orc.paged_multi(q, kc, vc, tables, sl, qs, q_dtype="f16", cache_dtype="f16",
+                          scale=0.2)
+    for s in range(3):
+        for i in range(int(qlens[s])):
+            cut = sl.copy()
+            cut[s] = lens[s] - qlens[s] + i + 1
+            qd = np.zeros((3, 4, 64), np.float16)
+            qd[s] = q[qs[s] + i]
+            ref = orc.paged_decode(qd, kc, vc, tables, cut, q_dtype="f16", cache_dtype="f16",
+                                   scale=0.2, rows=[s * 4 + hq for hq in range(4)])
+            assert np.array_equal(out[qs[s] + i], ref[s])
+
+
+def test_multi_queries_before_the_sequence_are_zero(orc):
+    """Qn > L: query tokens whose position is negative see nothing."""
+    rng = np.random.default_rng(412)
+    Ks, Vs, kc, vc, tables, sl, qs, q = _multi_case(rng, np.array([3]), np.array([5]), 1, 1,
+                                                     64, 16, "f32")
+    out = orc.paged_multi(q, kc, vc, tables, sl, qs, q_dtype="f32", cache_dtype="f32",
+                          scale=0.125)
+    assert np.all(out[:2] == 0.0)
+    assert np.isfinite(out[2:]).all() and np.any(out[2:] != 0.0)
