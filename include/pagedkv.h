@@ -1,8 +1,10 @@
 /*
  * pagedkv.h - PagedAttention decode on AMD Instinct MI355X (gfx950).
  *
- * C ABI of libpagedkv.so.  Three operations, a workspace query and a status
- * string.  All kernels are hand-written HIP for CDNA4.
+ * C ABI of libpagedkv.so.  Three operations of the decode step (cache write,
+ * decode attention, split-K reduce), multi-query attention over the same
+ * pool, a workspace query and a status string.  All kernels are hand-written
+ * HIP for CDNA4.
  *
  * Sources (by page title and section):
  *   [P4] "vLLM 推理引擎源码级拆解：PagedAttention 显存虚拟化、Continuous
@@ -203,6 +205,50 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
                                float v_scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes,
                                int32_t algo, hipStream_t stream);
+
+/*
+ * pkv_paged_attention_multi - several new query tokens per sequence against
+ * the paged K/V: chunked prefill ([P4] §6.3: a long prompt's prefill cut
+ * into chunks that run between decode steps; [P1] §2.3) and speculative
+ * verification ([P4] §6.5: the large model checks several drafted tokens in
+ * one pass).
+ *
+ * Sequence s brings Qn = query_start[s+1] - query_start[s] query tokens,
+ * rows query_start[s] .. query_start[s+1]-1 of `query`.  They are the last
+ * Qn of its L = seq_lens[s] cached tokens (stored by pkv_reshape_and_cache
+ * before this call, as in decode), so query token i sits at position
+ * L - Qn + i and attends to tokens 0 .. L - Qn + i (causal among the new
+ * tokens, every earlier token visible):
+ *     z_t = scale * k_scale' * sum_d query[r][hq][d] * K[t][d],  t <= L - Qn + i
+ *     out[r][hq][:] = sum_t softmax(z)_t * v_scale' * V[t][:]
+ * with r = query_start[s] + i, h = hq / G, K/V and the scales as in
+ * pkv_paged_attention_decode.  A query token whose position is negative
+ * (Qn > L) gets a zero row.  The pages give no kernel for this step; the
+ * definition above is this library's reading of theirs.
+ *
+ *   out, query    [total_q][num_q_heads][head_dim], dtype q_dtype, where
+ *                 total_q = query_start[num_seqs]
+ *   query_start   [num_seqs + 1] int32, query_start[0] = 0, non-decreasing
+ *   max_query_len host-side bound on every Qn (sizes the grid); rows of
+ *                 tokens past it are not written
+ *   other arguments as for pkv_paged_attention_decode
+ *
+ * Supported: the matrix-core combinations of pkv_paged_attention_decode
+ * (f16/bf16 query; f16/bf16/fp8 cache; head_dim 64 or 128; block_size 8, 16
+ * or 32; G <= 16).  One wavefront serves 16 / G consecutive query tokens of
+ * one sequence and one KV head, so K/V is read once per 16 / G query tokens.
+ * Preconditions for a meaningful result as for decode, and
+ * Qn <= max_query_len.
+ */
+int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
+                              const void* k_cache, const void* v_cache,
+                              pkv_dtype cache_dtype, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              const int32_t* query_start, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              int32_t max_query_len, float scale, float k_scale,
+                              float v_scale, hipStream_t stream);
 
 /*
  * pkv_decode_workspace_bytes - bytes of workspace split-K decode needs

@@ -70,6 +70,9 @@ def _load():
                                                I32, I32, I32, I32, F, F, F, I32, P, SZ,
                                                I32, P]
     lib.pkv_paged_attention_decode.restype = I
+    lib.pkv_paged_attention_multi.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32, I32,
+                                              I32, I32, I32, I32, I32, F, F, F, P]
+    lib.pkv_paged_attention_multi.restype = I
     lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_decode_workspace_bytes.restype = SZ
     lib.pkv_paged_attention_reduce.argtypes = [P, I, P, SZ, P, I32, I32, I32, I32, I32, I32, P]
@@ -151,6 +154,26 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
         float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, ALGO[algo],
         _stream(stream))
     _check("pkv_paged_attention_decode", rc)
+
+
+def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,
+                          v_cache: torch.Tensor, block_tables: torch.Tensor,
+                          seq_lens: torch.Tensor, query_start: torch.Tensor, *, scale: float,
+                          max_seq_len: int, max_query_len: int, k_scale: float = 1.0,
+                          v_scale: float = 1.0, stream=None) -> None:
+    """Several new query tokens per sequence (chunked prefill, speculative
+    verification).  out, query [total_q, Hq, D]; query_start [S + 1] int32;
+    query token i of sequence s (row query_start[s] + i) sits at position
+    seq_lens[s] - Qn + i and attends to the tokens up to it."""
+    TQ, Hq, D = query.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    S = seq_lens.shape[0]
+    rc = _load().pkv_paged_attention_multi(
+        _ptr(out), _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(v_cache),
+        _dtype_code(k_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        _ptr(query_start), S, Hq, Hkv, D, bs, NB, int(max_seq_len), int(max_query_len),
+        float(scale), float(k_scale), float(v_scale), _stream(stream))
+    _check("pkv_paged_attention_multi", rc)
 
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor,

@@ -142,6 +142,69 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
     return launch_status(launch_reshape_and_cache(src_dtype, cache_dtype, p, stream));
 }
 
+int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
+                              const void* k_cache, const void* v_cache,
+                              pkv_dtype cache_dtype, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              const int32_t* query_start, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
+                              int32_t max_query_len, float scale, float k_scale,
+                              float v_scale, hipStream_t stream) {
+    if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+    if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
+        max_query_len <= 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (num_kv_heads > 4096) return PKV_ERR_SHAPE;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PKV_ERR_SHAPE;
+    if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+    const int G = num_q_heads / num_kv_heads;
+    if (!decode_mfma_supported(q_dtype, cache_dtype, head_dim, G)) return PKV_ERR_UNSUPPORTED;
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u) ||
+        ((uintptr_t)query_start & 3u))
+        return PKV_ERR_ALIGN;
+    const int qpg = 16 / G;                        // query tokens per wavefront
+    const int64_t groups = (max_query_len + qpg - 1) / qpg;
+    const int64_t units = (int64_t)num_seqs * groups * num_kv_heads;
+    if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
+
+    DecodeParams p;
+    p.out = out;
+    p.q = query;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.lens = seq_lens;
+    p.ws_m = p.ws_l = p.ws_o = nullptr;
+    p.ws_hdr = p.ws_pre = nullptr;
+    p.nW = 0;
+    p.epoch = 0;
+    p.q_start = query_start;
+    p.max_groups = (int)groups;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    p.G = G;
+    p.bs = block_size;
+    p.NB = num_blocks;
+    p.max_blocks = max_blocks_per_seq;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    p.len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
+    p.P = 0;
+    p.P_max = 1;
+    const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    p.scale_log2 = scale * ks * kLog2e;
+    p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    return launch_status(launch_multi_query(q_dtype, cache_dtype, p, stream));
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition_size) {
@@ -192,6 +255,9 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     p.ws_m = p.ws_l = p.ws_o = nullptr;
     p.ws_hdr = p.ws_pre = nullptr;
     p.nW = 0;
+    p.epoch = 0;
+    p.q_start = nullptr;
+    p.max_groups = 0;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;

@@ -36,6 +36,8 @@ struct DecodeParams {
     int32_t* ws_pre;       // balanced mode: tile prefix of the sequences [S + 1]
     int nW;                // balanced mode: wavefronts of the persistent grid
     uint32_t epoch;        // balanced mode: this call's number (never repeats soon)
+    const int32_t* q_start;  // multi-query: [S + 1] first query token of each sequence
+    int max_groups;        // multi-query: query-token groups per sequence in the grid
     int S, Hq, Hkv, D, G, bs, NB, max_blocks;
     int len_cap;           // min(max_seq_len, max_blocks * bs)
     int P;                 // partition size, 0 = one pass
@@ -159,6 +161,7 @@ hipError_t launch_decode_mfma(int qdt, int cdt, const DecodeParams& p, hipStream
 // kernel that would serve these types and shapes (0 if unknown), and launch.
 int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S);
 hipError_t launch_decode_balanced(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
+hipError_t launch_multi_query(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 hipError_t launch_reduce(int out_dt, const ReduceParams& p, hipStream_t st);
 hipError_t launch_reduce_balanced(int out_dt, const ReduceParams& p, hipStream_t st);
 

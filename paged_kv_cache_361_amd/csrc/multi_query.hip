@@ -1,0 +1,147 @@
+// multi_query.hip - paged attention for several new query tokens per
+// sequence: chunked prefill ("vLLM 推理引擎源码级拆解" §6.3: a long prompt's
+// prefill cut into chunks run between decode steps) and speculative
+// verification (§6.5: the large model checks several drafted tokens in one
+// pass).  The Qn new tokens of sequence s are its last Qn cached tokens
+// (already stored by reshape_and_cache); query token i sits at position
+// L - Qn + i and attends to tokens 0 .. L - Qn + i through the block table,
+// with the same single-pass online softmax as decode.
+//
+// Work layout.  The matrix-core tile of tile_mfma.hpp takes 16 B columns;
+// here a column is a (query token, query head) pair: column c holds head
+// c % G of query token c / G, so a wavefront serves 16 / G consecutive query
+// tokens of one sequence and all G heads of one KV head, and each K/V tile it
+// loads feeds every one of them.  Column c drops the tokens past its own
+// position (the causal limit inside the chunk).  A wavefront reads tokens
+// 0 .. (its last query token's position) with the decode kernel's pipeline:
+// windows of 64 table entries, a ring of DEPTH tiles in flight.  Units are
+// numbered with the query group innermost, so the wavefronts that re-read
+// one sequence's K/V for its different groups run side by side and share it
+// through the caches.
+#include "tile_mfma.hpp"
+
+namespace pkv {
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 4;
+
+template <class Q, class C, int D, bool PAIR, int DEPTH>
+__global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p) {
+    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef typename TM::T T;
+    typedef typename TM::v8 v8;
+    const TM tm;
+    const int lane = tm.lane;
+
+    const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cg = unit % p.max_groups;
+    const int h = (unit / p.max_groups) % p.Hkv;
+    const int s = unit / p.max_groups / p.Hkv;
+    if (s >= p.S) return;
+    const int G = p.G;
+    const int QPG = 16 / G;                            // query tokens per wavefront
+    const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[s]);
+    const int Qn = __builtin_amdgcn_readfirstlane(p.q_start[s + 1]) - q0;
+    const int qbase = cg * QPG;
+    if (qbase >= Qn) return;
+    const int nq = min(QPG, Qn - qbase);
+    const int ncols = nq * G;
+    int L = __builtin_amdgcn_readfirstlane(p.lens[s]);
+    L = L < p.len_cap ? L : p.len_cap;
+    const int pos0 = L - Qn + qbase;                   // position of the group's first token
+    const int t_end = pos0 + nq;                       // tokens [0, t_end) are read
+
+    auto out_row = [&](int c) {
+        return (T*)p.out + ((size_t)(q0 + qbase + c / G) * p.Hq + (size_t)h * G + c % G) * D;
+    };
+    if (t_end <= 0) {                                  // every token of the group precedes the sequence
+        for (int c = 0; c < ncols; c++)
+            for (int i = lane; i < D; i += 64) out_row(c)[i] = (T)0.0f;
+        return;
+    }
+
+    // B operand: column j16 = (token j16 / G, head j16 % G); zero past ncols
+    v8 qb[TM::KS];
+    {
+        const T* qrow = (const T*)p.q +
+                        ((size_t)(q0 + qbase + tm.j16 / G) * p.Hq + (size_t)h * G + tm.j16 % G) * D;
+#pragma unroll
+        for (int kk = 0; kk < TM::KS; kk++) {
+            const int d0 = TM::kFp8 ? (kk >> 1) * 64 + 16 * tm.g4 + (kk & 1) * 8 : 32 * kk + 8 * tm.g4;
+            qb[kk] = tm.j16 < ncols ? *(const v8*)(qrow + d0) : v8{};
+        }
+    }
+    // this lane's column: last token it may see (-1: none)
+    const int pc = tm.j16 < ncols ? pos0 + tm.j16 / G : -1;
+
+    const Head hd = make_head<C, D>(p, h);
+    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
+    const int nblk = (t_end + p.bs - 1) >> hd.bs_shift;
+
+    typename TM::Acc acc;
+    tm.reset(acc);
+    const int wtok = 64 << hd.bs_shift;
+    for (int w0 = 0; w0 < t_end; w0 += wtok) {
+        const int w1 = min(t_end, w0 + wtok);
+        const int wb = w0 >> hd.bs_shift;
+        const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
+        typename TM::Tile tl[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++)
+            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; j++) {
+                const int tj = t0 + 16 * j;
+                if (j == 0 || tj < w1)
+                    tm.template consume<true>(acc, qb, p.scale_log2, t_end - 1 - tj, tl[j], pc - tj);
+                const int tn = tj + 16 * DEPTH;
+                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+            }
+        }
+    }
+
+    tm.finish(
+        acc, ncols, true, p.v_scale, out_row, [](int) { return (float*)nullptr; },
+        [](int) { return (float*)nullptr; }, [](int) { return (float*)nullptr; });
+}
+
+// Tiles in flight per wavefront, as in the one-pass decode kernel.
+template <bool PAIR>
+constexpr int pipeline_depth() {
+    return PAIR ? 2 : 4;
+}
+
+template <class Q, class C, int D>
+hipError_t launch_dd(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
+    if (p.bs == 8)
+        return launch_kernel(multi_query_kernel<Q, C, D, true, pipeline_depth<true>()>, grid,
+                             block, st, p);
+    return launch_kernel(multi_query_kernel<Q, C, D, false, pipeline_depth<false>()>, grid,
+                         block, st, p);
+}
+
+template <class Q, class C>
+hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
+    const long units = (long)p.S * p.max_groups * p.Hkv;
+    const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(64 * kWaves);
+    if (p.D == 64) return launch_dd<Q, C, 64>(p, grid, block, st);
+    if (p.D == 128) return launch_dd<Q, C, 128>(p, grid, block, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_multi_query(int qdt, int cdt, const DecodeParams& p, hipStream_t st) {
+    if (!decode_mfma_supported(qdt, cdt, p.D, p.G)) return hipErrorInvalidValue;
+    if (qdt == kBF16) {
+        if (cdt == kFP8) return launch_d<BF16, FP8>(p, st);
+        return launch_d<BF16, BF16>(p, st);
+    }
+    if (cdt == kFP8) return launch_d<F16, FP8>(p, st);
+    return launch_d<F16, F16>(p, st);
+}
+
+}  // namespace pkv

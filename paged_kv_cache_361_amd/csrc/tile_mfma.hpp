@@ -297,9 +297,13 @@ struct TileMath {
     }
 
     // Consumes one tile: scores, online softmax update, PV accumulate.  lim
-    // as for issue(); rows past it get no weight.
+    // as for issue(); rows past it get no weight.  CAUSAL: the B columns are
+    // query tokens as well as heads, and column lane%16 also drops the rows
+    // past clim (its own limit within the tile); a column can then have
+    // seen no token yet, so weights of dropped rows are forced to zero.
+    template <bool CAUSAL = false>
     __device__ inline void consume(Acc& a, const v8 (&qb)[KS], float scale_log2, int lim,
-                                   const Tile& cur) const {
+                                   const Tile& cur, int clim = 0) const {
         f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < KL; i++) {
@@ -317,10 +321,11 @@ struct TileMath {
             }
         }
         float z[4];
+        const int rlim = CAUSAL ? (clim < lim ? clim : lim) : lim;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const float x = sc[r] * scale_log2;
-            z[r] = (4 * g4 + r <= lim) ? x : -INFINITY;
+            z[r] = (4 * g4 + r <= rlim) ? x : -INFINITY;
         }
 
         // ---- online softmax: tile max over the 16 tokens of each head ----
@@ -341,7 +346,8 @@ struct TileMath {
         }
         float pz[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) pz[r] = exp2f(z[r] - a.m);
+        for (int r = 0; r < 4; r++)
+            pz[r] = (CAUSAL && z[r] == -INFINITY) ? 0.0f : exp2f(z[r] - a.m);
         a.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
 
         // ---- weights as the A operand, value rows as the B operand ----
@@ -396,7 +402,7 @@ struct TileMath {
             const float mh = __shfl(a.m, head, 64);
             if (head >= G) continue;
             if (final_out) {
-                const float inv = v_scale / lh;
+                const float inv = lh > 0.0f ? v_scale / lh : 0.0f;   // no token seen: zeros
                 vrow o;
 #pragma unroll
                 for (int n = 0; n < NT; n++) o[n] = (T)(a.o[n][r] * inv);

@@ -35,8 +35,8 @@ def declared_symbols():
 def test_header_declares_the_three_operations():
     syms = declared_symbols()
     for s in ("pkv_reshape_and_cache", "pkv_paged_attention_decode",
-              "pkv_paged_attention_reduce", "pkv_decode_workspace_bytes",
-              "pkv_status_string"):
+              "pkv_paged_attention_reduce", "pkv_paged_attention_multi",
+              "pkv_decode_workspace_bytes", "pkv_status_string"):
         assert s in syms
 
 
@@ -148,3 +148,26 @@ def test_reduce_rejects_bad_arguments(lib, pkv, kw, status):
     args = [a[k] for k in ("out", "odt", "ws", "ws_bytes", "lens", "S", "Hq", "Hkv", "D",
                            "max_len", "P", "stream")]
     assert lib.pkv_paged_attention_reduce(*args) == status
+
+
+def multi_args(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=2, k=FAKE, v=FAKE, cdt=2, tables=FAKE, max_blocks=16,
+             lens=FAKE, qstart=FAKE, S=4, Hq=32, Hkv=8, D=128, bs=16, NB=100, max_len=256,
+             max_q=8, scale=0.1, ks=1.0, vs=1.0, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "qdt", "k", "v", "cdt", "tables", "max_blocks",
+                           "lens", "qstart", "S", "Hq", "Hkv", "D", "bs", "NB", "max_len",
+                           "max_q", "scale", "ks", "vs", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), -1), (dict(qstart=None), -1), (dict(lens=None), -1),
+    (dict(qdt=7), -3), (dict(qdt=1, cdt=2), -3),
+    (dict(S=0), -2), (dict(max_q=0), -2), (dict(Hq=30), -2), (dict(max_len=0), -2),
+    (dict(scale=float("nan")), -2),
+    (dict(qdt=0, cdt=0), -4), (dict(Hq=64, Hkv=2), -4), (dict(D=96), -4), (dict(bs=12), -4),
+    (dict(out=FAKE + 8), -6), (dict(qstart=FAKE + 2), -6),
+    (dict(S=1 << 20, max_q=1 << 20, Hkv=8, Hq=8), -2),
+])
+def test_multi_rejects_bad_arguments(lib, kw, status):
+    assert lib.pkv_paged_attention_multi(*multi_args(**kw)) == status

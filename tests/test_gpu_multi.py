@@ -1,0 +1,126 @@
+"""Multi-query paged attention on the GPU against the oracle: several new
+query tokens per sequence (chunked prefill, speculative verification;
+"vLLM 推理引擎源码级拆解" §6.3, §6.5), each attending to the tokens up to its
+own position.  Everything goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_361_amd as pkv
+import workloads
+from gpu_case import TOL, DevCase, from_dev, half_ulp, oracle_caches, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_multi(mc: workloads.MultiCase):
+    c = mc.case
+    d = DevCase(c)
+    d.write()
+    q = to_dev(mc.query, c.q_dtype)
+    qs = torch.from_numpy(mc.query_start).cuda()
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    pkv.paged_attention_multi(out, q, d.k_cache, d.v_cache, d.tables, d.lens, qs,
+                              scale=c.scale, max_seq_len=c.max_seq_len,
+                              max_query_len=mc.max_query_len, k_scale=c.k_scale,
+                              v_scale=c.v_scale)
+    torch.cuda.synchronize()
+    return from_dev(out), d
+
+
+def oracle_multi(mc: workloads.MultiCase, rows=None):
+    c = mc.case
+    kc, vc = oracle_caches(c)
+    return oracle.paged_multi(mc.query, kc, vc, c.block_tables, c.seq_lens, mc.query_start,
+                              q_dtype=c.q_dtype, cache_dtype=c.cache_dtype, scale=c.scale,
+                              k_scale=c.k_scale, v_scale=c.v_scale, rows=rows)
+
+
+def check(mc, out, ref, rows=None):
+    c = mc.case
+    if rows is not None:
+        TQ, Hq, D = ref.shape
+        out = out.reshape(TQ * Hq, D)[rows]
+        ref = ref.reshape(TQ * Hq, D)[rows]
+    assert np.isfinite(out).all(), "non-finite GPU output"
+    # short contexts average few values, so |out| can exceed 1: allow the
+    # output's own rounding on top of the tolerance
+    bound = TOL[c.cache_dtype] + half_ulp(ref, c.q_dtype)
+    err = np.abs(out - ref) - bound
+    print("%s: max excess %.3g" % (c.name, float(err.max())), flush=True)
+    assert np.all(err <= 0), float(err.max())
+
+
+def ragged(S, lo, hi, seed, dtype="bf16", cache="bf16", Hq=32, Hkv=8, D=128, bs=16,
+           lmin=1, lmax=600, **kw):
+    return workloads.make_multi_case(
+        "multi-ragged", seed, lambda r: r.integers(lmin, lmax, size=S),
+        lambda r, L: r.integers(lo, hi, size=S, endpoint=True), Hq, Hkv, D, bs,
+        q_dtype=dtype, cache_dtype=cache, max_seq_len=lmax + hi,
+        src_dtype=dtype if cache == "fp8" else None, **kw)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_verify_ragged_draft_lengths(dtype):
+    """Drafts of 0..8 tokens, some longer than the sequence (their leading
+    rows see nothing and are zero)."""
+    mc = ragged(48, 0, 8, 500, dtype=dtype, cache=dtype, lmin=1, lmax=400)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+@pytest.mark.parametrize("G,Hkv", [(1, 8), (8, 2), (16, 1)])
+def test_group_sizes(G, Hkv):
+    """16 / G query tokens per wavefront: G = 1 packs 16 tokens, G = 16 one."""
+    mc = ragged(12, 1, 40, 510 + G, Hq=G * Hkv, Hkv=Hkv, lmin=40, lmax=300)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_fp8_cache_block_sizes(bs):
+    mc = ragged(10, 1, 12, 520 + bs, cache="fp8", bs=bs, lmin=20, lmax=500)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_head_dim_64():
+    mc = ragged(16, 1, 20, 530, D=64, Hq=16, Hkv=4, lmin=1, lmax=700)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_spec_verify_workload_full():
+    mc = workloads.spec_verify()
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_chunked_prefill_workload_sampled_rows():
+    """Chunks of 512 new tokens after 512..3072 cached ones: the oracle on a
+    sample of rows (first, last and random query tokens of every sequence)."""
+    mc = workloads.chunked_prefill()
+    c = mc.case
+    rng = np.random.default_rng(540)
+    toks = set()
+    for s in range(c.S):
+        a, b = int(mc.query_start[s]), int(mc.query_start[s + 1])
+        toks.update([a, b - 1])
+        toks.update(rng.integers(a, b, size=6).tolist())
+    rows = sorted(t * c.Hq + hq for t in toks for hq in (0, 3, 4, 17, 31))
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc, rows), rows)
+
+
+def test_single_token_equals_decode_kernel():
+    """Qn = 1 everywhere is decode: the same rows as the one-pass decode
+    kernel, bit for bit."""
+    c = workloads.make_case("multi-as-decode", 550, lambda r: r.integers(1, 900, size=40),
+                            32, 8, 128, 16, q_dtype="bf16", cache_dtype="bf16",
+                            max_seq_len=900)
+    mc = workloads.MultiCase(c, c.query.copy(), np.arange(c.S + 1, dtype=np.int32), 1)
+    out, d = run_multi(mc)
+    d.decode("mfma", 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(out, from_dev(d.out))

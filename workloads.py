@@ -299,3 +299,53 @@ def shared_prefix_fp8(bs: int = 16, S: int = 128) -> Case:
 WORKLOADS = {"tiny-f32": tiny_f32, "llama2-13b-mha": llama2_13b_mha,
              "llama3-8b-gqa": llama3_8b_gqa, "long-context-gqa": long_context_gqa,
              "shared-prefix-fp8": shared_prefix_fp8}
+
+
+# --- several new query tokens per sequence ---------------------------------
+
+@dataclass
+class MultiCase:
+    """A paged pool and tables (`case`, whose seq_lens count the new tokens)
+    with Qn new query tokens per sequence: query [total_q, Hq, D], the
+    exclusive prefix query_start [S + 1] and the bound max_query_len."""
+    case: Case
+    query: np.ndarray
+    query_start: np.ndarray
+    max_query_len: int
+
+
+def make_multi_case(name: str, seed: int, lens, qlens, Hq: int, Hkv: int, D: int, bs: int, *,
+                    q_dtype: str, cache_dtype: str, **kw) -> MultiCase:
+    """Seeded multi-query case: the pool as make_case builds it (the Qn new
+    tokens of a sequence are its last Qn cached tokens), then the query
+    tokens drawn N(0,1) in the query dtype."""
+    rng = np.random.default_rng(seed)
+    if callable(lens):
+        lens = lens(rng)
+    if callable(qlens):
+        qlens = qlens(rng, np.asarray(lens))
+    c = make_case(name, seed, lens, Hq, Hkv, D, bs, q_dtype=q_dtype, cache_dtype=cache_dtype,
+                  rng=rng, **kw)
+    qlens = np.asarray(qlens, np.int64)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    query = draw(rng, (int(qs[-1]), Hq, D), q_dtype)
+    return MultiCase(c, query, qs, max(1, int(qlens.max()) if qlens.size else 1))
+
+
+def spec_verify(S: int = 256, draft: int = 4) -> MultiCase:
+    """Speculative verification on the Llama-3-8B GQA decode shape: every
+    sequence checks `draft` drafted tokens (its last `draft` cached tokens),
+    lengths as the Llama-3-8B decode workload."""
+    return make_multi_case("spec-verify-llama3-8b", 6, lambda r: np.maximum(
+        llama3_8b_gqa_lens(r, S), draft), np.full(S, draft), 32, 8, 128, 16,
+        q_dtype="bf16", cache_dtype="bf16", max_seq_len=4096)
+
+
+def chunked_prefill(S: int = 8, chunk: int = 512) -> MultiCase:
+    """Chunked prefill on the Llama-3-8B GQA shape: each sequence has 512 to
+    3072 tokens already cached and brings a chunk of `chunk` new prompt
+    tokens (the last `chunk` of its cached tokens)."""
+    return make_multi_case("chunked-prefill-llama3-8b", 7,
+                           lambda r: r.integers(512, 3072, size=S, endpoint=True) + chunk,
+                           np.full(S, chunk), 32, 8, 128, 16, q_dtype="bf16",
+                           cache_dtype="bf16", max_seq_len=3072 + chunk)
