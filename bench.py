@@ -199,12 +199,137 @@ WORKLOAD_NAMES = {
 }
 
 
+MULTI_WORKLOADS = {
+    "spec-verify": ("speculative verification on the Llama-3-8B GQA decode shape, bf16: "
+                    "256 seqs, L~lognormal(median 1024, sigma 1, cap 4096), 4 drafted "
+                    "tokens/seq checked in one pass, 32 q / 8 kv heads, D 128, bs 16"),
+    "chunked-prefill": ("chunked prefill on the Llama-3-8B GQA shape, bf16: 8 seqs with "
+                        "512..3072 cached tokens + a 512-token prompt chunk each, causal "
+                        "within the chunk, 32 q / 8 kv heads, D 128, bs 16"),
+}
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def multi_cost(mc):
+    """Algorithmic bytes (K/V of each (sequence, KV head) once, Q in, O out,
+    table entries, lengths, query offsets) and flops (QK and PV, 2 per
+    multiply-add) of one multi-query call."""
+    c = mc.case
+    L = c.seq_lens.astype(np.int64)
+    Qn = np.diff(mc.query_start.astype(np.int64))
+    kv = int(L.sum()) * c.Hkv * c.D * E[c.cache_dtype] * 2
+    qo = int(Qn.sum()) * c.Hq * c.D * E[c.q_dtype] * 2
+    table = 4 * int((-(-L // c.bs)).sum()) + 4 * c.S + 4 * (c.S + 1)
+    seen = 0
+    for s in range(c.S):              # tokens seen by each query token: its position + 1
+        first = int(L[s] - Qn[s]) + 1
+        seen += int(Qn[s]) * first + int(Qn[s]) * (int(Qn[s]) - 1) // 2
+    flops = 4 * seen * c.Hq * c.D
+    return kv + qo + table, flops
+
+
+def bench_multi(args) -> int:
+    import torch
+    import paged_kv_cache_361_amd as pkv
+    torch.cuda.set_device(0)
+    log("generating workload %s ..." % args.workload)
+    mc = workloads.spec_verify() if args.workload == "spec-verify" else workloads.chunked_prefill()
+    c = mc.case
+
+    def dev(a, d):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    query = dev(mc.query, c.q_dtype)
+    qs = torch.from_numpy(mc.query_start).cuda()
+    tables = torch.from_numpy(c.block_tables).cuda()
+    lens = torch.from_numpy(c.seq_lens).cuda()
+    k0, v0 = dev(c.k_cache, c.cache_dtype), dev(c.v_cache, c.cache_dtype)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(1, args.layers) - 1)]
+    out = torch.empty_like(query)
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        kc, vc = layers[i % len(layers)]
+        pkv.paged_attention_multi(out, query, kc, vc, tables, lens, qs, scale=c.scale,
+                                  max_seq_len=c.max_seq_len, max_query_len=mc.max_query_len)
+
+    W, K = args.warmup, args.steps
+    for i in range(W):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        evs[i][0].record(stream)
+        call(W + i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    call_s = float(np.mean(ms)) / 1e3
+    nbytes, flops = multi_cost(mc)
+    total_q = int(mc.query_start[-1])
+    if args.workload == "spec-verify":
+        metric = "paged multi-query attention: achieved HBM TB/s (% of peak) + query tokens/s/layer"
+        value, unit = nbytes / call_s / 1e12, "TB/s"
+        roof = {"bound": "hbm", "kernel": "paged_attention_multi",
+                "achieved": round(nbytes / call_s / 1e9, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(nbytes / call_s / 1e9 / PEAK_GBPS, 4), "traffic": None}
+    else:
+        metric = "paged multi-query attention: achieved TFLOP/s (% of bf16 MFMA peak) + query tokens/s/layer"
+        value, unit = flops / call_s / 1e12, "TFLOP/s"
+        roof = {"bound": "mfma", "kernel": "paged_attention_multi",
+                "achieved": round(flops / call_s / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+    res = {
+        "metric": metric, "value": round(value, 4), "unit": unit, "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(t_total / K * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": c.q_dtype, "data": "synthetic",
+        "config": {"workload": MULTI_WORKLOADS[args.workload], "seqs": c.S,
+                   "tokens": int(c.seq_lens.sum()), "query_tokens": total_q,
+                   "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.bs,
+                   "kv_pools_rotated": len(layers)},
+        "call_us": round(call_s * 1e6, 2),
+        "query_tokens_per_s_per_layer": round(total_q / call_s, 1),
+        "bytes_per_call": nbytes, "flops_per_call": flops,
+        "roofline": roof,
+    }
+    if args.cpu_baseline == "on":
+        import oracle
+        log("timing the CPU oracle ...")
+        threads = oracle.max_threads()
+        kc, vc = c.k_cache, c.v_cache
+        n = 1
+        while True:               # query tokens of the first sequence(s), about 10-20 s
+            rows = np.arange(n * c.Hq, dtype=np.int32)
+            t = time.perf_counter()
+            oracle.paged_multi(mc.query, kc, vc, c.block_tables, c.seq_lens, mc.query_start,
+                               q_dtype=c.q_dtype, cache_dtype=c.cache_dtype, scale=c.scale,
+                               rows=rows, threads=threads)
+            t = time.perf_counter() - t
+            if t > 5.0 or n >= total_q:
+                break
+            n = min(total_q, max(n + 1, int(n * min(8.0, 10.0 / max(t, 1e-3)))))
+        res["cpu_baseline"] = {
+            "value": round(n / t, 2), "unit": "query tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": "the first %d of %d query tokens, all %d query heads, gather + fp64 "
+                      "softmax attention, OpenMP over rows" % (n, total_q, c.Hq)}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama3-8b-gqa", choices=list(workloads.WORKLOADS))
+    ap.add_argument("--workload", default="llama3-8b-gqa",
+                    choices=list(workloads.WORKLOADS) + list(MULTI_WORKLOADS))
     ap.add_argument("--bs", type=int, default=16, help="block size of shared-prefix-fp8")
     ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=None,
@@ -223,6 +348,9 @@ def main() -> int:
               "in this library (each GPU owns its sequences' blocks); run with --gpus 1.",
               file=sys.stderr)
         return 2
+
+    if args.workload in MULTI_WORKLOADS:
+        return bench_multi(args)
 
     import torch
     import paged_kv_cache_361_amd as pkv
