@@ -55,7 +55,8 @@ typedef enum {
     PKV_ERR_UNSUPPORTED = -4, /* valid, but no kernel for this combination */
     PKV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
     PKV_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
-    PKV_ERR_HIP = -7          /* the HIP runtime reported a launch error */
+    PKV_ERR_HIP = -7,         /* the HIP runtime reported a launch error */
+    PKV_ERR_NO_BLOCKS = -8    /* block manager: the pool has no block to give */
 } pkv_status;
 
 typedef enum {
@@ -285,6 +286,94 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype,
                                int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t max_seq_len,
                                int32_t partition_size, hipStream_t stream);
+
+/*
+ * pkv_copy_blocks - copy whole blocks of both pools: for i < num_pairs,
+ * block block_pairs[2i] of k_cache and of v_cache is copied over block
+ * block_pairs[2i+1].  This is the data movement of copy on write ([P4] §2.1:
+ * a sequence about to write into a block that other block tables still
+ * reference gets its own copy); pkv_bm_append reports the pairs.  Pairs with
+ * a block id outside [0, num_blocks), or equal ids, are skipped.
+ *   k_cache, v_cache  pools [num_blocks][block_size][num_kv_heads][head_dim],
+ *                     cache_dtype (any pkv_dtype)
+ *   block_pairs       [num_pairs][2] int32, device memory
+ * Precondition: no block is both a destination and a source, or a
+ * destination twice, in one call.  num_pairs == 0 is a no-op.
+ */
+int pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                    const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    hipStream_t stream);
+
+/*
+ * Block manager - host-side books of one pool ([P4] §3.3: it records who
+ * holds which physical block, the reference counts and the free blocks, and
+ * never touches the data).  It hands out the block tables and slot numbers
+ * the calls above consume.  Host memory only; no call touches the GPU; one
+ * manager is not safe to use from several threads at once.
+ *
+ *  - Blocks are taken on demand ([P4] §2.1-2.2): a sequence's next token
+ *    goes into the free slot of its last block, or into a fresh block.
+ *  - Sharing: pkv_bm_fork gives a new sequence the same table (reference
+ *    counts + 1).  Writing into a block that another table still references
+ *    first moves the writer onto a fresh copy (copy on write); the caller
+ *    performs the copy with pkv_copy_blocks before writing the token.
+ *  - Prefix caching ([P4] §4.2), when enabled: each full block is registered
+ *    under a hash of its token ids and of the block before it; a new
+ *    sequence whose leading full blocks match registered ones points its
+ *    table at them (their K/V is reused, and the caller writes only the
+ *    tokens after them).  A registered block nobody references stays
+ *    registered until its block is needed.
+ *  - Order (the pages leave it open; fixed so that tables are
+ *    reproducible): the lowest-numbered free block is taken first; when no
+ *    block is free, the registered unreferenced block released longest ago
+ *    is taken (and unregistered).  A sequence's blocks are released last
+ *    block first.  A partial last block is never registered.
+ *  - A call that needs more blocks than the pool can give returns
+ *    PKV_ERR_NO_BLOCKS and changes nothing (the caller preempts a sequence:
+ *    frees it and recomputes it later, or swaps it out, [P4] §3.2).
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* New manager for a pool of num_blocks blocks of block_size tokens; NULL on
+ * bad sizes or out of memory. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                                 int32_t enable_prefix_cache);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Registers sequence seq_id with num_tokens tokens (its prompt) and takes its
+ * blocks.  slots[t] (host, [num_tokens]) receives the slot of token t; the
+ * first *num_cached tokens (a multiple of block_size) are held by reused
+ * prefix-cache blocks and need no writing.  Errors: the id exists
+ * (PKV_ERR_SHAPE), not enough blocks (PKV_ERR_NO_BLOCKS). */
+int pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* token_ids,
+                        int32_t num_tokens, int64_t* slots, int32_t* num_cached);
+
+/* Appends one token: *slot receives its slot.  If the sequence's last block
+ * was shared, *copy_src / *copy_dst receive the block to copy and its new
+ * copy (pass them to pkv_copy_blocks before writing the token), else -1. */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, int32_t token_id, int64_t* slot,
+                  int32_t* copy_src, int32_t* copy_dst);
+
+/* New sequence child sharing every block of parent (e.g. parallel samples). */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Releases a sequence's blocks. */
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+
+/* Blocks the pool can still give (free plus registered unreferenced). */
+int32_t pkv_bm_num_free_blocks(const pkv_block_manager* bm);
+
+/* Tokens of a sequence (negative status if unknown). */
+int32_t pkv_bm_seq_len(const pkv_block_manager* bm, int64_t seq_id);
+
+/* Copies up to max_entries entries of a sequence's block table into out
+ * (host) and returns its length (negative status if unknown). */
+int32_t pkv_bm_block_table(const pkv_block_manager* bm, int64_t seq_id, int32_t* out,
+                           int32_t max_entries);
+
+/* Reference count of a block (negative status if out of range). */
+int32_t pkv_bm_refcount(const pkv_block_manager* bm, int32_t block);
 
 /* Static, human-readable name of a pkv_status value. */
 const char* pkv_status_string(int status);

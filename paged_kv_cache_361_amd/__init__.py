@@ -73,6 +73,29 @@ def _load():
     lib.pkv_paged_attention_multi.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32, I32,
                                               I32, I32, I32, I32, I32, F, F, F, P]
     lib.pkv_paged_attention_multi.restype = I
+    lib.pkv_copy_blocks.argtypes = [P, P, I, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_copy_blocks.restype = I
+    lib.pkv_bm_create.argtypes = [I32, I32, I32]
+    lib.pkv_bm_create.restype = P
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_destroy.restype = None
+    I64 = ctypes.c_int64
+    lib.pkv_bm_add_sequence.argtypes = [P, I64, P, I32, P, P]
+    lib.pkv_bm_add_sequence.restype = I
+    lib.pkv_bm_append.argtypes = [P, I64, I32, P, P, P]
+    lib.pkv_bm_append.restype = I
+    lib.pkv_bm_fork.argtypes = [P, I64, I64]
+    lib.pkv_bm_fork.restype = I
+    lib.pkv_bm_free.argtypes = [P, I64]
+    lib.pkv_bm_free.restype = I
+    lib.pkv_bm_num_free_blocks.argtypes = [P]
+    lib.pkv_bm_num_free_blocks.restype = I32
+    lib.pkv_bm_seq_len.argtypes = [P, I64]
+    lib.pkv_bm_seq_len.restype = I32
+    lib.pkv_bm_block_table.argtypes = [P, I64, P, I32]
+    lib.pkv_bm_block_table.restype = I32
+    lib.pkv_bm_refcount.argtypes = [P, I32]
+    lib.pkv_bm_refcount.restype = I32
     lib.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_decode_workspace_bytes.restype = SZ
     lib.pkv_paged_attention_reduce.argtypes = [P, I, P, SZ, P, I32, I32, I32, I32, I32, I32, P]
@@ -197,3 +220,81 @@ def allocate_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor,
+                stream=None) -> None:
+    """Copies block block_pairs[i, 0] over block block_pairs[i, 1] in both
+    pools (copy on write).  block_pairs: int32 [n, 2] on the device."""
+    NB, bs, Hkv, D = k_cache.shape
+    n = block_pairs.shape[0]
+    rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+                                 _ptr(block_pairs) if n else None, n, NB, bs, Hkv, D,
+                                 _stream(stream))
+    _check("pkv_copy_blocks", rc)
+
+
+class BlockManager:
+    """Host books of one pool (C++ in libpagedkv): block tables, reference
+    counts, copy on write and block-level prefix caching.  See
+    include/pagedkv.h for the policies."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_cache: bool = True):
+        self._lib = _load()
+        self.block_size = block_size
+        self._h = self._lib.pkv_bm_create(num_blocks, block_size, 1 if prefix_cache else 0)
+        if not self._h:
+            raise PagedKVError("pkv_bm_create", -2)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pkv_bm_destroy(h)
+
+    def add_sequence(self, seq_id: int, token_ids):
+        """Returns (slots int64 [n], number of leading tokens already cached)."""
+        import numpy as np
+        t = np.ascontiguousarray(token_ids, dtype=np.int32)
+        slots = np.zeros(t.size, np.int64)
+        cached = ctypes.c_int32(0)
+        rc = self._lib.pkv_bm_add_sequence(self._h, seq_id, t.ctypes.data if t.size else None,
+                                           t.size, slots.ctypes.data if t.size else None,
+                                           ctypes.byref(cached))
+        _check("pkv_bm_add_sequence", rc)
+        return slots, cached.value
+
+    def append(self, seq_id: int, token_id: int):
+        """Returns (slot, (copy_src, copy_dst) or None)."""
+        slot = ctypes.c_int64(0)
+        src, dst = ctypes.c_int32(0), ctypes.c_int32(0)
+        rc = self._lib.pkv_bm_append(self._h, seq_id, token_id, ctypes.byref(slot),
+                                     ctypes.byref(src), ctypes.byref(dst))
+        _check("pkv_bm_append", rc)
+        return slot.value, ((src.value, dst.value) if src.value >= 0 else None)
+
+    def fork(self, parent: int, child: int) -> None:
+        _check("pkv_bm_fork", self._lib.pkv_bm_fork(self._h, parent, child))
+
+    def free(self, seq_id: int) -> None:
+        _check("pkv_bm_free", self._lib.pkv_bm_free(self._h, seq_id))
+
+    def num_free_blocks(self) -> int:
+        return int(self._lib.pkv_bm_num_free_blocks(self._h))
+
+    def seq_len(self, seq_id: int) -> int:
+        n = int(self._lib.pkv_bm_seq_len(self._h, seq_id))
+        if n < 0:
+            raise PagedKVError("pkv_bm_seq_len", n)
+        return n
+
+    def block_table(self, seq_id: int):
+        import numpy as np
+        n = int(self._lib.pkv_bm_block_table(self._h, seq_id, None, 0))
+        if n < 0:
+            raise PagedKVError("pkv_bm_block_table", n)
+        out = np.zeros(max(n, 1), np.int32)
+        self._lib.pkv_bm_block_table(self._h, seq_id, out.ctypes.data, n)
+        return out[:n]
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_bm_refcount(self._h, block))

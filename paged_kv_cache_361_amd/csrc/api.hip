@@ -29,6 +29,8 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 inline bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
 
+inline int elem_bytes(int d) { return d == PKV_F32 ? 4 : (d == PKV_FP8_E4M3 ? 1 : 2); }
+
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace pieces for split-K.  Fixed partitions: P_max entries per row,
@@ -101,6 +103,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case PKV_ERR_HIP: return "HIP launch error";
+    case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
     default: return "unknown status";
     }
 }
@@ -203,6 +206,30 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
     return launch_status(launch_multi_query(q_dtype, cache_dtype, p, stream));
+}
+
+int pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
+                    const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
+                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                    hipStream_t stream) {
+    if (!valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+    if (num_pairs < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
+        head_dim <= 0)
+        return PKV_ERR_SHAPE;
+    const int64_t bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(cache_dtype);
+    if (bytes % 16 != 0 || bytes > ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;
+    if (num_pairs == 0) return PKV_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PKV_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_pairs & 3u))
+        return PKV_ERR_ALIGN;
+    CopyParams p;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.pairs = block_pairs;
+    p.n = num_pairs;
+    p.NB = num_blocks;
+    p.block_bytes = (uint32_t)bytes;
+    return launch_status(launch_copy_blocks(p, stream));
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

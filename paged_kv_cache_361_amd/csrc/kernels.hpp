@@ -153,6 +153,17 @@ inline hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_
 // Launchers; the caller has checked the matching *_supported() first.  They
 // return hipErrorInvalidValue for a combination without a kernel.
 hipError_t launch_reshape_and_cache(int src, int cache, const WriteParams& p, hipStream_t st);
+
+// copy_blocks: whole blocks of both pools, pairs[2i] -> pairs[2i + 1].
+struct CopyParams {
+    void* k;
+    void* v;
+    const int32_t* pairs;
+    int n;                 // pairs
+    int NB;
+    uint32_t block_bytes;  // bytes of one block of one pool (a multiple of 16)
+};
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t st);
 bool decode_valu_supported(int qdt, int cdt, int D, int G);
 hipError_t launch_decode_valu(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 bool decode_mfma_supported(int qdt, int cdt, int D, int G);

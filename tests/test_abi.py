@@ -28,7 +28,8 @@ def lib(pkv):
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pkv_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|void|const char\*|"
+                                 r"pkv_block_manager\*)\s+(pkv_\w+)\s*\(",
                                  text, re.M)))
 
 

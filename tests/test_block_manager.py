@@ -1,0 +1,209 @@
+"""Block manager (host books of the pool) against the plain model in
+oracle/block_model.py, and the model against facts that do not come from
+it: the block counts printed in "vLLM 深度实战" (tests/golden/), and invariants
+of the books ("vLLM 推理引擎源码级拆解" §2.1-2.2, §4.2).  No GPU."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle.block_model import BlockModel, NoBlocks
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_361_amd as pkv
+    if not os.path.exists(pkv.LIB_PATH):
+        from paged_kv_cache_361_amd import build
+        build.build()
+    return pkv
+
+
+# ---- the model against facts ------------------------------------------------
+
+def test_model_block_tables_from_the_pages():
+    """The page's example at 16 tokens per block: a 48-token sequence holds
+    blocks 0..2 and a 200-token sequence, added next, blocks 3..15."""
+    g = json.load(open(os.path.join(GOLDEN, "p2_block_counts.json")))
+    m = BlockModel(64, g["block_size"], prefix_cache=False)
+    for i, case in enumerate(g["cases"]):
+        m.add_sequence(i, range(case["seq_len"]))
+        first = case["first_block"]
+        assert m.tables[i] == list(range(first, first + case["blocks"]))
+
+
+def test_library_block_tables_from_the_pages(pkv):
+    g = json.load(open(os.path.join(GOLDEN, "p2_block_counts.json")))
+    bm = pkv.BlockManager(64, g["block_size"], prefix_cache=False)
+    for i, case in enumerate(g["cases"]):
+        bm.add_sequence(i, np.arange(case["seq_len"]))
+        first = case["first_block"]
+        assert bm.block_table(i).tolist() == list(range(first, first + case["blocks"]))
+
+
+def check_invariants(m: BlockModel):
+    # reference counts are the number of table entries naming a block
+    count = [0] * m.NB
+    for t in m.tables.values():
+        for b in t:
+            count[b] += 1
+    assert count == m.ref
+    # every block is exactly one of: referenced, free, cached-unreferenced
+    referenced = {b for b in range(m.NB) if m.ref[b] > 0}
+    assert not (referenced & m.free) and not (referenced & set(m.lru))
+    assert len(referenced) + len(m.free) + len(m.lru) == m.NB
+    # a table covers its tokens exactly
+    for s, t in m.tables.items():
+        assert len(t) == -(-len(m.tokens[s]) // m.bs)
+    # a block shared by two tables holds the same tokens at the same place,
+    # after the same prefix, in both (sharing never mixes contents)
+    seen = {}
+    for s, t in m.tables.items():
+        toks = m.tokens[s]
+        for j, b in enumerate(t):
+            end = min(len(toks), (j + 1) * m.bs)
+            full = (j + 1) * m.bs <= len(toks)
+            key = tuple(toks[:end]) if full else None
+            if b in seen and full and seen[b] is not None:
+                assert seen[b] == key, (s, j, b)
+            seen.setdefault(b, key)
+
+
+def random_script(seed, n_ops=300):
+    rng = np.random.default_rng(seed)
+    prompts = [rng.integers(0, 50, size=int(rng.integers(0, 70))).tolist() for _ in range(4)]
+    ops, live, nxt = [], [], 0
+    for _ in range(n_ops):
+        r = rng.random()
+        if r < 0.3 or not live:
+            base = prompts[int(rng.integers(0, 4))]
+            cut = int(rng.integers(0, len(base) + 1))
+            toks = base[:cut] + rng.integers(0, 50, size=int(rng.integers(0, 20))).tolist()
+            ops.append(("add", nxt, toks))
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.65:
+            ops.append(("append", live[int(rng.integers(0, len(live)))], int(rng.integers(0, 50))))
+        elif r < 0.8:
+            ops.append(("fork", live[int(rng.integers(0, len(live)))], nxt))
+            live.append(nxt)
+            nxt += 1
+        else:
+            s = live.pop(int(rng.integers(0, len(live))))
+            ops.append(("free", s))
+    return ops
+
+
+def apply_model(m, op):
+    try:
+        if op[0] == "add":
+            return m.add_sequence(op[1], op[2])
+        if op[0] == "append":
+            return m.append(op[1], op[2])
+        if op[0] == "fork":
+            return m.fork(op[1], op[2])
+        return m.free_sequence(op[1])
+    except NoBlocks:
+        return "no blocks"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_model_invariants_hold(seed):
+    m = BlockModel(24 + 8 * seed, [8, 16, 32][seed % 3], prefix_cache=seed % 2 == 0)
+    alive = set()
+    for op in random_script(seed):
+        if op[0] in ("append", "fork", "free") and op[1] not in alive:
+            continue
+        r = apply_model(m, op)
+        if r != "no blocks":
+            if op[0] in ("add", "fork"):
+                alive.add(op[1] if op[0] == "add" else op[2])
+            elif op[0] == "free":
+                alive.discard(op[1])
+        check_invariants(m)
+
+
+def test_model_prefix_reuse_and_copy_on_write():
+    m = BlockModel(32, 4)
+    prompt = list(range(10))
+    m.add_sequence(0, prompt)
+    slots, cached = m.add_sequence(1, prompt + [99])
+    assert cached == 8                       # two full blocks reused; the partial one is not
+    assert m.tables[1][:2] == m.tables[0][:2] and m.tables[1][2] != m.tables[0][2]
+    m.fork(1, 2)                             # 11 tokens: last block shared, 3 of 4 used
+    slot, copy = m.append(2, 5)
+    assert copy == (m.tables[1][2], m.tables[2][2])
+    slot, copy = m.append(1, 6)              # the other owner now writes in place
+    assert copy is None and slot == m.tables[1][2] * 4 + 3
+
+
+# ---- the library against the model ---------------------------------------
+
+def run_both(pkv, nb, bs, prefix, ops):
+    bm = pkv.BlockManager(nb, bs, prefix_cache=prefix)
+    m = BlockModel(nb, bs, prefix_cache=prefix)
+    alive = set()
+    for op in ops:
+        if op[0] in ("append", "fork", "free") and op[1] not in alive:
+            continue
+        expect = apply_model(m, op)
+        try:
+            if op[0] == "add":
+                got = bm.add_sequence(op[1], op[2])
+                got = (got[0].tolist(), got[1])
+            elif op[0] == "append":
+                got = bm.append(op[1], op[2])
+            elif op[0] == "fork":
+                got = bm.fork(op[1], op[2])
+            else:
+                got = bm.free(op[1])
+        except pkv.PagedKVError as e:
+            assert e.status == -8, e
+            got = "no blocks"
+        assert got == (expect if not isinstance(expect, tuple) or op[0] != "add"
+                       else (list(expect[0]), expect[1])), op
+        if got != "no blocks":
+            if op[0] in ("add", "fork"):
+                alive.add(op[1] if op[0] == "add" else op[2])
+            elif op[0] == "free":
+                alive.discard(op[1])
+        assert bm.num_free_blocks() == m.available()
+        for s in alive:
+            assert bm.block_table(s).tolist() == m.tables[s]
+            assert bm.seq_len(s) == len(m.tokens[s])
+    for b in range(nb):
+        assert bm.refcount(b) == m.ref[b]
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_library_matches_model(pkv, seed):
+    nb = [16, 40, 200][seed % 3]
+    bs = [8, 16, 32, 4][seed % 4]
+    run_both(pkv, nb, bs, seed % 2 == 0, random_script(100 + seed, 400))
+
+
+def test_library_rejects_unknown_and_duplicate_ids(pkv):
+    bm = pkv.BlockManager(8, 16)
+    bm.add_sequence(1, [1, 2, 3])
+    with pytest.raises(pkv.PagedKVError):
+        bm.add_sequence(1, [4])
+    with pytest.raises(pkv.PagedKVError):
+        bm.append(7, 1)
+    with pytest.raises(pkv.PagedKVError):
+        bm.fork(1, 1)
+    with pytest.raises(pkv.PagedKVError):
+        bm.free(9)
+
+
+def test_library_pool_exhaustion_changes_nothing(pkv):
+    bm = pkv.BlockManager(4, 4, prefix_cache=False)
+    bm.add_sequence(0, list(range(12)))                 # 3 blocks
+    before = bm.num_free_blocks()
+    with pytest.raises(pkv.PagedKVError) as e:
+        bm.add_sequence(1, list(range(9)))              # needs 3, one left
+    assert e.value.status == -8 and bm.num_free_blocks() == before
+    with pytest.raises(pkv.PagedKVError):
+        bm.seq_len(1)
