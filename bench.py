@@ -323,13 +323,70 @@ def bench_multi(args) -> int:
     return 0
 
 
+HOST_LINK_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, nominal
+
+
+def bench_swap(args) -> int:
+    """Swapping ("vLLM 推理引擎源码级拆解" §3.2): 2048 blocks of the Llama-3-8B
+    GQA pool (16 tokens x 8 KV heads x 128, bf16: 32 KiB per block per pool)
+    out to a pinned host pool and back, with pkv_copy_blocks (the GPU reads
+    and writes host memory directly).  Bound by the host link."""
+    import torch
+    import paged_kv_cache_361_amd as pkv
+    torch.cuda.set_device(0)
+    n, bs, Hkv, D = 2048, 16, 8, 128
+    NB = 4 * n
+    k = torch.randn(NB, bs, Hkv, D, device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    hk = torch.empty((n, bs, Hkv, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty_like(hk).pin_memory()
+    rng = np.random.default_rng(8)
+    dev_blocks = rng.permutation(NB)[:n].astype(np.int32)
+    out_pairs = torch.from_numpy(np.stack([dev_blocks, np.arange(n, dtype=np.int32)], 1)).cuda()
+    in_pairs = torch.from_numpy(np.stack([np.arange(n, dtype=np.int32), dev_blocks], 1)).cuda()
+    nbytes = n * bs * Hkv * D * 2 * 2            # K and V blocks moved one way
+    stream = torch.cuda.current_stream()
+    res_ms = {}
+    for name, fn in (("out", lambda: pkv.swap_blocks(hk, hv, k, v, out_pairs)),
+                     ("in", lambda: pkv.swap_blocks(k, v, hk, hv, in_pairs))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        res_ms[name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    gbps = {k_: nbytes / (ms / 1e3) / 1e9 for k_, ms in res_ms.items()}
+    res = {
+        "metric": "block swap GPU <-> pinned host: achieved host-link GB/s per direction",
+        "value": round(min(gbps.values()), 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res_ms["out"] + res_ms["in"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap 2048 random blocks of the Llama-3-8B GQA pool "
+                               "(bs 16, 8 kv heads, D 128, bf16) out to pinned host memory "
+                               "and back", "blocks": n, "bytes_per_direction": nbytes},
+        "swap_out_gbps": round(gbps["out"], 2), "swap_in_gbps": round(gbps["in"], 2),
+        "roofline": {"bound": "host link", "kernel": "copy_blocks",
+                     "achieved": round(min(gbps.values()), 2), "peak": HOST_LINK_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(min(gbps.values()) / HOST_LINK_PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-gqa",
-                    choices=list(workloads.WORKLOADS) + list(MULTI_WORKLOADS))
+                    choices=list(workloads.WORKLOADS) + list(MULTI_WORKLOADS) + ["swap"])
     ap.add_argument("--bs", type=int, default=16, help="block size of shared-prefix-fp8")
     ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=None,
@@ -351,6 +408,8 @@ def main() -> int:
 
     if args.workload in MULTI_WORKLOADS:
         return bench_multi(args)
+    if args.workload == "swap":
+        return bench_swap(args)
 
     import torch
     import paged_kv_cache_361_amd as pkv

@@ -288,22 +288,37 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype,
                                int32_t partition_size, hipStream_t stream);
 
 /*
- * pkv_copy_blocks - copy whole blocks of both pools: for i < num_pairs,
- * block block_pairs[2i] of k_cache and of v_cache is copied over block
- * block_pairs[2i+1].  This is the data movement of copy on write ([P4] §2.1:
- * a sequence about to write into a block that other block tables still
- * reference gets its own copy); pkv_bm_append reports the pairs.  Pairs with
- * a block id outside [0, num_blocks), or equal ids, are skipped.
- *   k_cache, v_cache  pools [num_blocks][block_size][num_kv_heads][head_dim],
- *                     cache_dtype (any pkv_dtype)
- *   block_pairs       [num_pairs][2] int32, device memory
- * Precondition: no block is both a destination and a source, or a
- * destination twice, in one call.  num_pairs == 0 is a no-op.
+ * pkv_copy_blocks - copy whole blocks of the K and V pools: for i <
+ * num_pairs, block block_pairs[2i] of (src_k, src_v) is copied over block
+ * block_pairs[2i+1] of (dst_k, dst_v).
+ *  - Inside one pool (dst == src) it is the data movement of copy on write
+ *    ([P4] §2.1: a sequence about to write into a block that other block
+ *    tables still reference gets its own copy); pkv_bm_append reports the
+ *    pairs.
+ *  - Between the device pool and a pool in pinned host memory (allocated
+ *    with hipHostMalloc, which the GPU reads and writes directly over the
+ *    host link) it is swapping ([P4] §3.2: a preempted sequence's blocks move
+ *    to host memory and back, bound by the host link's bandwidth).
+ * Pairs with a block id outside its pool (src_blocks / dst_blocks blocks), or
+ * copying a block onto itself, are skipped.
+ *   pools         [*_blocks][block_size][num_kv_heads][head_dim], cache_dtype
+ *                 (any pkv_dtype); K and V are both same-pool or both not
+ *   block_pairs   [num_pairs][2] int32, device or pinned host memory
+ * Precondition: within one pool, no block is both a destination and a
+ * source, or a destination twice, in one call.  num_pairs == 0 is a no-op.
  */
-int pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
-                    const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
-                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                    hipStream_t stream);
+int pkv_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                    pkv_dtype cache_dtype, const int32_t* block_pairs, int32_t num_pairs,
+                    int32_t src_blocks, int32_t dst_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, hipStream_t stream);
+
+/*
+ * pkv_host_device_pointer - the address under which the GPU reaches pinned
+ * host memory (allocated with hipHostMalloc, e.g. a host pool for swapping),
+ * for use as a pkv_copy_blocks pool.  PKV_ERR_HIP if host_ptr is not pinned,
+ * mapped host memory (then *device_ptr is NULL).  Host-only.
+ */
+int pkv_host_device_pointer(const void* host_ptr, void** device_ptr);
 
 /*
  * Block manager - host-side books of one pool ([P4] §3.3: it records who

@@ -73,8 +73,10 @@ def _load():
     lib.pkv_paged_attention_multi.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32, I32,
                                               I32, I32, I32, I32, I32, F, F, F, P]
     lib.pkv_paged_attention_multi.restype = I
-    lib.pkv_copy_blocks.argtypes = [P, P, I, P, I32, I32, I32, I32, I32, P]
+    lib.pkv_copy_blocks.argtypes = [P, P, P, P, I, P, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks.restype = I
+    lib.pkv_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pkv_host_device_pointer.restype = I
     lib.pkv_bm_create.argtypes = [I32, I32, I32]
     lib.pkv_bm_create.restype = P
     lib.pkv_bm_destroy.argtypes = [P]
@@ -223,14 +225,48 @@ def allocate_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_
 
 
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_pairs: torch.Tensor,
+                src_k: Optional[torch.Tensor] = None, src_v: Optional[torch.Tensor] = None,
                 stream=None) -> None:
-    """Copies block block_pairs[i, 0] over block block_pairs[i, 1] in both
-    pools (copy on write).  block_pairs: int32 [n, 2] on the device."""
+    """Copies block block_pairs[i, 0] of the source pools over block
+    block_pairs[i, 1] of (k_cache, v_cache).  Without src_k/src_v the source
+    is the same pool (copy on write); with them, e.g. a pinned host pool and
+    the device pool, it is a swap.  block_pairs: int32 [n, 2], device or
+    pinned host memory."""
+    src_k = k_cache if src_k is None else src_k
+    src_v = v_cache if src_v is None else src_v
     NB, bs, Hkv, D = k_cache.shape
     n = block_pairs.shape[0]
-    rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
-                                 _ptr(block_pairs) if n else None, n, NB, bs, Hkv, D,
-                                 _stream(stream))
+    rc = _load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src_k), _ptr(src_v),
+                                 _dtype_code(k_cache), _ptr(block_pairs) if n else None, n,
+                                 src_k.shape[0], NB, bs, Hkv, D, _stream(stream))
+    _check("pkv_copy_blocks", rc)
+
+
+def swap_blocks(dst_k: torch.Tensor, dst_v: torch.Tensor, src_k: torch.Tensor,
+                src_v: torch.Tensor, block_pairs: torch.Tensor, stream=None) -> None:
+    """Swapping between the device pool and a pool in pinned host memory
+    (either direction): block block_pairs[i, 0] of the source pools over block
+    block_pairs[i, 1] of the destination pools.  Host pools must be pinned
+    (torch pin_memory=True); their device addresses are looked up first and
+    a host pool the GPU cannot reach raises before anything is launched."""
+    lib = _load()
+
+    def addr(t: torch.Tensor):
+        if t.is_cuda:
+            return _ptr(t)
+        if not t.is_pinned():
+            raise ValueError("host pools must be pinned")
+        d = ctypes.c_void_p()
+        _check("pkv_host_device_pointer",
+               lib.pkv_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(d)))
+        return d
+
+    NB_dst, bs, Hkv, D = dst_k.shape
+    n = block_pairs.shape[0]
+    pairs = addr(block_pairs) if n else None
+    rc = lib.pkv_copy_blocks(addr(dst_k), addr(dst_v), addr(src_k), addr(src_v),
+                             _dtype_code(dst_k), pairs, n, src_k.shape[0], NB_dst, bs, Hkv, D,
+                             _stream(stream))
     _check("pkv_copy_blocks", rc)
 
 

@@ -208,28 +208,45 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     return launch_status(launch_multi_query(q_dtype, cache_dtype, p, stream));
 }
 
-int pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype,
-                    const int32_t* block_pairs, int32_t num_pairs, int32_t num_blocks,
-                    int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                    hipStream_t stream) {
+int pkv_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
+                    pkv_dtype cache_dtype, const int32_t* block_pairs, int32_t num_pairs,
+                    int32_t src_blocks, int32_t dst_blocks, int32_t block_size,
+                    int32_t num_kv_heads, int32_t head_dim, hipStream_t stream) {
     if (!valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
-    if (num_pairs < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 ||
-        head_dim <= 0)
+    if (num_pairs < 0 || src_blocks <= 0 || dst_blocks <= 0 || block_size <= 0 ||
+        num_kv_heads <= 0 || head_dim <= 0)
         return PKV_ERR_SHAPE;
     const int64_t bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(cache_dtype);
     if (bytes % 16 != 0 || bytes > ((int64_t)1 << 31)) return PKV_ERR_UNSUPPORTED;
     if (num_pairs == 0) return PKV_OK;
-    if (!k_cache || !v_cache || !block_pairs) return PKV_ERR_NULL;
-    if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_pairs & 3u))
+    if (!dst_k || !dst_v || !src_k || !src_v || !block_pairs) return PKV_ERR_NULL;
+    if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v) ||
+        ((uintptr_t)block_pairs & 3u))
         return PKV_ERR_ALIGN;
+    if ((src_k == dst_k) != (src_v == dst_v)) return PKV_ERR_SHAPE;
     CopyParams p;
-    p.k = k_cache;
-    p.v = v_cache;
+    p.dk = dst_k;
+    p.dv = dst_v;
+    p.sk = src_k;
+    p.sv = src_v;
     p.pairs = block_pairs;
     p.n = num_pairs;
-    p.NB = num_blocks;
+    p.src_blocks = src_blocks;
+    p.dst_blocks = dst_blocks;
     p.block_bytes = (uint32_t)bytes;
     return launch_status(launch_copy_blocks(p, stream));
+}
+
+int pkv_host_device_pointer(const void* host_ptr, void** device_ptr) {
+    if (!host_ptr || !device_ptr) return PKV_ERR_NULL;
+    *device_ptr = nullptr;
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(host_ptr), 0) != hipSuccess || !d) {
+        (void)hipGetLastError();           // leave no sticky error behind
+        return PKV_ERR_HIP;
+    }
+    *device_ptr = d;
+    return PKV_OK;
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,

@@ -62,22 +62,26 @@ __global__ __launch_bounds__(kThreads) void quantize_rows_kernel(WriteParams p) 
     }
 }
 
-// Copy on write of shared blocks ("vLLM 推理引擎源码级拆解" §2.1: before a
-// sequence writes into a block other tables still point at, the block is
-// copied and the writer's table takes the copy).  One workgroup per pair,
-// both pools, 16-byte vector loads and stores; a pair with a block id
-// outside the pool, or src == dst, is skipped.
+// Whole-block copies.  Inside one pool this is copy on write of a shared
+// block ("vLLM 推理引擎源码级拆解" §2.1: before a sequence writes into a block
+// other tables still point at, the block is copied and the writer's table
+// takes the copy); between the device pool and a pool in pinned host memory
+// it is swapping (§3.2: a preempted sequence's blocks move to host memory and
+// back).  One workgroup per pair, both pools, 16-byte vector loads and
+// stores; a pair with a block id outside its pool, or a copy of a block onto
+// itself, is skipped.
 constexpr int kCopyThreads = 256;
 
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyParams p) {
     const int i = blockIdx.x;
     const int32_t src = p.pairs[2 * i], dst = p.pairs[2 * i + 1];
-    if (src < 0 || src >= p.NB || dst < 0 || dst >= p.NB || src == dst) return;
+    if (src < 0 || src >= p.src_blocks || dst < 0 || dst >= p.dst_blocks) return;
+    if (p.sk == p.dk && src == dst) return;
     const size_t so = (size_t)src * p.block_bytes, d_o = (size_t)dst * p.block_bytes;
-    const char* ks = (const char*)p.k + so;
-    const char* vs = (const char*)p.v + so;
-    char* kd = (char*)p.k + d_o;
-    char* vd = (char*)p.v + d_o;
+    const char* ks = (const char*)p.sk + so;
+    const char* vs = (const char*)p.sv + so;
+    char* kd = (char*)p.dk + d_o;
+    char* vd = (char*)p.dv + d_o;
     for (uint32_t b = threadIdx.x * 16u; b < p.block_bytes; b += kCopyThreads * 16u) {
         const u32x4 k = *(const u32x4*)(ks + b);
         const u32x4 v = *(const u32x4*)(vs + b);

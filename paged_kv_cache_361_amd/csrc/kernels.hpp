@@ -154,13 +154,16 @@ inline hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_
 // return hipErrorInvalidValue for a combination without a kernel.
 hipError_t launch_reshape_and_cache(int src, int cache, const WriteParams& p, hipStream_t st);
 
-// copy_blocks: whole blocks of both pools, pairs[2i] -> pairs[2i + 1].
+// copy_blocks: whole blocks, src pools' block pairs[2i] -> dst pools' block
+// pairs[2i + 1] (the pools may be the same, or one of them pinned host memory).
 struct CopyParams {
-    void* k;
-    void* v;
+    void* dk;
+    void* dv;
+    const void* sk;
+    const void* sv;
     const int32_t* pairs;
     int n;                 // pairs
-    int NB;
+    int src_blocks, dst_blocks;
     uint32_t block_bytes;  // bytes of one block of one pool (a multiple of 16)
 };
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t st);

@@ -35,9 +35,9 @@ def test_copy_blocks_bit_exact(dtype):
     dv = dv.view(tdt).view(shape) if dtype != "fp8" else dv.view(shape)
     # the fp8 pool is passed as bytes with its dtype code
     if dtype == "fp8":
-        rc = pkv._load().pkv_copy_blocks(pkv._ptr(dk), pkv._ptr(dv), 3,
-                                         pkv._ptr(torch.from_numpy(pairs).cuda()), len(pairs),
-                                         NB, bs, Hkv, D, pkv._stream(None))
+        rc = pkv._load().pkv_copy_blocks(pkv._ptr(dk), pkv._ptr(dv), pkv._ptr(dk), pkv._ptr(dv),
+                                         3, pkv._ptr(torch.from_numpy(pairs).cuda()),
+                                         len(pairs), NB, NB, bs, Hkv, D, pkv._stream(None))
         assert rc == 0
     else:
         pkv.copy_blocks(dk, dv, torch.from_numpy(pairs).cuda())
@@ -160,3 +160,75 @@ def test_block_manager_drives_decode():
         torch.cuda.synchronize()
         o = from_dev(out)
         assert np.all(np.abs(o - ref) <= TOL[dtype] + half_ulp(ref, dtype))
+
+
+def test_swap_round_trip_bit_exact():
+    """Device blocks out to a pinned host pool and back into other device
+    blocks ("vLLM 推理引擎源码级拆解" §3.2 swapping), byte for byte."""
+    rng = np.random.default_rng(620)
+    NB, NBh, bs, Hkv, D = 64, 16, 16, 2, 128
+    k = torch.from_numpy(workloads.draw(rng, (NB, bs, Hkv, D), "bf16").view(np.int16)).cuda()
+    v = torch.from_numpy(workloads.draw(rng, (NB, bs, Hkv, D), "bf16").view(np.int16)).cuda()
+    k, v = k.view(torch.bfloat16), v.view(torch.bfloat16)
+    hk = torch.zeros((NBh, bs, Hkv, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    src = [5, 9, 20, 33, 63]
+    out_pairs = torch.tensor([[b, i] for i, b in enumerate(src)], dtype=torch.int32).cuda()
+    orig_k, orig_v = k[src].cpu().clone(), v[src].cpu().clone()
+    pkv.swap_blocks(hk, hv, k, v, out_pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(hk[:5].view(torch.int16), orig_k.view(torch.int16))
+    assert torch.equal(hv[:5].view(torch.int16), orig_v.view(torch.int16))
+    # the device blocks are reused for other data, then the swapped-out ones return
+    pkv.copy_blocks(k, v, torch.tensor([[1, b] for b in src], dtype=torch.int32).cuda())
+    dst = [40, 41, 42, 43, 0]
+    in_pairs = torch.tensor([[i, b] for i, b in enumerate(dst)], dtype=torch.int32).cuda()
+    pkv.swap_blocks(k, v, hk, hv, in_pairs)
+    torch.cuda.synchronize()
+    assert torch.equal(k[dst].cpu().view(torch.int16), orig_k.view(torch.int16))
+    assert torch.equal(v[dst].cpu().view(torch.int16), orig_v.view(torch.int16))
+
+
+def test_preempt_by_swap_and_resume():
+    """A sequence is swapped out (its blocks copied to the host pool and
+    freed), its device blocks are taken and overwritten by another sequence,
+    and it is swapped back into fresh blocks: its decode is unchanged, bit for
+    bit."""
+    NB, NBh, bs, Hkv, G, D, dtype = 24, 16, 16, 2, 4, 64, "bf16"
+    gpu = pkv.BlockManager(NB, bs, prefix_cache=False)
+    host = pkv.BlockManager(NBh, bs, prefix_cache=False)
+    pool = Mirror(NB, bs, Hkv, D, dtype)
+    hk = torch.zeros((NBh, bs, Hkv, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    rng = np.random.default_rng(630)
+    toks = rng.integers(0, 1000, size=150).tolist()
+    slots, _ = gpu.add_sequence(0, toks)
+    pool.write(token_rows(toks, 0, len(toks), Hkv, D, dtype), slots)
+    q = to_dev(workloads.draw(rng, (1, Hkv * G, D), dtype), dtype)
+
+    def decode(table):
+        out = torch.empty(1, Hkv * G, D, dtype=torch.bfloat16, device="cuda")
+        pkv.paged_attention_decode(out, q, pool.dk, pool.dv,
+                                   torch.from_numpy(table[None].astype(np.int32)).cuda(),
+                                   torch.tensor([len(toks)], dtype=torch.int32).cuda(),
+                                   scale=0.125, max_seq_len=len(toks), algo="mfma")
+        torch.cuda.synchronize()
+        return out.cpu().clone()
+
+    before = decode(gpu.block_table(0))
+    # swap out: host blocks for the sequence, copy, free on the device
+    host.add_sequence(0, toks)
+    pairs = np.stack([gpu.block_table(0), host.block_table(0)], 1).astype(np.int32)
+    pkv.swap_blocks(hk, hv, pool.dk, pool.dv, torch.from_numpy(pairs).cuda())
+    gpu.free(0)
+    # another sequence takes (and overwrites) the freed blocks
+    other = rng.integers(0, 1000, size=200).tolist()
+    slots, _ = gpu.add_sequence(1, other)
+    pool.write(token_rows(other, 0, len(other), Hkv, D, dtype), slots)
+    # swap in: fresh device blocks, copy back, release the host blocks
+    gpu.add_sequence(2, toks)
+    pairs = np.stack([host.block_table(0), gpu.block_table(2)], 1).astype(np.int32)
+    pkv.swap_blocks(pool.dk, pool.dv, hk, hv, torch.from_numpy(pairs).cuda())
+    host.free(0)
+    after = decode(gpu.block_table(2))
+    assert torch.equal(before.view(torch.int16), after.view(torch.int16))
