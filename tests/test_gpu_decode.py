@@ -490,3 +490,40 @@ def test_balanced_agrees_with_fixed_partitions():
     a = gpu_run(c, "mfma", BAL)
     b = gpu_run(c, "mfma", 256)
     assert np.max(np.abs(a - b)) <= 4e-3
+
+
+@pytest.mark.parametrize("P", [BAL, 512])
+def test_split_decode_replays_in_a_graph(P):
+    """The split decode call (decode + reduce) holds no memset and its
+    balanced chunk counter needs no reset between calls, so it can be
+    captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, equals the eager result bit for bit."""
+    c = small_gqa(seed=96, S=48)
+    d = DevCase(c)
+    d.write()
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
+    d.decode("mfma", P, workspace=ws)
+    torch.cuda.synchronize()
+    eager = d.out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.out.fill_(float("nan"))
+        with torch.cuda.graph(g, stream=s):
+            pkv.paged_attention_decode(d.out, d.query, d.k_cache, d.v_cache, d.tables, d.lens,
+                                       scale=c.scale, max_seq_len=c.max_seq_len,
+                                       partition_size=P, workspace=ws, algo="mfma", stream=s)
+            pkv.paged_attention_reduce(d.out, ws, d.lens, num_kv_heads=c.Hkv,
+                                       max_seq_len=c.max_seq_len, partition_size=P, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        d.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.uint8), eager.view(torch.uint8))
+        d.decode("mfma", P, workspace=ws)      # eager calls between replays
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.uint8), eager.view(torch.uint8))
