@@ -210,6 +210,12 @@ MULTI_WORKLOADS = {
 PEAK_BF16_TFLOPS = 2500.0
 
 
+# Split-K partition size of the multi-query workloads: short drafts over long
+# contexts split like decode; 512-token prefill chunks already give one
+# wavefront per 16 / G tokens and need no split.
+MULTI_PARTITION = {"spec-verify": 1024, "chunked-prefill": 0}
+
+
 def multi_cost(mc):
     """Algorithmic bytes (K/V of each (sequence, KV head) once, Q in, O out,
     table entries, lengths, query offsets) and flops (QK and PV, 2 per
@@ -249,11 +255,14 @@ def bench_multi(args) -> int:
     layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(1, args.layers) - 1)]
     out = torch.empty_like(query)
     stream = torch.cuda.current_stream()
+    P = MULTI_PARTITION[args.workload] if args.partition is None else args.partition
+    ws = pkv.allocate_multi_workspace(c.S, mc.max_query_len, c.Hq, c.D, c.max_seq_len, P)
 
     def call(i):
         kc, vc = layers[i % len(layers)]
         pkv.paged_attention_multi(out, query, kc, vc, tables, lens, qs, scale=c.scale,
-                                  max_seq_len=c.max_seq_len, max_query_len=mc.max_query_len)
+                                  max_seq_len=c.max_seq_len, max_query_len=mc.max_query_len,
+                                  partition_size=P, workspace=ws)
 
     W, K = args.warmup, args.steps
     for i in range(W):
@@ -292,7 +301,7 @@ def bench_multi(args) -> int:
         "config": {"workload": MULTI_WORKLOADS[args.workload], "seqs": c.S,
                    "tokens": int(c.seq_lens.sum()), "query_tokens": total_q,
                    "q_heads": c.Hq, "kv_heads": c.Hkv, "head_dim": c.D, "block_size": c.bs,
-                   "kv_pools_rotated": len(layers)},
+                   "kv_pools_rotated": len(layers), "partition_size": P},
         "call_us": round(call_s * 1e6, 2),
         "query_tokens_per_s_per_layer": round(total_q / call_s, 1),
         "bytes_per_call": nbytes, "flops_per_call": flops,

@@ -240,6 +240,27 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
  * one sequence and one KV head, so K/V is read once per 16 / G query tokens.
  * Preconditions for a meaningful result as for decode, and
  * Qn <= max_query_len.
+ *
+ *   partition_size 0: each wavefront walks its query tokens' whole context
+ *                 (no workspace).  P > 0 (a multiple of 16 and of
+ *                 block_size): split-K as in decode - the context is cut
+ *                 into P-token partitions, one wavefront per (partition,
+ *                 group of query tokens, KV head), and a second kernel on
+ *                 the same stream merges the partials of every row (query
+ *                 token, query head) whose token sees more than P tokens;
+ *                 rows that see at most P are written by the first kernel.
+ *                 Partitions wholly after a query token's last visible
+ *                 token are skipped for it.
+ *   workspace     device memory of at least pkv_multi_workspace_bytes(...)
+ *                 bytes for the same num_seqs, max_query_len, num_q_heads,
+ *                 head_dim, max_seq_len and partition_size, 16-byte aligned,
+ *                 owned by the caller; its contents on entry do not matter.
+ *                 Ignored (may be NULL) for partition_size 0.  Calls that
+ *                 share a workspace must be ordered on one stream.
+ *
+ * Errors (nothing launched): as for decode; PKV_ERR_SHAPE also for a
+ * negative partition_size or one that is not a multiple of 16 and of
+ * block_size; PKV_ERR_WORKSPACE for a missing or short workspace.
  */
 int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
                               const void* k_cache, const void* v_cache,
@@ -249,7 +270,20 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
                               int32_t max_query_len, float scale, float k_scale,
-                              float v_scale, hipStream_t stream);
+                              float v_scale, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_multi_workspace_bytes - bytes of workspace pkv_paged_attention_multi
+ * needs for partition_size P > 0: with rows = num_seqs * max_query_len *
+ * num_q_heads and P_max = ceil(max_seq_len / P), m and l [rows][P_max] and
+ * o [rows][P_max][head_dim] float32, then [num_seqs * max_query_len] int32
+ * context lengths, each part starting on a 256-byte boundary.  0 when
+ * partition_size <= 0 or a size is not positive.  Host-only.
+ */
+size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t max_query_len,
+                                 int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t partition_size);
 
 /*
  * pkv_decode_workspace_bytes - bytes of workspace split-K decode needs

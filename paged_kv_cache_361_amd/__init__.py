@@ -71,8 +71,11 @@ def _load():
                                                I32, P]
     lib.pkv_paged_attention_decode.restype = I
     lib.pkv_paged_attention_multi.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32, I32,
-                                              I32, I32, I32, I32, I32, F, F, F, P]
+                                              I32, I32, I32, I32, I32, F, F, F, I32, P, SZ,
+                                              P]
     lib.pkv_paged_attention_multi.restype = I
+    lib.pkv_multi_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    lib.pkv_multi_workspace_bytes.restype = SZ
     lib.pkv_copy_blocks.argtypes = [P, P, P, P, I, P, I32, I32, I32, I32, I32, I32, P]
     lib.pkv_copy_blocks.restype = I
     lib.pkv_host_device_pointer.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
@@ -185,20 +188,42 @@ def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, k_cache: torch
                           v_cache: torch.Tensor, block_tables: torch.Tensor,
                           seq_lens: torch.Tensor, query_start: torch.Tensor, *, scale: float,
                           max_seq_len: int, max_query_len: int, k_scale: float = 1.0,
-                          v_scale: float = 1.0, stream=None) -> None:
+                          v_scale: float = 1.0, partition_size: int = 0,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Several new query tokens per sequence (chunked prefill, speculative
     verification).  out, query [total_q, Hq, D]; query_start [S + 1] int32;
     query token i of sequence s (row query_start[s] + i) sits at position
-    seq_lens[s] - Qn + i and attends to the tokens up to it."""
+    seq_lens[s] - Qn + i and attends to the tokens up to it.  partition_size
+    P > 0 splits each context into P-token partitions (workspace from
+    allocate_multi_workspace); the merge runs inside the call."""
     TQ, Hq, D = query.shape
     NB, bs, Hkv, _ = k_cache.shape
     S = seq_lens.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = _load().pkv_paged_attention_multi(
         _ptr(out), _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(v_cache),
         _dtype_code(k_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
         _ptr(query_start), S, Hq, Hkv, D, bs, NB, int(max_seq_len), int(max_query_len),
-        float(scale), float(k_scale), float(v_scale), _stream(stream))
+        float(scale), float(k_scale), float(v_scale), int(partition_size), _ptr(workspace),
+        ws_bytes, _stream(stream))
     _check("pkv_paged_attention_multi", rc)
+
+
+def multi_workspace_bytes(num_seqs: int, max_query_len: int, num_q_heads: int,
+                          head_dim: int, max_seq_len: int, partition_size: int) -> int:
+    return int(_load().pkv_multi_workspace_bytes(num_seqs, max_query_len, num_q_heads,
+                                                 head_dim, max_seq_len, partition_size))
+
+
+def allocate_multi_workspace(num_seqs: int, max_query_len: int, num_q_heads: int,
+                             head_dim: int, max_seq_len: int, partition_size: int,
+                             device="cuda") -> Optional[torch.Tensor]:
+    """A byte tensor large enough for split multi-query attention (None for P = 0)."""
+    n = multi_workspace_bytes(num_seqs, max_query_len, num_q_heads, head_dim, max_seq_len,
+                              partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def paged_attention_reduce(out: torch.Tensor, workspace: torch.Tensor,

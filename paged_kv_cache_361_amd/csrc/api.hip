@@ -87,6 +87,30 @@ inline bool valid_decode_types(int qdt, int cdt) {
     return qdt == cdt;
 }
 
+// Multi-query split-K workspace: m, l [rows][P_max], o [rows][P_max][D] for
+// rows = num_seqs * max_query_len * num_q_heads (the bound on query rows),
+// then the per-query-token lengths [num_seqs * max_query_len] int32.
+struct MultiWs {
+    int P_max = 1;
+    size_t off_m = 0, off_l = 0, off_o = 0, off_len = 0, bytes = 0;
+};
+
+inline bool multi_ws_layout(int S, int Qmax, int Hq, int D, int max_len, int P, MultiWs* w) {
+    if (S <= 0 || Qmax <= 0 || Hq <= 0 || D <= 0 || max_len <= 0 || P < 0) return false;
+    if (P == 0) return true;
+    w->P_max = (int)(((int64_t)max_len + P - 1) / P);
+    const int64_t rows = (int64_t)S * Qmax * Hq;
+    const int64_t n = rows * w->P_max;
+    if (n * D > ((int64_t)1 << 31) || (int64_t)S * Qmax > ((int64_t)1 << 30)) return false;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    w->off_m = 0;
+    w->off_l = (size_t)up(4 * n);
+    w->off_o = 2 * w->off_l;
+    w->off_len = w->off_o + (size_t)up(4 * n * D);
+    w->bytes = w->off_len + (size_t)up(4 * (int64_t)S * Qmax);
+    return true;
+}
+
 inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
 
 }  // namespace
@@ -153,17 +177,20 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                               int32_t block_size, int32_t num_blocks, int32_t max_seq_len,
                               int32_t max_query_len, float scale, float k_scale,
-                              float v_scale, hipStream_t stream) {
+                              float v_scale, int32_t partition_size, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
     if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
-        max_query_len <= 0)
+        max_query_len <= 0 || partition_size < 0)
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
     if (num_kv_heads > 4096) return PKV_ERR_SHAPE;
     if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PKV_ERR_SHAPE;
     if (!supported_block_size(block_size)) return PKV_ERR_UNSUPPORTED;
+    if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+        return PKV_ERR_SHAPE;
     const int G = num_q_heads / num_kv_heads;
     if (!decode_mfma_supported(q_dtype, cache_dtype, head_dim, G)) return PKV_ERR_UNSUPPORTED;
     if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start)
@@ -174,8 +201,18 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         return PKV_ERR_ALIGN;
     const int qpg = 16 / G;                        // query tokens per wavefront
     const int64_t groups = (max_query_len + qpg - 1) / qpg;
-    const int64_t units = (int64_t)num_seqs * groups * num_kv_heads;
+    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
+    const int len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
+    MultiWs w;
+    if (!multi_ws_layout(num_seqs, max_query_len, num_q_heads, head_dim, len_cap,
+                         partition_size, &w))
+        return PKV_ERR_SHAPE;
+    const int64_t units = (int64_t)num_seqs * w.P_max * groups * num_kv_heads;
     if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
+    if (partition_size > 0) {
+        if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    }
 
     DecodeParams p;
     p.out = out;
@@ -190,6 +227,8 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     p.epoch = 0;
     p.q_start = query_start;
     p.max_groups = (int)groups;
+    p.ws_len = nullptr;
+    p.len_rows = num_seqs * max_query_len;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
@@ -198,14 +237,46 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     p.bs = block_size;
     p.NB = num_blocks;
     p.max_blocks = max_blocks_per_seq;
-    const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
-    p.len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
-    p.P = 0;
-    p.P_max = 1;
+    p.len_cap = len_cap;
+    p.P = partition_size;
+    p.P_max = w.P_max;
     const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
-    return launch_status(launch_multi_query(q_dtype, cache_dtype, p, stream));
+    if (partition_size > 0) {
+        p.ws_m = (float*)((char*)workspace + w.off_m);
+        p.ws_l = (float*)((char*)workspace + w.off_l);
+        p.ws_o = (float*)((char*)workspace + w.off_o);
+        p.ws_len = (int32_t*)((char*)workspace + w.off_len);
+    }
+    hipError_t e = launch_multi_query(q_dtype, cache_dtype, p, stream);
+    if (e != hipSuccess || partition_size == 0) return launch_status(e);
+    // merge the partials of the rows (query token, query head)
+    ReduceParams r;
+    r.out = out;
+    r.ws_m = p.ws_m;
+    r.ws_l = p.ws_l;
+    r.ws_o = p.ws_o;
+    r.ws_hdr = r.ws_pre = nullptr;
+    r.lens = p.ws_len;
+    r.S = p.len_rows;
+    r.Hq = num_q_heads;
+    r.Hkv = num_kv_heads;
+    r.D = head_dim;
+    r.P = partition_size;
+    r.P_max = w.P_max;
+    r.len_cap = len_cap;
+    return launch_status(launch_reduce(q_dtype, r, stream));
+}
+
+size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t partition_size) {
+    if (partition_size <= 0) return 0;
+    MultiWs w;
+    if (!multi_ws_layout(num_seqs, max_query_len, num_q_heads, head_dim, max_seq_len,
+                         partition_size, &w))
+        return 0;
+    return w.bytes;
 }
 
 int pkv_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v,
@@ -302,6 +373,8 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     p.epoch = 0;
     p.q_start = nullptr;
     p.max_groups = 0;
+    p.ws_len = nullptr;
+    p.len_rows = 0;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;

@@ -42,6 +42,7 @@
 // of the chunk after its current one (the counter's atomic add) are all
 // requested one step ahead, and the lengths and tile prefix the walk needs
 // are held in LDS, so moving on never drains the ring.
+#include "split_units.hpp"
 #include "tile_mfma.hpp"
 
 namespace pkv {

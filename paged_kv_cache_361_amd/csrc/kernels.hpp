@@ -38,6 +38,8 @@ struct DecodeParams {
     uint32_t epoch;        // balanced mode: this call's number (never repeats soon)
     const int32_t* q_start;  // multi-query: [S + 1] first query token of each sequence
     int max_groups;        // multi-query: query-token groups per sequence in the grid
+    int32_t* ws_len;       // multi-query split: tokens seen by each query token, for the reduce
+    int len_rows;          // multi-query split: entries of ws_len (num_seqs * max_query_len)
     int S, Hq, Hkv, D, G, bs, NB, max_blocks;
     int len_cap;           // min(max_seq_len, max_blocks * bs)
     int P;                 // partition size, 0 = one pass

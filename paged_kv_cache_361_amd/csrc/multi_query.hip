@@ -18,6 +18,16 @@
 // numbered with the query group innermost, so the wavefronts that re-read
 // one sequence's K/V for its different groups run side by side and share it
 // through the caches.
+//
+// Split-K (partition_size P > 0), for long contexts and short drafts: the
+// units are (sequence, partition, KV head, query group) in the decode
+// kernel's order (full partitions first, split_units.hpp), a unit reads the
+// tokens of its partition, and each column's row is written directly when
+// the column sees at most P tokens (partition 0 holds them all) or left as
+// partials otherwise.  The call then runs the decode reduce over the rows
+// (query token, head), with the number of tokens each query token sees
+// written by this kernel into the workspace.
+#include "split_units.hpp"
 #include "tile_mfma.hpp"
 
 namespace pkv {
@@ -27,7 +37,7 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 
-template <class Q, class C, int D, bool PAIR, int DEPTH>
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool SPLIT>
 __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p) {
     typedef TileMath<Q, C, D, PAIR> TM;
     typedef typename TM::T T;
@@ -38,8 +48,19 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
     const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int cg = unit % p.max_groups;
     const int h = (unit / p.max_groups) % p.Hkv;
-    const int s = unit / p.max_groups / p.Hkv;
-    if (s >= p.S) return;
+    int s = unit / p.max_groups / p.Hkv, part = 0;
+    if constexpr (SPLIT) {
+        if (unit == 0) {
+            // the reduce reads ws_len for num_seqs * max_query_len rows: rows
+            // past the batch's query tokens see nothing
+            for (int i = p.q_start[p.S] + lane; i < p.len_rows; i += 64) p.ws_len[i] = 0;
+        }
+        if (!find_unit(p, s, &s, &part)) return;
+        s = __builtin_amdgcn_readfirstlane(s);
+        part = __builtin_amdgcn_readfirstlane(part);
+    } else if (s >= p.S) {
+        return;
+    }
     const int G = p.G;
     const int QPG = 16 / G;                            // query tokens per wavefront
     const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[s]);
@@ -48,19 +69,30 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
     if (qbase >= Qn) return;
     const int nq = min(QPG, Qn - qbase);
     const int ncols = nq * G;
+    // split rows live in a workspace of num_seqs * max_query_len query
+    // tokens: a batch that breaks Qn <= max_query_len loses its later rows
+    // rather than write past it
+    if (SPLIT && q0 + qbase + nq > p.len_rows) return;
     int L = __builtin_amdgcn_readfirstlane(p.lens[s]);
     L = L < p.len_cap ? L : p.len_cap;
     const int pos0 = L - Qn + qbase;                   // position of the group's first token
-    const int t_end = pos0 + nq;                       // tokens [0, t_end) are read
+    const int t_end = pos0 + nq;                       // tokens [0, t_end) are seen
+    if constexpr (SPLIT) {
+        if (part == 0 && h == 0 && lane < nq) p.ws_len[q0 + qbase + lane] = max(pos0 + lane + 1, 0);
+    }
+    const int t_begin = SPLIT ? part * p.P : 0;
+    const int t_stop = SPLIT ? min(t_end, t_begin + p.P) : t_end;   // this unit's tokens
 
     auto out_row = [&](int c) {
         return (T*)p.out + ((size_t)(q0 + qbase + c / G) * p.Hq + (size_t)h * G + c % G) * D;
     };
     if (t_end <= 0) {                                  // every token of the group precedes the sequence
-        for (int c = 0; c < ncols; c++)
-            for (int i = lane; i < D; i += 64) out_row(c)[i] = (T)0.0f;
+        if (part == 0)
+            for (int c = 0; c < ncols; c++)
+                for (int i = lane; i < D; i += 64) out_row(c)[i] = (T)0.0f;
         return;
     }
+    if (t_begin >= t_stop) return;                     // no token of the group in this partition
 
     // B operand: column j16 = (token j16 / G, head j16 % G); zero past ncols
     v8 qb[TM::KS];
@@ -78,13 +110,13 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
 
     const Head hd = make_head<C, D>(p, h);
     const int32_t* table = p.tables + (size_t)s * p.max_blocks;
-    const int nblk = (t_end + p.bs - 1) >> hd.bs_shift;
+    const int nblk = (t_stop + p.bs - 1) >> hd.bs_shift;
 
     typename TM::Acc acc;
     tm.reset(acc);
     const int wtok = 64 << hd.bs_shift;
-    for (int w0 = 0; w0 < t_end; w0 += wtok) {
-        const int w1 = min(t_end, w0 + wtok);
+    for (int w0 = t_begin; w0 < t_stop; w0 += wtok) {
+        const int w1 = min(t_stop, w0 + wtok);
         const int wb = w0 >> hd.bs_shift;
         const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
         typename TM::Tile tl[DEPTH];
@@ -96,16 +128,23 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
             for (int j = 0; j < DEPTH; j++) {
                 const int tj = t0 + 16 * j;
                 if (j == 0 || tj < w1)
-                    tm.template consume<true>(acc, qb, p.scale_log2, t_end - 1 - tj, tl[j], pc - tj);
+                    tm.template consume<true>(acc, qb, p.scale_log2, t_stop - 1 - tj, tl[j], pc - tj);
                 const int tn = tj + 16 * DEPTH;
                 tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
             }
         }
     }
 
-    tm.finish(
-        acc, ncols, true, p.v_scale, out_row, [](int) { return (float*)nullptr; },
-        [](int) { return (float*)nullptr; }, [](int) { return (float*)nullptr; });
+    // row of column c in the reduce's layout: (query token, query head)
+    auto row_of = [&](int c) {
+        return (size_t)(q0 + qbase + c / G) * p.Hq + (size_t)h * G + c % G;
+    };
+    tm.finish_each(
+        acc, ncols,
+        [&](int c) { return !SPLIT || (part == 0 && pos0 + c / G + 1 <= p.P); }, p.v_scale,
+        out_row, [&](int c) { return p.ws_m + row_of(c) * p.P_max + part; },
+        [&](int c) { return p.ws_l + row_of(c) * p.P_max + part; },
+        [&](int c) { return p.ws_o + (row_of(c) * p.P_max + part) * D; });
 }
 
 // Tiles in flight per wavefront, as in the one-pass decode kernel.
@@ -114,18 +153,24 @@ constexpr int pipeline_depth() {
     return PAIR ? 2 : 4;
 }
 
+template <class Q, class C, int D, bool SPLIT>
+hipError_t launch_ds(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
+    if (p.bs == 8)
+        return launch_kernel(multi_query_kernel<Q, C, D, true, pipeline_depth<true>(), SPLIT>,
+                             grid, block, st, p);
+    return launch_kernel(multi_query_kernel<Q, C, D, false, pipeline_depth<false>(), SPLIT>,
+                         grid, block, st, p);
+}
+
 template <class Q, class C, int D>
 hipError_t launch_dd(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
-    if (p.bs == 8)
-        return launch_kernel(multi_query_kernel<Q, C, D, true, pipeline_depth<true>()>, grid,
-                             block, st, p);
-    return launch_kernel(multi_query_kernel<Q, C, D, false, pipeline_depth<false>()>, grid,
-                         block, st, p);
+    if (p.P > 0) return launch_ds<Q, C, D, true>(p, grid, block, st);
+    return launch_ds<Q, C, D, false>(p, grid, block, st);
 }
 
 template <class Q, class C>
 hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
-    const long units = (long)p.S * p.max_groups * p.Hkv;
+    const long units = (long)p.S * p.P_max * p.max_groups * p.Hkv;
     const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(64 * kWaves);
     if (p.D == 64) return launch_dd<Q, C, 64>(p, grid, block, st);
     if (p.D == 128) return launch_dd<Q, C, 128>(p, grid, block, st);

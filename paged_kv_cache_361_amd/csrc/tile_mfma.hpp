@@ -145,17 +145,6 @@ struct Mfma<F16> {
     }
 };
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ inline int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
-
 // Wave-uniform addressing of one KV head's rows in the pool.
 struct Head {
     const char* kbase;     // k_cache + head offset
@@ -394,6 +383,14 @@ struct TileMath {
     template <class OutRow, class MAt, class LAt, class OAt>
     __device__ inline void finish(const Acc& a, int G, bool final_out, float v_scale,
                                   OutRow out_row, MAt m_at, LAt l_at, OAt o_at) const {
+        finish_each(a, G, [&](int) { return final_out; }, v_scale, out_row, m_at, l_at, o_at);
+    }
+
+    // As finish(), with the choice between the output row and the partials
+    // made per column: final_of(head).
+    template <class Final, class OutRow, class MAt, class LAt, class OAt>
+    __device__ inline void finish_each(const Acc& a, int G, Final final_of, float v_scale,
+                                       OutRow out_row, MAt m_at, LAt l_at, OAt o_at) const {
         const float l_tot = strided_sum<16>(a.l);     // head j16, over all tokens
 #pragma unroll
         for (int r = 0; r < 4; r++) {
@@ -401,7 +398,7 @@ struct TileMath {
             const float lh = __shfl(l_tot, head, 64);
             const float mh = __shfl(a.m, head, 64);
             if (head >= G) continue;
-            if (final_out) {
+            if (final_of(head)) {
                 const float inv = lh > 0.0f ? v_scale / lh : 0.0f;   // no token seen: zeros
                 vrow o;
 #pragma unroll

@@ -154,11 +154,11 @@ def test_reduce_rejects_bad_arguments(lib, pkv, kw, status):
 def multi_args(**kw):
     a = dict(out=FAKE, q=FAKE, qdt=2, k=FAKE, v=FAKE, cdt=2, tables=FAKE, max_blocks=16,
              lens=FAKE, qstart=FAKE, S=4, Hq=32, Hkv=8, D=128, bs=16, NB=100, max_len=256,
-             max_q=8, scale=0.1, ks=1.0, vs=1.0, stream=None)
+             max_q=8, scale=0.1, ks=1.0, vs=1.0, P=0, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return [a[k] for k in ("out", "q", "qdt", "k", "v", "cdt", "tables", "max_blocks",
                            "lens", "qstart", "S", "Hq", "Hkv", "D", "bs", "NB", "max_len",
-                           "max_q", "scale", "ks", "vs", "stream")]
+                           "max_q", "scale", "ks", "vs", "P", "ws", "ws_bytes", "stream")]
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -169,6 +169,20 @@ def multi_args(**kw):
     (dict(qdt=0, cdt=0), -4), (dict(Hq=64, Hkv=2), -4), (dict(D=96), -4), (dict(bs=12), -4),
     (dict(out=FAKE + 8), -6), (dict(qstart=FAKE + 2), -6),
     (dict(S=1 << 20, max_q=1 << 20, Hkv=8, Hq=8), -2),
+    (dict(P=-1), -2), (dict(P=24), -2), (dict(P=16, bs=32), -2),
+    (dict(P=64), -5), (dict(P=64, ws=FAKE, ws_bytes=1024), -5),
+    (dict(P=64, ws=FAKE + 4, ws_bytes=1 << 40), -6),
 ])
 def test_multi_rejects_bad_arguments(lib, kw, status):
     assert lib.pkv_paged_attention_multi(*multi_args(**kw)) == status
+
+
+def test_multi_workspace_bytes_layout(pkv):
+    S, Qm, Hq, D, L, P = 8, 5, 32, 128, 4096, 256
+    rows = S * Qm * Hq
+    n = rows * (-(-L // P))
+    up = lambda x: -(-x // 256) * 256
+    assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, P) == 2 * up(4 * n) + up(4 * n * D) + \
+        up(4 * S * Qm)
+    assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, 0) == 0
+    assert pkv.multi_workspace_bytes(0, Qm, Hq, D, L, P) == 0

@@ -14,17 +14,31 @@ from gpu_case import TOL, DevCase, from_dev, half_ulp, oracle_caches, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def run_multi(mc: workloads.MultiCase):
+def multi_workspace(mc: workloads.MultiCase, P: int, fill: int = 0xFF):
+    """A split workspace whose contents on entry are garbage (0xFF bytes are
+    NaN floats and -1 lengths)."""
     c = mc.case
-    d = DevCase(c)
-    d.write()
+    ws = pkv.allocate_multi_workspace(c.S, mc.max_query_len, c.Hq, c.D, c.max_seq_len, P)
+    if ws is not None:
+        ws.fill_(fill)
+    return ws
+
+
+def run_multi(mc: workloads.MultiCase, P: int = 0, ws=None, d=None):
+    c = mc.case
+    if d is None:
+        d = DevCase(c)
+        d.write()
+    if P and ws is None:
+        ws = multi_workspace(mc, P)
     q = to_dev(mc.query, c.q_dtype)
     qs = torch.from_numpy(mc.query_start).cuda()
     out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    print("multi %s S=%d max_q=%d P=%d" % (c.name, c.S, mc.max_query_len, P), flush=True)
     pkv.paged_attention_multi(out, q, d.k_cache, d.v_cache, d.tables, d.lens, qs,
                               scale=c.scale, max_seq_len=c.max_seq_len,
                               max_query_len=mc.max_query_len, k_scale=c.k_scale,
-                              v_scale=c.v_scale)
+                              v_scale=c.v_scale, partition_size=P, workspace=ws)
     torch.cuda.synchronize()
     return from_dev(out), d
 
@@ -124,3 +138,60 @@ def test_single_token_equals_decode_kernel():
     d.decode("mfma", 0)
     torch.cuda.synchronize()
     assert np.array_equal(out, from_dev(d.out))
+
+
+# ---- split-K ------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [16, 64, 256])
+def test_split_ragged(P):
+    """Contexts cut into P-token partitions, merged by the reduce inside the
+    call; drafts of 0..8 tokens, some longer than the sequence."""
+    mc = ragged(40, 0, 8, 560 + P, lmin=1, lmax=700)
+    out, _ = run_multi(mc, P)
+    check(mc, out, oracle_multi(mc))
+
+
+@pytest.mark.parametrize("G,Hkv,bs,cache", [(1, 8, 32, "fp8"), (16, 1, 8, "bf16"),
+                                            (4, 8, 16, "f16")])
+def test_split_groups_block_sizes(G, Hkv, bs, cache):
+    dtype = "f16" if cache == "f16" else "bf16"
+    mc = ragged(12, 1, 24, 570 + G, dtype=dtype, cache=cache, Hq=G * Hkv, Hkv=Hkv, bs=bs,
+                lmin=1, lmax=500)
+    out, _ = run_multi(mc, 64 if bs != 32 else 96)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_split_head_dim_64_long_chunks():
+    """Query groups that straddle partition boundaries: 40-token chunks over
+    up to 900 tokens with P = 32."""
+    mc = ragged(10, 30, 40, 580, D=64, Hq=16, Hkv=4, lmin=30, lmax=900)
+    out, _ = run_multi(mc, 32)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_split_workspace_reused_by_a_smaller_batch():
+    """Two calls on one workspace, the second with fewer query tokens: rows
+    the first call left in the workspace must not reach the second's output,
+    which is compared with the oracle and with the unsplit kernel."""
+    big = ragged(32, 4, 8, 590, lmin=200, lmax=800)
+    small = ragged(9, 1, 3, 591, lmin=1, lmax=800)
+    P = 64
+    ws = multi_workspace(big, P, fill=0x00)
+    out_big, _ = run_multi(big, P, ws)
+    check(big, out_big, oracle_multi(big))
+    assert pkv.multi_workspace_bytes(small.case.S, small.max_query_len, 32, 128,
+                                     small.case.max_seq_len, P) <= ws.numel()
+    # the small batch's bounds sized to the big workspace's: same max_query_len
+    small = workloads.MultiCase(small.case, small.query, small.query_start, big.max_query_len)
+    out_small, d = run_multi(small, P, ws)
+    check(small, out_small, oracle_multi(small))
+    ref_unsplit, _ = run_multi(small, 0, d=d)
+    c = small.case
+    assert np.all(np.abs(out_small - ref_unsplit) <= 2 * TOL[c.cache_dtype] +
+                  2 * half_ulp(ref_unsplit, c.q_dtype))
+
+
+def test_split_spec_verify_workload_full():
+    mc = workloads.spec_verify()
+    out, _ = run_multi(mc, 512)
+    check(mc, out, oracle_multi(mc))
