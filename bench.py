@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import math
 import os
 import sys
@@ -103,10 +104,33 @@ def decode_bytes(c, P: int, nW: int = 0) -> dict:
             "append": append, "step": dec + red + append}
 
 
-def kernel_source_hash() -> str:
+# Source file each profiled kernel is compiled from.
+KERNEL_SOURCE = {"decode_balanced_kernel": "decode_balanced.hip"}
+
+
+def kernel_sources(top: str) -> list:
+    """`top` and every csrc header it includes (quoted includes, recursively)."""
+    csrc = os.path.join(ROOT, "paged_kv_cache_361_amd", "csrc")
+    seen, todo = [], [top]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        seen.append(name)
+        with open(os.path.join(csrc, name)) as f:
+            for line in f:
+                m = re.match(r'\s*#\s*include\s+"([^"]+)"', line)
+                if m and os.path.exists(os.path.join(csrc, m.group(1))):
+                    todo.append(m.group(1))
+    return sorted(seen)
+
+
+def kernel_source_hash(kernel: str = "decode_balanced_kernel") -> str:
+    """Hash of the sources the kernel is built from: counters taken from an
+    older version of them no longer describe it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_361_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in kernel_sources(KERNEL_SOURCE[kernel]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -125,6 +149,51 @@ def traffic_from_profiles(workload: str, launch_bytes: float):
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_means(path: str, kernel: str):
+    """Mean counter value (KiB) per dispatch of `kernel`, and the largest
+    value read for a device copy (the calibration copy)."""
+    import csv
+    vals, copies = [], []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name, v = row["Kernel_Name"], float(row["Counter_Value"])
+            if kernel + "<" in name:
+                vals.append(v)
+            elif "copyBuffer" in name:
+                copies.append(v)
+    if not vals or not copies:
+        raise SystemExit("%s: no %s or copy dispatches" % (path, kernel))
+    return sum(vals) / len(vals), max(copies), len(vals)
+
+
+def record_traffic(args) -> int:
+    """Writes HBM bytes per launch of the balanced decode kernel from two
+    counter runs.  Each counter is scaled by what it reads for the plain
+    device copy of --copy-calib-mib MiB (that many bytes fetched and
+    written)."""
+    if not args.copy_calib_mib:
+        raise SystemExit("--record-traffic needs the --copy-calib-mib the runs used")
+    kernel = "decode_balanced_kernel"
+    known_kib = args.copy_calib_mib * 1024.0
+    fetch, fcopy, n = _counter_means(args.record_traffic[0], kernel)
+    write, wcopy, _ = _counter_means(args.record_traffic[1], kernel)
+    fs, wsc = known_kib / fcopy, known_kib / wcopy
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[args.workload] = {
+        "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
+        "hbm_bytes_per_launch": int(round((fetch * fs + write * wsc) * 1024)),
+        "fetch_size_kib": round(fetch, 1), "fetch_scale": round(fs, 4),
+        "write_size_kib": round(write, 1), "write_scale": round(wsc, 4),
+        "dispatches": n,
+    }
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    print(json.dumps(data[args.workload]))
+    return 0
 
 
 def cpu_baseline(c, budget_s: float = 20.0) -> dict:
@@ -406,7 +475,13 @@ def main() -> int:
     ap.add_argument("--cpu-baseline", default="on", choices=["on", "off"])
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter scaling)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: turn the counter_collection.csv files of a FETCH_SIZE "
+                         "and a WRITE_SIZE run (each with --copy-calib-mib) into the "
+                         "workload's entry of profiles/decode_traffic.json")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
