@@ -458,13 +458,105 @@ def bench_swap(args) -> int:
     return 0
 
 
+def bench_mixed(args) -> int:
+    """Decode over a pool of 8-token pages whose sequences have 8-, 16- or
+    32-token blocks (picked by length), with the append, split and reduce of
+    a decode step, timed like the main bench."""
+    import torch
+    import paged_kv_cache_361_amd as pkv
+    torch.cuda.set_device(0)
+    log("generating workload %s ..." % args.workload)
+    mc = workloads.mixed_block_sizes()
+    c = mc.case
+    P = 512 if args.partition is None else args.partition
+
+    def dev(a, d):
+        if d == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    query = dev(c.query, c.q_dtype)
+    tables = torch.from_numpy(c.block_tables).cuda()
+    lens = torch.from_numpy(c.seq_lens).cuda()
+    sbs = torch.from_numpy(mc.seq_bs).cuda()
+    new_k, new_v = dev(c.new_key, c.src_dtype), dev(c.new_value, c.src_dtype)
+    slots = torch.from_numpy(c.slot_mapping).cuda()
+    k0, v0 = dev(c.k_cache, c.cache_dtype), dev(c.v_cache, c.cache_dtype)
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(1, args.layers) - 1)]
+    out = torch.empty_like(query)
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P) if P else None
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        kc, vc = layers[i % len(layers)]
+        pkv.reshape_and_cache(new_k, new_v, kc, vc, slots)
+        if ev:
+            ev[0].record(stream)
+        pkv.paged_attention_decode_mixed(out, query, kc, vc, tables, lens, sbs, scale=c.scale,
+                                         max_seq_len=c.max_seq_len, partition_size=P,
+                                         workspace=ws)
+        if ev:
+            ev[1].record(stream)
+        if P:
+            pkv.paged_attention_reduce(out, ws, lens, num_kv_heads=c.Hkv,
+                                       max_seq_len=c.max_seq_len, partition_size=P)
+        if ev:
+            ev[2].record(stream)
+
+    W, K = args.warmup, args.steps
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(W + i, evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    red_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    b = decode_bytes(c, P)
+    L = c.seq_lens.astype(np.int64)
+    # table entries: one per block of each sequence's own size, plus the sizes
+    table_fix = 4 * int((-(-L // mc.seq_bs.astype(np.int64))).sum()) + 4 * c.S \
+        - 4 * int((-(-L // c.bs)).sum())
+    dec_bytes = b["decode_kernel"] + table_fix
+    call_s = float(np.mean(dec_ms + red_ms)) / 1e3
+    dec_s = float(np.mean(dec_ms)) / 1e3
+    counts = {int(k): int((mc.seq_bs == k).sum()) for k in (8, 16, 32)}
+    res = {
+        "metric": "paged decode attention, mixed block sizes: achieved HBM TB/s (% of peak) "
+                  "+ decode tokens/s/layer",
+        "value": round((dec_bytes + b["reduce_kernel"]) / call_s / 1e12, 4), "unit": "TB/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(t_total / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.q_dtype,
+        "data": "synthetic",
+        "config": {"workload": "Llama-3-8B-shaped GQA decode layer, bf16, block size per "
+                               "sequence by length (<128: 8, <2048: 16, else 32 tokens) over "
+                               "8-token pages: 256 seqs, L~lognormal(median 1024, sigma 1, "
+                               "cap 4096), 32 q / 8 kv heads, D 128",
+                   "seqs": c.S, "tokens": int(L.sum()), "sequences_by_block_size": counts,
+                   "partition_size": P, "kv_pools_rotated": len(layers)},
+        "decode_us": round(dec_s * 1e6, 2), "reduce_us": round(float(np.mean(red_ms)) * 1e3, 2),
+        "tokens_per_s_per_layer": round(c.S / call_s, 1),
+        "bytes_per_call": {"decode_kernel": dec_bytes, "reduce_kernel": b["reduce_kernel"]},
+        "roofline": {"bound": "hbm", "kernel": "paged_attention_decode_mixed",
+                     "achieved": round(dec_bytes / dec_s / 1e9, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dec_bytes / dec_s / 1e9 / PEAK_GBPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-gqa",
-                    choices=list(workloads.WORKLOADS) + list(MULTI_WORKLOADS) + ["swap"])
+                    choices=list(workloads.WORKLOADS) + list(MULTI_WORKLOADS) +
+                    ["swap", "mixed-bs"])
     ap.add_argument("--bs", type=int, default=16, help="block size of shared-prefix-fp8")
     ap.add_argument("--algo", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition", type=int, default=None,
@@ -494,6 +586,8 @@ def main() -> int:
         return bench_multi(args)
     if args.workload == "swap":
         return bench_swap(args)
+    if args.workload == "mixed-bs":
+        return bench_mixed(args)
 
     import torch
     import paged_kv_cache_361_amd as pkv

@@ -208,6 +208,47 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
                                int32_t algo, hipStream_t stream);
 
 /*
+ * pkv_paged_attention_decode_mixed - decode over a pool whose sequences use
+ * different block sizes: "vLLM 推理引擎源码级拆解" §1.3 picks 8, 16 or 32
+ * tokens per block per request (short requests small blocks, long ones
+ * large).  The pages do not say how blocks of several sizes share memory;
+ * this library's reading:
+ *
+ *   The pool is kept in pages of page_size tokens, laid out as a pool of
+ *   page_size-token blocks: k_cache, v_cache [num_pages][page_size]
+ *   [num_kv_heads][head_dim].  Sequence s has blocks of bs_s =
+ *   seq_block_sizes[s] tokens (8, 16 or 32, a multiple of page_size); a
+ *   block is bs_s / page_size consecutive pages, and block_tables[s][j] is
+ *   the first page of its block j.  Token t of sequence s is therefore row
+ *       block_tables[s][t / bs_s] * page_size + t % bs_s
+ *   of the pool (the slot pkv_reshape_and_cache takes, with block_size =
+ *   page_size and num_blocks = num_pages).
+ *
+ * What is computed, the other arguments, partition_size (P > 0: a multiple
+ * of 32; the partials then go to the workspace of
+ * pkv_decode_workspace_bytes with the same sizes and P, and
+ * pkv_paged_attention_reduce merges them) and the errors are as for
+ * pkv_paged_attention_decode with block_size = page_size and num_blocks =
+ * num_pages, for the matrix-core type combinations (f16/bf16 query;
+ * f16/bf16/fp8 cache; head_dim 64 or 128; G <= 16; no balanced split).
+ * Also PKV_ERR_NULL for a NULL seq_block_sizes ([num_seqs] int32, device);
+ * PKV_ERR_SHAPE for a pool smaller than 32 tokens or P not a multiple of 32.
+ * Preconditions: each bs_s is 8, 16 or 32 and at least page_size (other
+ * values are read as the nearest of page_size and 32); a block's pages lie
+ * in the pool; seq_lens[s] <= max_blocks_per_seq * bs_s.
+ */
+int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_dtype,
+                                     const void* k_cache, const void* v_cache,
+                                     pkv_dtype cache_dtype, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     const int32_t* seq_block_sizes, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t max_seq_len, float scale, float k_scale,
+                                     float v_scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pkv_paged_attention_multi - several new query tokens per sequence against
  * the paged K/V: chunked prefill ([P4] §6.3: a long prompt's prefill cut
  * into chunks that run between decode steps; [P1] §2.3) and speculative

@@ -49,6 +49,9 @@ def _load():
     lib.orc_paged_decode.argtypes = [P, P, I, P, P, I, P, I, P, I, I, I, I, I, I,
                                      D, D, D, P, I, I]
     lib.orc_paged_decode.restype = I
+    lib.orc_paged_decode_mixed.argtypes = [P, P, I, P, P, I, P, I, P, P, I, I, I, I, I, I,
+                                           D, D, D, P, I, I]
+    lib.orc_paged_decode_mixed.restype = I
     lib.orc_paged_multi.argtypes = [P, P, I, P, P, I, P, I, P, P, I, I, I, I, I, I,
                                     D, D, D, P, I, I]
     lib.orc_paged_multi.restype = I
@@ -155,6 +158,36 @@ def paged_decode(query, k_cache, v_cache, block_tables, seq_lens, *,
         _ptr(seq_lens), S, Hq, Hkv, D, bs, NB, float(scale), float(k_scale),
         float(v_scale), _ptr(r), 0 if r is None else r.size, int(threads))
     _check(rc, "paged_decode")
+    return out
+
+
+def paged_decode_mixed(query, k_cache, v_cache, block_tables, seq_lens, seq_block_sizes, *,
+                       q_dtype: str, cache_dtype: str, scale: float,
+                       k_scale: float = 1.0, v_scale: float = 1.0,
+                       rows: Optional[Sequence[int]] = None,
+                       threads: int = 0) -> np.ndarray:
+    """paged_decode over a pool of pages (k_cache [num_pages, page, Hkv, D])
+    whose sequences have blocks of seq_block_sizes[s] tokens, each that many
+    / page consecutive pages from the page the table names ("vLLM 推理引擎源码级拆解"
+    §1.3 block sizes per request; the page layout is this library's reading)."""
+    query = _c(query, _NP[q_dtype])
+    k_cache = _c(k_cache, _NP[cache_dtype])
+    v_cache = _c(v_cache, _NP[cache_dtype])
+    block_tables = _c(block_tables, np.int32)
+    seq_lens = _c(seq_lens, np.int32)
+    seq_bs = _c(seq_block_sizes, np.int32)
+    S, Hq, D = query.shape
+    NP, page, Hkv, D2 = k_cache.shape
+    assert D2 == D and block_tables.shape[0] == S and seq_lens.shape == (S,)
+    assert seq_bs.shape == (S,)
+    out = np.full((S, Hq, D), np.nan, np.float64)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    rc = _load().orc_paged_decode_mixed(
+        _ptr(out), _ptr(query), _DT[q_dtype], _ptr(k_cache), _ptr(v_cache),
+        _DT[cache_dtype], _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), _ptr(seq_bs), S, Hq, Hkv, D, page, NP, float(scale),
+        float(k_scale), float(v_scale), _ptr(r), 0 if r is None else r.size, int(threads))
+    _check(rc, "paged_decode_mixed")
     return out
 
 

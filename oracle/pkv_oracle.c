@@ -264,6 +264,9 @@ typedef struct {
     const int32_t* seq_lens;
     int S, Hq, Hkv, D, bs, NB;
     double scale, k_scale, v_scale;
+    /* Mixed block sizes: tokens per block of each sequence, or NULL when
+     * every block has bs tokens.  With it, bs and NB count pages. */
+    const int32_t* seq_bs;
 } orc_problem;
 
 /* Stored cache element as a real number: exact widening, or the fp8 code's
@@ -278,17 +281,23 @@ static double orc_cache_value(const orc_problem* p, const void* cache,
 
 /* Step 1: gather tokens [t0, t1) of sequence s, KV head h, into K, V
  * ([t1-t0][D], row-major) through the block table ([P4] §2.2-2.3:
- * logical block t/bs, offset t%bs, physical block from the table). */
+ * logical block t/bs, offset t%bs, physical block from the table).
+ * Mixed block sizes ([P1] §1.3): sequence s has blocks of bs_s tokens, each
+ * bs_s/bs consecutive pages of bs tokens from the page the table names, so
+ * token t is row (entry * bs + t % bs_s) of the pool. */
 static int orc_gather(const orc_problem* p, int s, int h, int t0, int t1,
                       double* K, double* V)
 {
+    int bs_s = p->seq_bs ? p->seq_bs[s] : p->bs;
+    if (bs_s < p->bs || bs_s % p->bs != 0)
+        return ORC_EARG;
     for (int t = t0; t < t1; t++) {
-        int logical = t / p->bs;
-        int offset = t % p->bs;
+        int logical = t / bs_s;
+        int offset = t % bs_s;
         if (logical >= p->max_blocks)
             return ORC_EBLOCK;
         int32_t b = p->block_tables[(size_t)s * p->max_blocks + logical];
-        if (b < 0 || b >= p->NB)
+        if (b < 0 || (int64_t)b + bs_s / p->bs > p->NB)
             return ORC_EBLOCK;
         size_t base = (((size_t)b * p->bs + (size_t)offset) * p->Hkv + (size_t)h) * p->D;
         for (int d = 0; d < p->D; d++) {
@@ -395,17 +404,11 @@ static int orc_decode_row(const orc_problem* p, int s, int hq, double* out)
 /* out[S][Hq][D] (double).  rows: optional list of n_rows flat indices
  * s*Hq + hq to compute (others untouched); NULL computes every row.
  * nthreads <= 0 uses the OpenMP default. */
-int orc_paged_decode(double* out, const void* query, int q_dt,
-                     const void* k_cache, const void* v_cache, int cache_dt,
-                     const int32_t* block_tables, int max_blocks,
-                     const int32_t* seq_lens, int S, int Hq, int Hkv, int D,
-                     int bs, int NB, double scale, double k_scale,
-                     double v_scale, const int32_t* rows, int n_rows,
-                     int nthreads)
+static int orc_decode_rows(const orc_problem* pp, double* out, const int32_t* rows,
+                           int n_rows, int nthreads)
 {
-    orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
-                     max_blocks, seq_lens, S, Hq, Hkv, D, bs, NB, scale,
-                     k_scale, v_scale};
+    const orc_problem p = *pp;
+    const int S = p.S, Hq = p.Hq, D = p.D;
     int rc = orc_check(&p);
     if (rc != ORC_OK || !out)
         return rc != ORC_OK ? rc : ORC_EARG;
@@ -430,6 +433,37 @@ int orc_paged_decode(double* out, const void* query, int q_dt,
     return err;
 }
 
+int orc_paged_decode(double* out, const void* query, int q_dt,
+                     const void* k_cache, const void* v_cache, int cache_dt,
+                     const int32_t* block_tables, int max_blocks,
+                     const int32_t* seq_lens, int S, int Hq, int Hkv, int D,
+                     int bs, int NB, double scale, double k_scale,
+                     double v_scale, const int32_t* rows, int n_rows,
+                     int nthreads)
+{
+    orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
+                     max_blocks, seq_lens, S, Hq, Hkv, D, bs, NB, scale,
+                     k_scale, v_scale, NULL};
+    return orc_decode_rows(&p, out, rows, n_rows, nthreads);
+}
+
+/* Decode over a pool of NP pages of `page` tokens whose sequences have
+ * blocks of seq_bs[s] tokens (multiples of page; see orc_gather). */
+int orc_paged_decode_mixed(double* out, const void* query, int q_dt,
+                           const void* k_cache, const void* v_cache, int cache_dt,
+                           const int32_t* block_tables, int max_blocks,
+                           const int32_t* seq_lens, const int32_t* seq_bs, int S, int Hq,
+                           int Hkv, int D, int page, int NP, double scale, double k_scale,
+                           double v_scale, const int32_t* rows, int n_rows, int nthreads)
+{
+    if (!seq_bs)
+        return ORC_EARG;
+    orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
+                     max_blocks, seq_lens, S, Hq, Hkv, D, page, NP, scale,
+                     k_scale, v_scale, seq_bs};
+    return orc_decode_rows(&p, out, rows, n_rows, nthreads);
+}
+
 /* Split-K partials for partition size P (> 0): for each (s, hq) and each
  * partition k < ceil(L/P) covering tokens [kP, min(L, (k+1)P)):
  *   m[s][hq][k] = max z,  l[s][hq][k] = sum exp(z - m),
@@ -447,7 +481,7 @@ int orc_paged_partials(double* m_out, double* l_out, double* o_out,
 {
     orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
                      max_blocks, seq_lens, S, Hq, Hkv, D, bs, NB, scale,
-                     k_scale, v_scale};
+                     k_scale, v_scale, NULL};
     int rc = orc_check(&p);
     if (rc != ORC_OK)
         return rc;
@@ -573,7 +607,7 @@ int orc_paged_multi(double* out, const void* query, int q_dt,
 {
     orc_problem p = {query, q_dt, k_cache, v_cache, cache_dt, block_tables,
                      max_blocks, seq_lens, S, Hq, Hkv, D, bs, NB, scale,
-                     k_scale, v_scale};
+                     k_scale, v_scale, NULL};
     int rc = orc_check(&p);
     if (rc != ORC_OK || !out || !query_start)
         return rc != ORC_OK ? rc : ORC_EARG;
@@ -635,7 +669,7 @@ int orc_gather_sequence(double* K, double* V, const void* k_cache,
 {
     orc_problem p = {k_cache, ORC_F32, k_cache, v_cache, cache_dt,
                      block_tables, max_blocks, seq_lens, S, Hkv, Hkv, D, bs,
-                     NB, 1.0, k_scale, v_scale};
+                     NB, 1.0, k_scale, v_scale, NULL};
     if (!K || !V || orc_check(&p) != ORC_OK || s < 0 || s >= S || h < 0 || h >= Hkv)
         return ORC_EARG;
     int L = seq_lens[s];

@@ -74,6 +74,10 @@ def _load():
                                               I32, I32, I32, I32, I32, F, F, F, I32, P, SZ,
                                               P]
     lib.pkv_paged_attention_multi.restype = I
+    lib.pkv_paged_attention_decode_mixed.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32,
+                                                     I32, I32, I32, I32, I32, F, F, F, I32, P,
+                                                     SZ, P]
+    lib.pkv_paged_attention_decode_mixed.restype = I
     lib.pkv_multi_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
     lib.pkv_multi_workspace_bytes.restype = SZ
     lib.pkv_copy_blocks.argtypes = [P, P, P, P, I, P, I32, I32, I32, I32, I32, I32, P]
@@ -182,6 +186,31 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
         float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, ALGO[algo],
         _stream(stream))
     _check("pkv_paged_attention_decode", rc)
+
+
+def paged_attention_decode_mixed(out: torch.Tensor, query: torch.Tensor,
+                                 k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                 seq_block_sizes: torch.Tensor, *, scale: float,
+                                 max_seq_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                                 partition_size: int = 0,
+                                 workspace: Optional[torch.Tensor] = None,
+                                 stream=None) -> None:
+    """Decode over a pool of pages (caches [num_pages, page, Hkv, D]) whose
+    sequences have blocks of seq_block_sizes[s] tokens (8, 16 or 32; int32
+    [S]), each that many / page consecutive pages from the page the table
+    names.  partition_size P > 0 (a multiple of 32): call
+    paged_attention_reduce next, as for paged_attention_decode."""
+    S, Hq, D = query.shape
+    NP, page, Hkv, _ = k_cache.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = _load().pkv_paged_attention_decode_mixed(
+        _ptr(out), _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(v_cache),
+        _dtype_code(k_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        _ptr(seq_block_sizes), S, Hq, Hkv, D, page, NP, int(max_seq_len), float(scale),
+        float(k_scale), float(v_scale), int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(stream))
+    _check("pkv_paged_attention_decode_mixed", rc)
 
 
 def paged_attention_multi(out: torch.Tensor, query: torch.Tensor, k_cache: torch.Tensor,

@@ -229,6 +229,8 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     p.max_groups = (int)groups;
     p.ws_len = nullptr;
     p.len_rows = num_seqs * max_query_len;
+    p.seq_bs = nullptr;
+    p.page_shift = 0;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;
@@ -320,6 +322,90 @@ int pkv_host_device_pointer(const void* host_ptr, void** device_ptr) {
     return PKV_OK;
 }
 
+int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_dtype,
+                                     const void* k_cache, const void* v_cache,
+                                     pkv_dtype cache_dtype, const int32_t* block_tables,
+                                     int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                     const int32_t* seq_block_sizes, int32_t num_seqs,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                     int32_t max_seq_len, float scale, float k_scale,
+                                     float v_scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
+    if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        page_size <= 0 || num_pages <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
+        partition_size < 0)
+        return PKV_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
+    if (num_kv_heads > 4096) return PKV_ERR_SHAPE;
+    if (!(scale == scale) || !(k_scale == k_scale) || !(v_scale == v_scale)) return PKV_ERR_SHAPE;
+    if (!supported_block_size(page_size)) return PKV_ERR_UNSUPPORTED;
+    // the pool holds at least one block of the largest size; token counts
+    // of whole tables (max_blocks_per_seq * 32) stay 32-bit on the device
+    if ((int64_t)num_pages * page_size < 32) return PKV_ERR_SHAPE;
+    if (max_blocks_per_seq > (1 << 25)) return PKV_ERR_SHAPE;
+    if (partition_size > 0 && partition_size % 32 != 0) return PKV_ERR_SHAPE;
+    const int G = num_q_heads / num_kv_heads;
+    if (!decode_mfma_supported(q_dtype, cache_dtype, head_dim, G)) return PKV_ERR_UNSUPPORTED;
+    if (!out || !query || !k_cache || !v_cache || !block_tables || !seq_lens ||
+        !seq_block_sizes)
+        return PKV_ERR_NULL;
+    if (!aligned16(out) || !aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u) ||
+        ((uintptr_t)seq_block_sizes & 3u))
+        return PKV_ERR_ALIGN;
+
+    DecodeParams p;
+    p.out = out;
+    p.q = query;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.tables = block_tables;
+    p.lens = seq_lens;
+    p.ws_m = p.ws_l = p.ws_o = nullptr;
+    p.ws_hdr = p.ws_pre = nullptr;
+    p.nW = 0;
+    p.epoch = 0;
+    p.q_start = nullptr;
+    p.max_groups = 0;
+    p.ws_len = nullptr;
+    p.len_rows = 0;
+    p.seq_bs = seq_block_sizes;
+    p.page_shift = page_size == 8 ? 3 : (page_size == 16 ? 4 : 5);
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = num_kv_heads;
+    p.D = head_dim;
+    p.G = G;
+    p.bs = page_size;
+    p.NB = num_pages;
+    p.max_blocks = max_blocks_per_seq;
+    const int64_t cap = (int64_t)max_blocks_per_seq * 32;
+    p.len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
+    p.P = partition_size;
+    p.P_max = 1;
+    const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
+    p.scale_log2 = scale * ks * kLog2e;
+    p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    if (partition_size > 0) {
+        WsLayout w;
+        if (!ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                       partition_size, &w))
+            return PKV_ERR_SHAPE;
+        if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+        p.P_max = w.P_max;
+        p.ws_m = (float*)((char*)workspace + w.off_m);
+        p.ws_l = (float*)((char*)workspace + w.off_l);
+        p.ws_o = (float*)((char*)workspace + w.off_o);
+    }
+    const int64_t units = (int64_t)num_seqs * p.P_max * num_kv_heads;
+    if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
+    return launch_status(launch_decode_mixed(q_dtype, cache_dtype, p, stream));
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition_size) {
@@ -375,6 +461,8 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     p.max_groups = 0;
     p.ws_len = nullptr;
     p.len_rows = 0;
+    p.seq_bs = nullptr;
+    p.page_shift = 0;
     p.S = num_seqs;
     p.Hq = num_q_heads;
     p.Hkv = num_kv_heads;

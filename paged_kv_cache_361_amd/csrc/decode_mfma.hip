@@ -30,6 +30,61 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 
+// Walks tokens [t_begin, t_end) of one unit: DEPTH tiles in flight in a ring
+// of tile buffers unrolled by hand.  Tile j of each round is consumed, then
+// refilled with the tile DEPTH positions ahead, so DEPTH - 1 tiles stay in
+// flight during the arithmetic; loads are issued unconditionally (dead tiles
+// read zeros).  The unit is walked in windows of 64 table entries (one per
+// lane); a split-K partition of at most 64 blocks is a single window.  PR:
+// 8-token blocks (a tile spans two).
+template <bool PR, int DEPTH, class TM>
+__device__ inline void walk_unit(const TM& tm, const Head& hd, const int32_t* table,
+                                 int t_begin, int t_end, const typename TM::v8 (&qb)[TM::KS],
+                                 float scale_log2, typename TM::Acc& acc) {
+    const int lane = tm.lane;
+    const int nblk = (t_end + (1 << hd.bs_shift) - 1) >> hd.bs_shift;   // table entries used
+    const int wtok = 64 << hd.bs_shift;
+    for (int w0 = t_begin; w0 < t_end; w0 += wtok) {
+        const int w1 = min(t_end, w0 + wtok);
+        const int wb = w0 >> hd.bs_shift;
+        const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
+        typename TM::Tile tl[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++)
+            tm.template issue_as<PR>(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; j++) {
+                const int tj = t0 + 16 * j;
+                if (j == 0 || tj < w1) tm.consume(acc, qb, scale_log2, t_end - 1 - tj, tl[j]);
+                const int tn = tj + 16 * DEPTH;
+                tm.template issue_as<PR>(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+            }
+        }
+    }
+}
+
+// Selects the unit = (sequence, partition, KV head) of this wavefront; false
+// when the wavefront has none.  Everything that selects the unit is
+// wave-uniform; readfirstlane tells the compiler so, which keeps block
+// descriptors in scalar registers.
+__device__ inline bool select_unit(const DecodeParams& p, int* s_out, int* part_out, int* h_out) {
+    const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    *h_out = unit % p.Hkv;
+    const int sp = unit / p.Hkv;
+    int s = sp, part = 0;
+    if (p.P > 0) {
+        if (!find_unit(p, sp, &s, &part)) return false;
+        s = __builtin_amdgcn_readfirstlane(s);
+        part = __builtin_amdgcn_readfirstlane(part);
+    } else if (s >= p.S) {
+        return false;
+    }
+    *s_out = s;
+    *part_out = part;
+    return true;
+}
+
 // DEPTH: tiles whose loads are issued ahead of the arithmetic (the ring).
 template <class Q, class C, int D, bool PAIR, int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p) {
@@ -37,20 +92,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
     typedef typename TM::T T;
     const TM tm;
     const int lane = tm.lane;
-
-    // Everything that selects the unit is wave-uniform; readfirstlane tells
-    // the compiler so, which keeps block descriptors in scalar registers.
-    const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = unit % p.Hkv;
-    const int sp = unit / p.Hkv;
-    int s = sp, part = 0;
-    if (p.P > 0) {
-        if (!find_unit(p, sp, &s, &part)) return;
-        s = __builtin_amdgcn_readfirstlane(s);
-        part = __builtin_amdgcn_readfirstlane(part);
-    } else if (s >= p.S) {
-        return;
-    }
+    int s, part, h;
+    if (!select_unit(p, &s, &part, &h)) return;
 
     const int G = p.G;
     int L = p.lens[s];
@@ -71,37 +114,70 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
     typename TM::v8 qb[TM::KS];
     tm.load_q((const T*)p.q + ((size_t)s * p.Hq + (size_t)h * G) * D, G, qb);
     const Head hd = make_head<C, D>(p, h);
-    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
-    const int nblk = (t_end + p.bs - 1) >> hd.bs_shift;       // table entries used
-
     typename TM::Acc acc;
     tm.reset(acc);
+    walk_unit<PAIR, DEPTH>(tm, hd, p.tables + (size_t)s * p.max_blocks, t_begin, t_end, qb,
+                           p.scale_log2, acc);
 
-    // ---- DEPTH tiles in flight: a ring of tile buffers unrolled by hand ----
-    // Tile j of each round is consumed, then refilled with the tile DEPTH
-    // positions ahead, so DEPTH - 1 tiles stay in flight during the
-    // arithmetic; loads are issued unconditionally (dead tiles read zeros).
-    // The unit is walked in windows of 64 table entries (one per lane); a
-    // split-K partition of at most 64 blocks is a single window.
-    const int wtok = 64 << hd.bs_shift;
-    for (int w0 = t_begin; w0 < t_end; w0 += wtok) {
-        const int w1 = min(t_end, w0 + wtok);
-        const int wb = w0 >> hd.bs_shift;
-        const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
-        typename TM::Tile tl[DEPTH];
-#pragma unroll
-        for (int j = 0; j < DEPTH; j++)
-            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
-        for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
-#pragma unroll
-            for (int j = 0; j < DEPTH; j++) {
-                const int tj = t0 + 16 * j;
-                if (j == 0 || tj < w1) tm.consume(acc, qb, p.scale_log2, t_end - 1 - tj, tl[j]);
-                const int tn = tj + 16 * DEPTH;
-                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
-            }
-        }
+    const size_t row0 = (size_t)s * p.Hq + (size_t)h * G;
+    tm.finish(
+        acc, G, final_out, p.v_scale,
+        [&](int head) { return out + (size_t)head * D; },
+        [&](int head) { return p.ws_m + (row0 + head) * p.P_max + part; },
+        [&](int head) { return p.ws_l + (row0 + head) * p.P_max + part; },
+        [&](int head) { return p.ws_o + ((row0 + head) * p.P_max + part) * D; });
+}
+
+// Mixed block sizes ("vLLM 推理引擎源码级拆解" §1.3: 8, 16 or 32 tokens per
+// block, chosen per request).  The pool is kept in pages of p.bs tokens, laid
+// out like a pool of p.bs-token blocks; a block of bs_s = seq_bs[s] tokens is
+// bs_s / p.bs consecutive pages, and table entries give its first page.  So
+// the table is walked in bs_s-token steps, a block's base is (entry * p.bs)
+// rows in, and its descriptor covers bs_s rows.  Each wavefront runs the
+// 8-token-block loop or the larger-block one for its own sequence.  A block
+// size outside [page, 32] is taken as the nearest of the two.
+template <class Q, class C, int D>
+__global__ __launch_bounds__(64 * kWaves) void decode_mixed_kernel(DecodeParams p) {
+    typedef TileMath<Q, C, D, false> TM;
+    typedef typename TM::T T;
+    const TM tm;
+    const int lane = tm.lane;
+    int s, part, h;
+    if (!select_unit(p, &s, &part, &h)) return;
+
+    const int bs_s = __builtin_amdgcn_readfirstlane(p.seq_bs[s]);
+    const int shift = bs_s >= 32 ? 5 : max(bs_s >= 16 ? 4 : 3, p.page_shift);
+    const int G = p.G;
+    int L = p.lens[s];
+    L = L < p.len_cap ? L : p.len_cap;
+    L = L < (p.max_blocks << shift) ? L : (p.max_blocks << shift);
+    T* out = (T*)p.out + ((size_t)s * p.Hq + (size_t)h * G) * D;
+    if (L <= 0) {
+        for (int i = lane; i < G * D; i += 64) out[i] = (T)0.0f;
+        return;
     }
+    int t_begin = 0, t_end = L;
+    bool final_out = true;
+    if (p.P > 0) {
+        t_begin = part * p.P;
+        t_end = min(L, t_begin + p.P);
+        final_out = (L + p.P - 1) / p.P <= 1;
+    }
+
+    typename TM::v8 qb[TM::KS];
+    tm.load_q((const T*)p.q + ((size_t)s * p.Hq + (size_t)h * G) * D, G, qb);
+    Head hd = make_head<C, D>(p, h);                  // pages of p.bs tokens
+    const uint32_t head_off = (uint32_t)(h * D * C::kBytes);
+    hd.bs_shift = shift;
+    hd.rec_bytes = (hd.row_bytes << shift) - head_off;
+    hd.nb_last = (uint32_t)(p.NB - (1 << (shift - p.page_shift)));
+    typename TM::Acc acc;
+    tm.reset(acc);
+    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
+    if (shift == 3)
+        walk_unit<true, 2>(tm, hd, table, t_begin, t_end, qb, p.scale_log2, acc);
+    else
+        walk_unit<false, 4>(tm, hd, table, t_begin, t_end, qb, p.scale_log2, acc);
 
     const size_t row0 = (size_t)s * p.Hq + (size_t)h * G;
     tm.finish(
@@ -139,7 +215,26 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <class Q, class C>
+hipError_t launch_mixed_d(const DecodeParams& p, hipStream_t st) {
+    const long units = (long)p.S * p.P_max * p.Hkv;
+    const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(64 * kWaves);
+    if (p.D == 64) return launch_kernel(decode_mixed_kernel<Q, C, 64>, grid, block, st, p);
+    if (p.D == 128) return launch_kernel(decode_mixed_kernel<Q, C, 128>, grid, block, st, p);
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_decode_mixed(int qdt, int cdt, const DecodeParams& p, hipStream_t st) {
+    if (!decode_mfma_supported(qdt, cdt, p.D, p.G)) return hipErrorInvalidValue;
+    if (qdt == kBF16) {
+        if (cdt == kFP8) return launch_mixed_d<BF16, FP8>(p, st);
+        return launch_mixed_d<BF16, BF16>(p, st);
+    }
+    if (cdt == kFP8) return launch_mixed_d<F16, FP8>(p, st);
+    return launch_mixed_d<F16, F16>(p, st);
+}
 
 bool decode_mfma_supported(int qdt, int cdt, int D, int G) {
     const bool types = (qdt == kF16 || qdt == kBF16) && (cdt == qdt || cdt == kFP8);

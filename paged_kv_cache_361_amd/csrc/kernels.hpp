@@ -40,6 +40,8 @@ struct DecodeParams {
     int max_groups;        // multi-query: query-token groups per sequence in the grid
     int32_t* ws_len;       // multi-query split: tokens seen by each query token, for the reduce
     int len_rows;          // multi-query split: entries of ws_len (num_seqs * max_query_len)
+    const int32_t* seq_bs; // mixed block sizes: tokens per block of each sequence [S]
+    int page_shift;        // mixed block sizes: log2 of the pool's page (bs is the page)
     int S, Hq, Hkv, D, G, bs, NB, max_blocks;
     int len_cap;           // min(max_seq_len, max_blocks * bs)
     int P;                 // partition size, 0 = one pass
@@ -173,6 +175,8 @@ bool decode_valu_supported(int qdt, int cdt, int D, int G);
 hipError_t launch_decode_valu(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 bool decode_mfma_supported(int qdt, int cdt, int D, int G);
 hipError_t launch_decode_mfma(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
+// Mixed block sizes per sequence over a pool of pages (p.bs tokens each).
+hipError_t launch_decode_mixed(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 // Balanced mode (matrix-core kernel): resident wavefronts per CU of the
 // kernel that would serve these types and shapes (0 if unknown), and launch.
 int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S);

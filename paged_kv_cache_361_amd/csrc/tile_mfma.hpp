@@ -239,19 +239,28 @@ struct TileMath {
     // the window when live).
     __device__ inline void issue(const Head& hd, int t0, int lim, int wb, int win,
                                  Tile& tl) const {
+        issue_as<PAIR>(hd, t0, lim, wb, win, tl);
+    }
+
+    // issue() for 8-token blocks (PR) or larger ones, whatever the tile's
+    // own PAIR: a kernel whose wavefronts meet both block sizes picks per
+    // wavefront.
+    template <bool PR>
+    __device__ inline void issue_as(const Head& hd, int t0, int lim, int wb, int win,
+                                    Tile& tl) const {
         uint32_t pa = 0, pb = 0;
         if (lim >= 0) {
             const int blk = (t0 >> hd.bs_shift) - wb;
             pa = (uint32_t)__builtin_amdgcn_readlane(win, blk);
             pa = pa < hd.nb_last ? pa : hd.nb_last;
-            if (PAIR && lim >= 8) {
+            if (PR && lim >= 8) {
                 pb = (uint32_t)__builtin_amdgcn_readlane(win, blk + 1);
                 pb = pb < hd.nb_last ? pb : hd.nb_last;
             }
         }
         const rsrc_t ka = make_rsrc(hd.kbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
         const rsrc_t va = make_rsrc(hd.vbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
-        if constexpr (!PAIR) {
+        if constexpr (!PR) {
             const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
             const uint32_t krow = j16 <= lim ? (in_blk + (uint32_t)j16) * hd.row_bytes : kOOB;
 #pragma unroll

@@ -63,3 +63,45 @@ def relabel(k_cache, v_cache, tables, rng):
     k2[pi] = k_cache
     v2[pi] = v_cache
     return k2, v2, pi[tables]
+
+
+def build_mixed_pool(Ks, Vs, seq_bs, page, *, dtype, rng=None, spare_groups=2):
+    """A pool of `page`-token pages where sequence s has blocks of seq_bs[s]
+    tokens, each seq_bs[s] / page consecutive pages ("vLLM 推理引擎源码级拆解"
+    §1.3 block sizes per request; pages are this library's layout for them).
+    Each block is placed in its own piece of a shuffled 32-token group of
+    pages, and its tokens are copied with one slice into the pool seen as
+    rows: block j of sequence s starts at row table[s][j] * page.
+
+    Returns (k_cache, v_cache, block_tables, seq_lens)."""
+    rng = rng or np.random.default_rng(0)
+    S = len(Ks)
+    Hkv, D = Ks[0].shape[1], Ks[0].shape[2]
+    lens = np.array([k.shape[0] for k in Ks], np.int32)
+    gp = 32 // page
+    nblk = [-(-int(L) // int(b)) for L, b in zip(lens, seq_bs)]
+    groups_needed = sum(-(-n * int(b) // 32) for n, b in zip(nblk, seq_bs))
+    n_groups = groups_needed + spare_groups
+    order = list(rng.permutation(n_groups))
+    poison = workloads.POISON[dtype]
+    npdt = workloads.NP_DTYPE[dtype]
+    NP = n_groups * gp
+    kc = np.full((NP, page, Hkv, D), poison, npdt)
+    vc = np.full((NP, page, Hkv, D), poison, npdt)
+    krows = kc.reshape(NP * page, Hkv, D)
+    vrows = vc.reshape(NP * page, Hkv, D)
+    max_blocks = max(nblk)
+    tables = np.full((S, max_blocks), order[-1] * gp, np.int32)
+    for s in range(S):
+        b = int(seq_bs[s])
+        free = []
+        for j in range(nblk[s]):
+            if not free:                   # a fresh group, cut into 32 / b blocks
+                g = order.pop(0)
+                free = [g * gp + k * (b // page) for k in range(32 // b)]
+            first = free.pop(0)
+            tables[s, j] = first
+            lo, hi = j * b, min((j + 1) * b, int(lens[s]))
+            krows[first * page:first * page + hi - lo] = Ks[s][lo:hi]
+            vrows[first * page:first * page + hi - lo] = Vs[s][lo:hi]
+    return kc, vc, tables, lens

@@ -186,3 +186,26 @@ def test_multi_workspace_bytes_layout(pkv):
         up(4 * S * Qm)
     assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, 0) == 0
     assert pkv.multi_workspace_bytes(0, Qm, Hq, D, L, P) == 0
+
+
+def mixed_args(**kw):
+    a = dict(out=FAKE, q=FAKE, qdt=2, k=FAKE, v=FAKE, cdt=2, tables=FAKE, max_blocks=16,
+             lens=FAKE, sbs=FAKE, S=4, Hq=32, Hkv=8, D=128, page=8, NP=100, max_len=256,
+             scale=0.1, ks=1.0, vs=1.0, P=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return [a[k] for k in ("out", "q", "qdt", "k", "v", "cdt", "tables", "max_blocks",
+                           "lens", "sbs", "S", "Hq", "Hkv", "D", "page", "NP", "max_len",
+                           "scale", "ks", "vs", "P", "ws", "ws_bytes", "stream")]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), -1), (dict(sbs=None), -1), (dict(tables=None), -1),
+    (dict(qdt=7), -3), (dict(qdt=1, cdt=2), -3),
+    (dict(S=0), -2), (dict(Hq=30), -2), (dict(max_len=0), -2), (dict(NP=3), -2),
+    (dict(P=16), -2), (dict(P=48), -2), (dict(P=-1), -2),
+    (dict(P=64), -5), (dict(P=64, ws=FAKE, ws_bytes=64), -5),
+    (dict(qdt=0, cdt=0), -4), (dict(Hq=64, Hkv=2), -4), (dict(D=96), -4), (dict(page=12), -4),
+    (dict(out=FAKE + 8), -6), (dict(sbs=FAKE + 2), -6), (dict(max_blocks=(1 << 25) + 1), -2),
+])
+def test_mixed_rejects_bad_arguments(lib, kw, status):
+    assert lib.pkv_paged_attention_decode_mixed(*mixed_args(**kw)) == status

@@ -409,3 +409,76 @@ def test_multi_queries_before_the_sequence_are_zero(orc):
                           scale=0.125)
     assert np.all(out[:2] == 0.0)
     assert np.isfinite(out[2:]).all() and np.any(out[2:] != 0.0)
+
+
+# --- mixed block sizes ([P1] "vLLM 0.5 ..." §1.3) ------------------------------
+
+from pool_util import build_mixed_pool  # noqa: E402
+
+
+@pytest.mark.parametrize("seed,page", [(0, 8), (1, 8), (2, 16)])
+def test_mixed_matches_dense_softmax(orc, seed, page):
+    """Sequences with 8-, 16- and 32-token blocks over one pool of pages,
+    against the library brute force on the logical K/V."""
+    rng = np.random.default_rng(700 + seed)
+    dtype = ["bf16", "f16", "f32"][seed]
+    Hkv, G, D = 2, 4, 64
+    sizes = [b for b in (8, 16, 32) if b >= page]
+    S = 6
+    lens = rng.integers(1, 140, size=S)
+    seq_bs = np.array([sizes[i % len(sizes)] for i in range(S)], np.int32)
+    Ks, Vs = rand_logical(rng, lens, Hkv, D, dtype)
+    kc, vc, tables, sl = build_mixed_pool(Ks, Vs, seq_bs, page, dtype=dtype, rng=rng)
+    q = workloads.draw(rng, (S, Hkv * G, D), dtype)
+    scale = 1.0 / math.sqrt(D)
+    out = orc.paged_decode_mixed(q, kc, vc, tables, sl, seq_bs, q_dtype=dtype,
+                                 cache_dtype=dtype, scale=scale)
+    for s in range(S):
+        for hq in range(Hkv * G):
+            ref = dense_attention_fp64(widen(q[s, hq], dtype, orc),
+                                       widen(Ks[s][:, hq // G], dtype, orc),
+                                       widen(Vs[s][:, hq // G], dtype, orc), scale)
+            np.testing.assert_allclose(out[s, hq], ref, rtol=0, atol=1e-12)
+
+
+def test_mixed_equals_page_tables(orc):
+    """A block of k pages is the same as k one-page blocks: expanding every
+    table entry e of a bs_s-token block into e, e+1, .., e + bs_s/page - 1
+    gives a uniform page-sized table with bit-identical output."""
+    rng = np.random.default_rng(710)
+    page, Hkv, G, D = 8, 2, 2, 64
+    lens = rng.integers(1, 200, size=5)
+    seq_bs = np.array([8, 16, 32, 16, 32], np.int32)
+    Ks, Vs = rand_logical(rng, lens, Hkv, D, "bf16")
+    kc, vc, tables, sl = build_mixed_pool(Ks, Vs, seq_bs, page, dtype="bf16", rng=rng)
+    q = workloads.draw(rng, (5, Hkv * G, D), "bf16")
+    kw = dict(q_dtype="bf16", cache_dtype="bf16", scale=0.125)
+    mixed = orc.paged_decode_mixed(q, kc, vc, tables, sl, seq_bs, **kw)
+    rows = []
+    for s in range(5):
+        k = int(seq_bs[s]) // page
+        nblk = -(-int(lens[s]) // int(seq_bs[s]))
+        rows.append([int(tables[s, j]) + i for j in range(nblk) for i in range(k)])
+    wide = np.zeros((5, max(len(r) for r in rows)), np.int32)
+    for s, r in enumerate(rows):
+        wide[s, :len(r)] = r
+    uniform = orc.paged_decode(q, kc, vc, wide, sl, **kw)
+    assert np.array_equal(mixed, uniform)
+
+
+def test_mixed_with_page_sized_blocks_is_plain_decode(orc):
+    rng = np.random.default_rng(720)
+    Ks, Vs = rand_logical(rng, [5, 40, 77], 2, 64, "f16")
+    kc, vc, tables, sl = build_pool(Ks, Vs, 16, dtype="f16", rng=rng)
+    q = workloads.draw(rng, (3, 4, 64), "f16")
+    kw = dict(q_dtype="f16", cache_dtype="f16", scale=0.125)
+    assert np.array_equal(
+        orc.paged_decode_mixed(q, kc, vc, tables, sl, np.full(3, 16, np.int32), **kw),
+        orc.paged_decode(q, kc, vc, tables, sl, **kw))
+
+
+def test_mixed_block_size_rule():
+    """[P1] §1.3: short requests (< 128 tokens) 8 per block, medium (< 2048)
+    16, long 32."""
+    assert [workloads.block_size_for_length(L) for L in (1, 127, 128, 2047, 2048, 9000)] == \
+        [8, 8, 16, 16, 32, 32]

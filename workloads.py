@@ -246,6 +246,132 @@ def make_case(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, *,
                 notes={"prefix_len": prefix_len, "append_last": append_last})
 
 
+# --- mixed block sizes ---------------------------------------------------
+
+def block_size_for_length(L: int) -> int:
+    """Tokens per block by expected length, the thresholds of "vLLM 推理引擎源码级拆解"
+    §1.3 (short < 128: 8; medium < 2048: 16; long: 32); here the length
+    itself stands in for the estimate."""
+    return 8 if L < 128 else (16 if L < 2048 else 32)
+
+
+@dataclass
+class MixedCase:
+    """A pool of pages (case.bs = page tokens, case.NB = pages) whose
+    sequences have blocks of seq_bs[s] tokens: seq_bs[s] / page consecutive
+    pages from the page the table names."""
+    case: Case
+    seq_bs: np.ndarray
+
+
+def make_mixed_case(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, page: int, *,
+                    q_dtype: str, cache_dtype: str, block_sizes=None,
+                    src_dtype: Optional[str] = None, pool_factor: float = 1.1,
+                    max_seq_len: Optional[int] = None, append_last: bool = False,
+                    rng: Optional[np.random.Generator] = None) -> MixedCase:
+    """Seeded case with a block size per sequence (default: by length, as
+    block_size_for_length).  Pages are handed out in aligned groups of 32
+    tokens (32 / page pages), shuffled: a 32-token block takes a group, a
+    16-token block half of one, an 8-token block a quarter, so every block's
+    pages are consecutive.  Unused pages and the dead rows of each last
+    block are poisoned.  fp8: every live token arrives through the writer,
+    as in make_case."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    if callable(lens):
+        lens = lens(rng)
+    seq_lens = np.asarray(lens, dtype=np.int64)
+    S = seq_lens.size
+    if block_sizes is None:
+        seq_bs = np.array([block_size_for_length(int(L)) for L in seq_lens], np.int64)
+    else:
+        seq_bs = np.asarray(block_sizes(rng, seq_lens) if callable(block_sizes)
+                            else block_sizes, np.int64)
+    assert np.all(seq_bs >= page) and np.all(seq_bs % page == 0) and np.all(seq_bs <= 32)
+    src_dtype = src_dtype or cache_dtype
+    write_all = cache_dtype == "fp8"
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max())
+    max_blocks = max(1, -(-max_seq_len // page))       # enough for the smallest block
+    gp = 32 // page                                    # pages per 32-token group
+    nblk = -(-seq_lens // seq_bs)
+    need_groups = int(math.ceil(float((nblk * seq_bs).sum()) / 32))
+    n_groups = int(math.ceil(pool_factor * need_groups - 1e-9)) + 1
+    NP = n_groups * gp
+    groups = rng.permutation(n_groups).astype(np.int64)
+    pad_page = int(groups[-1]) * gp
+    tables = np.full((S, max_blocks), pad_page, np.int32)
+    gi = 0
+    for size in (32, 16, 8):                           # largest blocks first
+        owners = [(s, j) for s in range(S) if seq_bs[s] == size for j in range(nblk[s])]
+        per = 32 // size
+        pieces = []
+        while len(pieces) < len(owners):
+            g = int(groups[gi])
+            gi += 1
+            pieces += [g * gp + k * (size // page) for k in range(per)]
+        pieces = rng.permutation(np.asarray(pieces, np.int64))[:len(owners)]
+        for (s, j), first in zip(owners, pieces):
+            tables[s, j] = first
+    assert gi < n_groups
+
+    shape = (NP, page, Hkv, D)
+    if write_all:
+        k_cache = np.full(shape, POISON[cache_dtype], NP_DTYPE[cache_dtype])
+        v_cache = np.full(shape, POISON[cache_dtype], NP_DTYPE[cache_dtype])
+    else:
+        k_cache = draw(rng, shape, cache_dtype)
+        v_cache = draw(rng, shape, cache_dtype)
+    query = draw(rng, (S, Hq, D), q_dtype)
+
+    def rows_of(s, t):                                 # pool rows of tokens t of sequence s
+        b = int(seq_bs[s])
+        return tables[s, t // b].astype(np.int64) * page + t % b
+
+    def row_of(s, t):
+        return int(rows_of(s, np.array([t]))[0])
+
+    if not write_all:
+        live = np.zeros(NP * page, bool)
+        cached = seq_lens - 1 if append_last else seq_lens
+        for s in range(S):
+            live[rows_of(s, np.arange(int(cached[s])))] = True
+        kf = k_cache.reshape(NP * page, Hkv, D)
+        vf = v_cache.reshape(NP * page, Hkv, D)
+        kf[~live] = POISON[cache_dtype]
+        vf[~live] = POISON[cache_dtype]
+    if write_all:
+        slots = np.concatenate([rows_of(s, np.arange(int(seq_lens[s]))) for s in range(S)])
+    elif append_last:
+        slots = [row_of(s, int(seq_lens[s]) - 1) for s in range(S)]
+    else:
+        slots = []
+    T = len(slots)
+    new_key = draw(rng, (T, Hkv, D), src_dtype)
+    new_value = draw(rng, (T, Hkv, D), src_dtype)
+    k_scale = v_scale = 1.0
+    if cache_dtype == "fp8":
+        k_scale = amax_scale(new_key, src_dtype)
+        v_scale = amax_scale(new_value, src_dtype)
+    c = Case(name=name, seed=seed, S=S, Hq=Hq, Hkv=Hkv, D=D, bs=page, NB=NP,
+             q_dtype=q_dtype, cache_dtype=cache_dtype, src_dtype=src_dtype,
+             scale=float(np.float32(1.0 / math.sqrt(D))), max_seq_len=int(max_seq_len),
+             partition_size=0, seq_lens=seq_lens.astype(np.int32), block_tables=tables,
+             query=query, k_cache=k_cache, v_cache=v_cache, new_key=new_key,
+             new_value=new_value, slot_mapping=np.asarray(slots, np.int64).reshape(T),
+             k_scale=k_scale, v_scale=v_scale, pad_block=pad_page,
+             notes={"append_last": append_last, "mixed": True})
+    return MixedCase(c, seq_bs.astype(np.int32))
+
+
+def mixed_block_sizes(S: int = 256) -> MixedCase:
+    """The Llama-3-8B GQA decode shape with each sequence's block size picked
+    by its length (8 / 16 / 32 tokens), over a pool of 8-token pages."""
+    return make_mixed_case("mixed-bs-llama3-8b", 8, lambda r: llama3_8b_gqa_lens(r, S),
+                           32, 8, 128, 8, q_dtype="bf16", cache_dtype="bf16",
+                           max_seq_len=4096, append_last=True)
+
+
 # --- the five workloads ------------------------------------------------
 
 def tiny_f32() -> Case:
