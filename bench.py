@@ -48,15 +48,15 @@ def log(*a):
 def balanced_split(lens: np.ndarray, Hkv: int, nW: int):
     """The balanced split's pieces, replayed on the host: the streams
     (sequence, KV head) of 16-token tiles laid end to end and cut into chunks
-    by the guided schedule (nW chunks of max(1, 7A/10) tiles, nW of
-    max(1, A/4), then max(4, A/8), A = T / nW).  Returns (number of streams
+    by the guided schedule (nW chunks of max(1, 4A/5) tiles, nW of
+    max(1, A/7), then max(4, A/16), A = T / nW).  Returns (number of streams
     spread over several chunks, partial entries they write per query head)."""
     nt = -(-np.maximum(lens.astype(np.int64), 0) // 16)
     T = int(nt.sum()) * Hkv
     if T == 0:
         return 0, 0
     A = T // nW
-    C1, C2, C3 = max(1, A * 7 // 10), max(1, A // 4), max(4, A // 8)
+    C1, C2, C3 = max(1, A * 4 // 5), max(1, A // 7), max(4, A // 16)
     e1, e2 = min(nW * C1, T), min(nW * (C1 + C2), T)
 
     def chunk_of(x):

@@ -166,8 +166,8 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          num_seqs <= 8192): the whole batch's work -- every (sequence, KV
  *          head) pair's tokens in 16-token tiles, laid end to end -- is cut
  *          into chunks by a guided schedule (large chunks first, small ones
- *          last) and spread over a persistent grid of as many wavefronts as
- *          the GPU holds at once (at most 2048); each wavefront starts on a
+ *          last) and spread over a persistent grid of one wavefront per
+ *          SIMD (at most 2048); each wavefront starts on a
  *          chunk of its own and then takes chunks in order from a counter,
  *          so that ragged lengths and uneven wavefront speeds cost no load
  *          balance.  One kernel is enqueued.  A

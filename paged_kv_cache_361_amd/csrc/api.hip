@@ -74,7 +74,7 @@ inline int balanced_grid_waves(int qdt, int cdt, int D, int bs, int S) {
         cus <= 0)
         cus = 256;
     int per_cu = decode_balanced_waves_per_cu(qdt, cdt, D, bs, S);
-    if (per_cu <= 0) per_cu = 8;
+    if (per_cu <= 0) per_cu = 4;
     const long n = (long)cus * per_cu;
     return (int)(n < kBalancedMaxWaves ? n : kBalancedMaxWaves);
 }

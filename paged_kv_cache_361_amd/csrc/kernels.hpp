@@ -65,11 +65,11 @@ struct ReduceParams {
 //
 // The T tiles of a batch (16 tokens of one (sequence, KV head) stream each,
 // streams laid end to end) are cut into chunks by a guided schedule that
-// depends only on T and the grid size nW: nW chunks of C1 tiles (70% of an
-// even share A = T / nW), then nW chunks of C2 (25%), then chunks of
-// C3 = max(4, A / 8) up to T.  (Sizes measured best on MI355X for ragged
-// batches: a smaller first share costs more chunk switches and counter
-// adds; smaller last chunks saturate the counter.)  Chunk c starts at tile
+// depends only on T and the grid size nW: nW chunks of C1 tiles (80% of an
+// even share A = T / nW), then nW chunks of C2 (A / 7), then chunks of
+// C3 = max(4, A / 16) up to T.  (Sizes measured best on MI355X for ragged
+// batches on a grid of one wave per SIMD; neighbouring choices were 1-15 us
+// slower per call.)  Chunk c starts at tile
 // chunk_begin(c); the decode grid takes chunks 0..nW-1 statically and the
 // rest from a counter, and the reduce finds a stream's chunks with
 // chunk_of().
@@ -109,9 +109,9 @@ __host__ __device__ inline Sched make_sched(int T, int nW) {
     q.T = T;
     q.nW = nW;
     const int A = nW > 0 ? T / nW : 0;
-    q.C1 = A * 7 / 10 > 1 ? A * 7 / 10 : 1;
-    q.C2 = A / 4 > 1 ? A / 4 : 1;
-    q.C3 = A / 8 > 4 ? A / 8 : 4;
+    q.C1 = A * 4 / 5 > 1 ? A * 4 / 5 : 1;
+    q.C2 = A / 7 > 1 ? A / 7 : 1;
+    q.C3 = A / 16 > 4 ? A / 16 : 4;
     const int64_t e1 = (int64_t)nW * q.C1;
     const int64_t e2 = e1 + (int64_t)nW * q.C2;
     q.e1 = (int)(e1 < T ? e1 : T);
@@ -140,9 +140,9 @@ __host__ __device__ inline int chunk_of(const Sched& q, int x) {
 }
 
 // Most chunks any batch can produce on a grid of nW waves (the workspace
-// bound): phases one and two hold 2 nW chunks; the third covers fewer than
-// (0.05 A + 2.7) nW tiles in chunks of max(4, A/8), fewer than 1.1 nW + 1
-// chunks for every A.  The bound keeps room to spare.
+// bound): phases one and two hold 2 nW chunks; C1 + C2 > 0.94 A - 2, so the
+// third covers fewer than (0.06 A + 3) nW tiles in chunks of max(4, A/16),
+// fewer than 2 nW + 1 chunks for every A.  The bound keeps room to spare.
 __host__ __device__ inline int64_t max_chunks(int nW) { return 5 * (int64_t)nW + 8; }
 
 // Launches a kernel whose only parameter is a parameter struct and returns

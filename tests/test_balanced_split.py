@@ -3,8 +3,8 @@
 The decode kernel lays the batch's 16-token tiles end to end per (sequence,
 KV head) stream and cuts them into chunks by a guided schedule that depends
 only on the tile count T and the grid size nW: nW chunks of
-C1 = max(1, 7A/10) tiles, nW of C2 = max(1, A/4), then chunks of
-C3 = max(4, A/8), with A = T / nW.  Inside a chunk a piece of a stream is a
+C1 = max(1, 4A/5) tiles, nW of C2 = max(1, A/7), then chunks of
+C3 = max(4, A/16), with A = T / nW.  Inside a chunk a piece of a stream is a
 segment: a whole stream writes its output, any other segment is the first
 (slot 0) or last (slot 1) of its chunk.  The reduce finds the chunks of a
 stream with chunk_of() and reads slot 1 of the first one when the stream
@@ -20,7 +20,7 @@ import pytest
 
 def sched(T, nW):
     A = T // nW
-    C1, C2, C3 = max(1, A * 7 // 10), max(1, A // 4), max(4, A // 8)
+    C1, C2, C3 = max(1, A * 4 // 5), max(1, A // 7), max(4, A // 16)
     e1 = min(nW * C1, T)
     e2 = min(nW * C1 + nW * C2, T)
     if T <= 0:
