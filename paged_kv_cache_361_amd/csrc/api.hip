@@ -199,8 +199,11 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u) ||
         ((uintptr_t)query_start & 3u))
         return PKV_ERR_ALIGN;
-    const int qpg = 16 / G;                        // query tokens per wavefront
-    const int64_t groups = (max_query_len + qpg - 1) / qpg;
+    const int qpg = 16 / G;                        // query tokens per column block
+    // long query runs without a split: 2 or 4 column blocks per wavefront
+    const int nb = partition_size > 0 || max_query_len <= qpg ? 1
+                   : (max_query_len >= 4 * qpg ? 4 : 2);
+    const int64_t groups = (max_query_len + (int64_t)qpg * nb - 1) / ((int64_t)qpg * nb);
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
     const int len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
     MultiWs w;
@@ -227,6 +230,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     p.epoch = 0;
     p.q_start = query_start;
     p.max_groups = (int)groups;
+    p.col_blocks = nb;
     p.ws_len = nullptr;
     p.len_rows = num_seqs * max_query_len;
     p.seq_bs = nullptr;
@@ -370,6 +374,7 @@ int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_d
     p.epoch = 0;
     p.q_start = nullptr;
     p.max_groups = 0;
+    p.col_blocks = 1;
     p.ws_len = nullptr;
     p.len_rows = 0;
     p.seq_bs = seq_block_sizes;
@@ -459,6 +464,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     p.epoch = 0;
     p.q_start = nullptr;
     p.max_groups = 0;
+    p.col_blocks = 1;
     p.ws_len = nullptr;
     p.len_rows = 0;
     p.seq_bs = nullptr;

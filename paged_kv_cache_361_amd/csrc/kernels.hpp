@@ -37,7 +37,8 @@ struct DecodeParams {
     int nW;                // balanced mode: wavefronts of the persistent grid
     uint32_t epoch;        // balanced mode: this call's number (never repeats soon)
     const int32_t* q_start;  // multi-query: [S + 1] first query token of each sequence
-    int max_groups;        // multi-query: query-token groups per sequence in the grid
+    int max_groups;        // multi-query: wavefronts per (sequence, KV head) in the grid
+    int col_blocks;        // multi-query: groups of 16 / G query tokens per wavefront
     int32_t* ws_len;       // multi-query split: tokens seen by each query token, for the reduce
     int len_rows;          // multi-query split: entries of ws_len (num_seqs * max_query_len)
     const int32_t* seq_bs; // mixed block sizes: tokens per block of each sequence [S]

@@ -147,10 +147,118 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
         [&](int c) { return p.ws_o + (row_of(c) * p.P_max + part) * D; });
 }
 
+// Long query runs (chunked prefill): every wavefront of the kernel above
+// reads the sequence's K/V for its 16 / G tokens, so a 512-token chunk reads
+// it 128 times (from the caches after the first).  Here a wavefront carries
+// NB column blocks (NB * 16 / G consecutive query tokens, each block with
+// its own query operand, causal limits and accumulators) and feeds every K/V
+// tile it loads to all of them: NB times the arithmetic per byte loaded.
+// One pass (no split); one wavefront per SIMD, the accumulators and ring
+// spilling into the accumulation registers.
+template <class Q, class C, int D, bool PAIR, int DEPTH, int NB>
+__global__ __launch_bounds__(64 * kWaves, 1) void multi_query_wide_kernel(DecodeParams p) {
+    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef typename TM::T T;
+    typedef typename TM::v8 v8;
+    const TM tm;
+    const int lane = tm.lane;
+
+    const int unit = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cg = unit % p.max_groups;
+    const int h = (unit / p.max_groups) % p.Hkv;
+    const int s = unit / p.max_groups / p.Hkv;
+    if (s >= p.S) return;
+    const int G = p.G;
+    const int QPG = 16 / G;                            // query tokens per column block
+    const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[s]);
+    const int Qn = __builtin_amdgcn_readfirstlane(p.q_start[s + 1]) - q0;
+    const int qbase = cg * QPG * NB;                   // the wave's first query token
+    if (qbase >= Qn) return;
+    int L = __builtin_amdgcn_readfirstlane(p.lens[s]);
+    L = L < p.len_cap ? L : p.len_cap;
+    const int nq = min(QPG * NB, Qn - qbase);          // query tokens of this wave
+    const int t_end = L - Qn + qbase + nq;             // tokens the last one sees
+
+    // row of column c of block b
+    auto out_row = [&](int b, int c) {
+        return (T*)p.out +
+               ((size_t)(q0 + qbase + b * QPG + c / G) * p.Hq + (size_t)h * G + c % G) * D;
+    };
+    if (t_end <= 0) {                                  // every token precedes the sequence
+        for (int c = 0; c < nq * G; c++)
+            for (int i = lane; i < D; i += 64) out_row(0, c)[i] = (T)0.0f;
+        return;
+    }
+
+    v8 qb[NB][TM::KS];
+    int pc[NB];                                        // this lane's column: last token seen
+    int ncols[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        const int tb = qbase + b * QPG;
+        const int nqb = max(0, min(QPG, Qn - tb));
+        ncols[b] = nqb * G;
+        const T* qrow = (const T*)p.q +
+                        ((size_t)(q0 + tb + tm.j16 / G) * p.Hq + (size_t)h * G + tm.j16 % G) * D;
+#pragma unroll
+        for (int kk = 0; kk < TM::KS; kk++) {
+            const int d0 = TM::kFp8 ? (kk >> 1) * 64 + 16 * tm.g4 + (kk & 1) * 8 : 32 * kk + 8 * tm.g4;
+            qb[b][kk] = tm.j16 < ncols[b] ? *(const v8*)(qrow + d0) : v8{};
+        }
+        pc[b] = tm.j16 < ncols[b] ? L - Qn + tb + tm.j16 / G : -1;
+    }
+
+    const Head hd = make_head<C, D>(p, h);
+    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
+    const int nblk = (t_end + p.bs - 1) >> hd.bs_shift;
+    typename TM::Acc acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) tm.reset(acc[b]);
+    const int wtok = 64 << hd.bs_shift;
+    for (int w0 = 0; w0 < t_end; w0 += wtok) {
+        const int w1 = min(t_end, w0 + wtok);
+        const int wb = w0 >> hd.bs_shift;
+        const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
+        typename TM::Tile tl[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH; j++)
+            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
+#pragma unroll
+            for (int j = 0; j < DEPTH; j++) {
+                const int tj = t0 + 16 * j;
+                if (j == 0 || tj < w1) {
+#pragma unroll
+                    for (int b = NB - 1; b >= 0; b--)
+                        tm.template consume<true>(acc[b], qb[b], p.scale_log2, t_end - 1 - tj,
+                                                  tl[j], pc[b] - tj);
+                }
+                const int tn = tj + 16 * DEPTH;
+                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+            }
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; b++)
+        tm.finish_each(
+            acc[b], ncols[b], [&](int) { return true; }, p.v_scale,
+            [&](int c) { return out_row(b, c); }, [&](int) { return (float*)nullptr; },
+            [&](int) { return (float*)nullptr; }, [&](int) { return (float*)nullptr; });
+}
+
 // Tiles in flight per wavefront, as in the one-pass decode kernel.
 template <bool PAIR>
 constexpr int pipeline_depth() {
     return PAIR ? 2 : 4;
+}
+
+template <class Q, class C, int D, int NB>
+hipError_t launch_wide(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
+    if (p.bs == 8)
+        return launch_kernel(multi_query_wide_kernel<Q, C, D, true, pipeline_depth<true>(), NB>,
+                             grid, block, st, p);
+    return launch_kernel(multi_query_wide_kernel<Q, C, D, false, pipeline_depth<false>(), NB>,
+                         grid, block, st, p);
 }
 
 template <class Q, class C, int D, bool SPLIT>
@@ -165,6 +273,8 @@ hipError_t launch_ds(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t s
 template <class Q, class C, int D>
 hipError_t launch_dd(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
     if (p.P > 0) return launch_ds<Q, C, D, true>(p, grid, block, st);
+    if (p.col_blocks == 4) return launch_wide<Q, C, D, 4>(p, grid, block, st);
+    if (p.col_blocks == 2) return launch_wide<Q, C, D, 2>(p, grid, block, st);
     return launch_ds<Q, C, D, false>(p, grid, block, st);
 }
 
