@@ -195,3 +195,31 @@ def test_split_spec_verify_workload_full():
     mc = workloads.spec_verify()
     out, _ = run_multi(mc, 512)
     check(mc, out, oracle_multi(mc))
+
+
+def test_wide_rows_equal_single_token_calls():
+    """Rows of a long query run (several column blocks per wavefront) equal,
+    bit for bit, one-token calls over each token's own prefix: the tiles a
+    column does not see add exact zeros."""
+    mc = ragged(3, 30, 40, 600, lmin=60, lmax=300)
+    c = mc.case
+    out, d = run_multi(mc)
+    rng = np.random.default_rng(601)
+    checked = 0
+    for s in range(c.S):
+        a, b = int(mc.query_start[s]), int(mc.query_start[s + 1])
+        L, Qn = int(c.seq_lens[s]), b - a
+        for i in sorted(set(rng.integers(0, Qn, size=5).tolist()) | {0, Qn - 1}):
+            pos = L - Qn + i
+            if pos < 0:
+                continue
+            q1 = torch.from_numpy(np.ascontiguousarray(mc.query[a + i:a + i + 1]).view(np.int16)).view(torch.bfloat16).cuda()
+            o1 = torch.full_like(q1, float("nan"))
+            pkv.paged_attention_multi(o1, q1, d.k_cache, d.v_cache, d.tables[s:s + 1].contiguous(),
+                                      torch.tensor([pos + 1], dtype=torch.int32, device="cuda"),
+                                      torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
+                                      scale=c.scale, max_seq_len=c.max_seq_len, max_query_len=1)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(o1)[0], out[a + i]), (s, i)
+            checked += 1
+    assert checked >= 6
