@@ -282,7 +282,7 @@ PEAK_BF16_TFLOPS = 2500.0
 # Split-K partition size of the multi-query workloads: short drafts over long
 # contexts split like decode; 512-token prefill chunks already give one
 # wavefront per 16 / G tokens and need no split.
-MULTI_PARTITION = {"spec-verify": 1024, "chunked-prefill": 0}
+MULTI_PARTITION = {"spec-verify": -1, "chunked-prefill": 0}
 
 
 def multi_cost(mc):

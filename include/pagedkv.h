@@ -292,6 +292,16 @@ int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_d
  *                 rows that see at most P are written by the first kernel.
  *                 Partitions wholly after a query token's last visible
  *                 token are skipped for it.
+ *   PKV_PARTITION_BALANCED (-1), for speculative verification with
+ *                 max_query_len <= 16 / G (else PKV_ERR_UNSUPPORTED): the
+ *                 balanced split of pkv_paged_attention_decode over the
+ *                 (sequence, KV head) streams, whose last query token sees
+ *                 all L tokens; the B operand's columns are the (query
+ *                 token, head) pairs, each dropping the tokens past its own
+ *                 position.  The call enqueues the decode kernel and its
+ *                 reduce over the rows (query token, head); calls on one
+ *                 workspace must not overlap (its chunk counter, as for
+ *                 decode).
  *   workspace     device memory of at least pkv_multi_workspace_bytes(...)
  *                 bytes for the same num_seqs, max_query_len, num_q_heads,
  *                 head_dim, max_seq_len and partition_size, 16-byte aligned,
@@ -300,8 +310,9 @@ int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_d
  *                 share a workspace must be ordered on one stream.
  *
  * Errors (nothing launched): as for decode; PKV_ERR_SHAPE also for a
- * negative partition_size or one that is not a multiple of 16 and of
- * block_size; PKV_ERR_WORKSPACE for a missing or short workspace.
+ * negative partition_size other than PKV_PARTITION_BALANCED or one that is
+ * not a multiple of 16 and of block_size; PKV_ERR_WORKSPACE for a missing
+ * or short workspace.
  */
 int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
                               const void* k_cache, const void* v_cache,
@@ -316,11 +327,13 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
 
 /*
  * pkv_multi_workspace_bytes - bytes of workspace pkv_paged_attention_multi
- * needs for partition_size P > 0: with rows = num_seqs * max_query_len *
+ * needs.  PKV_PARTITION_BALANCED: a 256-byte header, num_seqs + 1 words,
+ * then m, l [2 * (5 * 2048 + 8) * 16] and o [same][head_dim] float32 (each
+ * part on a 256-byte boundary), whatever the lengths.  P > 0: with rows = num_seqs * max_query_len *
  * num_q_heads and P_max = ceil(max_seq_len / P), m and l [rows][P_max] and
  * o [rows][P_max][head_dim] float32, then [num_seqs * max_query_len] int32
- * context lengths, each part starting on a 256-byte boundary.  0 when
- * partition_size <= 0 or a size is not positive.  Host-only.
+ * context lengths, each part starting on a 256-byte boundary.  0 for
+ * partition_size 0 or a size that is not positive.  Host-only.
  */
 size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t max_query_len,
                                  int32_t num_q_heads, int32_t head_dim,

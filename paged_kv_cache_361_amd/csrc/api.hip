@@ -96,8 +96,22 @@ struct MultiWs {
 };
 
 inline bool multi_ws_layout(int S, int Qmax, int Hq, int D, int max_len, int P, MultiWs* w) {
-    if (S <= 0 || Qmax <= 0 || Hq <= 0 || D <= 0 || max_len <= 0 || P < 0) return false;
+    if (S <= 0 || Qmax <= 0 || Hq <= 0 || D <= 0 || max_len <= 0) return false;
     if (P == 0) return true;
+    if (P == PKV_PARTITION_BALANCED) {
+        // the balanced layout: header, tile prefix, then entries of 16
+        // columns (query token, head) per chunk slot
+        auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+        const int64_t n = 2 * max_chunks(kBalancedMaxWaves) * 16;
+        w->P_max = 1;
+        w->off_len = 256;                          // the tile prefix here
+        w->off_m = (size_t)up(256 + 4 * ((int64_t)S + 1));
+        w->off_l = w->off_m + (size_t)up(4 * n);
+        w->off_o = w->off_l + (size_t)up(4 * n);
+        w->bytes = w->off_o + (size_t)(4 * n * D);
+        return true;
+    }
+    if (P < 0) return false;
     w->P_max = (int)(((int64_t)max_len + P - 1) / P);
     const int64_t rows = (int64_t)S * Qmax * Hq;
     const int64_t n = rows * w->P_max;
@@ -183,7 +197,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         block_size <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
-        max_query_len <= 0 || partition_size < 0)
+        max_query_len <= 0 || (partition_size < 0 && partition_size != PKV_PARTITION_BALANCED))
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
     if (num_kv_heads > 4096) return PKV_ERR_SHAPE;
@@ -201,7 +215,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         return PKV_ERR_ALIGN;
     const int qpg = 16 / G;                        // query tokens per column block
     // long query runs without a split: 2 or 4 column blocks per wavefront
-    const int nb = partition_size > 0 || max_query_len <= qpg ? 1
+    const int nb = partition_size != 0 || max_query_len <= qpg ? 1
                    : (max_query_len >= 4 * qpg ? 4 : 2);
     const int64_t groups = (max_query_len + (int64_t)qpg * nb - 1) / ((int64_t)qpg * nb);
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
@@ -212,7 +226,15 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         return PKV_ERR_SHAPE;
     const int64_t units = (int64_t)num_seqs * w.P_max * groups * num_kv_heads;
     if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;
-    if (partition_size > 0) {
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
+    if (balanced) {
+        // one column group of 16 / G query tokens per sequence; tile counts
+        // are 32-bit on the device
+        if (max_query_len > qpg || num_seqs > kBalancedMaxSeqs) return PKV_ERR_UNSUPPORTED;
+        const int64_t tiles = (int64_t)num_seqs * num_kv_heads * ((len_cap + 15) / 16);
+        if (tiles > ((int64_t)1 << 31) - 1) return PKV_ERR_SHAPE;
+    }
+    if (partition_size != 0) {
         if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
     }
@@ -249,6 +271,37 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    if (balanced) {
+        p.P = 0;
+        p.P_max = 1;
+        p.ws_hdr = (int32_t*)workspace;
+        p.ws_pre = (int32_t*)((char*)workspace + w.off_len);
+        p.ws_m = (float*)((char*)workspace + w.off_m);
+        p.ws_l = (float*)((char*)workspace + w.off_l);
+        p.ws_o = (float*)((char*)workspace + w.off_o);
+        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size, num_seqs);
+        p.epoch = next_call_number();
+        hipError_t e = launch_decode_balanced(q_dtype, cache_dtype, p, stream);
+        if (e != hipSuccess) return launch_status(e);
+        ReduceParams r;
+        r.out = out;
+        r.ws_hdr = p.ws_hdr;
+        r.ws_pre = p.ws_pre;
+        r.ws_m = p.ws_m;
+        r.ws_l = p.ws_l;
+        r.ws_o = p.ws_o;
+        r.lens = seq_lens;
+        r.S = p.len_rows;
+        r.Hq = num_q_heads;
+        r.Hkv = num_kv_heads;
+        r.D = head_dim;
+        r.P = 0;
+        r.P_max = 1;
+        r.len_cap = len_cap;
+        r.q_start = query_start;
+        r.S_seq = num_seqs;
+        return launch_status(launch_reduce_balanced(q_dtype, r, stream));
+    }
     if (partition_size > 0) {
         p.ws_m = (float*)((char*)workspace + w.off_m);
         p.ws_l = (float*)((char*)workspace + w.off_l);
@@ -272,12 +325,14 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     r.P = partition_size;
     r.P_max = w.P_max;
     r.len_cap = len_cap;
+    r.q_start = nullptr;
+    r.S_seq = num_seqs;
     return launch_status(launch_reduce(q_dtype, r, stream));
 }
 
 size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_size) {
-    if (partition_size <= 0) return 0;
+    if (partition_size <= 0 && partition_size != PKV_PARTITION_BALANCED) return 0;
     MultiWs w;
     if (!multi_ws_layout(num_seqs, max_query_len, num_q_heads, head_dim, max_seq_len,
                          partition_size, &w))
@@ -562,6 +617,8 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* works
     p.P = balanced ? 0 : partition_size;
     p.P_max = w.P_max;
     p.len_cap = max_seq_len;
+    p.q_start = nullptr;
+    p.S_seq = num_seqs;
     if (balanced) return launch_status(launch_reduce_balanced(out_dtype, p, stream));
     return launch_status(launch_reduce(out_dtype, p, stream));
 }

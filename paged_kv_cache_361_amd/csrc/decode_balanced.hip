@@ -246,7 +246,13 @@ struct Walk {
     }
 };
 
-template <class Q, class C, int D, bool PAIR, int DEPTH>
+// MULTI: speculative verification (several query tokens per sequence, at
+// most 16 / G of them, query_start in p.q_start).  The last query token of a
+// sequence sees all its L tokens, so the streams, chunks and walk are those
+// of decode; the B operand's 16 columns are (query token, head) pairs as in
+// multi_query.hip, each column drops the tokens past its own position, and
+// rows and partial entries are per column (QPG * G of them per chunk slot).
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool MULTI>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeParams p) {
     typedef TileMath<Q, C, D, PAIR> TM;
     typedef typename TM::T T;
@@ -254,7 +260,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     extern __shared__ int lds[];
     int* pre = lds;                        // [S + 1] tile prefix
     int* len = lds + p.S + 1;              // [S] clamped lengths
+    int* qs = lds + 2 * p.S + 1;           // MULTI: [S + 1] query_start
     int32_t* hdr = p.ws_hdr;
+    if constexpr (MULTI) {
+        for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) qs[i] = p.q_start[i];
+    }
     wg_prefix(p, pre, len);
 
     const TM tm;
@@ -280,6 +290,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     const int G = p.G;
     const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
     unsigned long long* counter = (unsigned long long*)(hdr + kHdrCounter);
+    const int QPG = MULTI ? 16 / G : 1;    // query tokens per stream
+    const int ncol = QPG * G;              // columns (rows) per stream
+    // MULTI: first query row and query tokens (at most QPG) of sequence s
+    auto q_first = [&](int s) { return __builtin_amdgcn_readfirstlane(qs[s]); };
+    auto q_count = [&](int s) {
+        const int n = __builtin_amdgcn_readfirstlane(qs[s + 1]) - q_first(s);
+        return max(0, min(n, QPG));
+    };
 
     // ---- requests made one round ahead ---------------------------------
     // The index of the wave's next chunk (the counter's atomic add), the
@@ -337,10 +355,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
         return (int)Buf<4>::load(r, (uint32_t)(sp.wb + lane) * 4u);
     };
     // Query rows of the span's group as the B operand (heads past G read 0).
+    // MULTI: column j16 is head j16 % G of query token j16 / G.
     auto load_query = [&](const Span& sp, bool want, v8 (&qv)[TM::KS]) {
-        const char* base = (const char*)p.q + ((size_t)sp.s() * p.Hq + (size_t)sp.h() * G) * D * sizeof(T);
-        const rsrc_t r = make_rsrc(base, want ? (uint32_t)(G * D * sizeof(T)) : 0u);
-        const uint32_t row = (uint32_t)(tm.j16 * D * sizeof(T));
+        size_t first_row = (size_t)sp.s();
+        uint32_t range = (uint32_t)(G * D * sizeof(T));
+        uint32_t row = (uint32_t)(tm.j16 * D * sizeof(T));
+        if constexpr (MULTI) {
+            const int n = q_count(sp.s());
+            first_row = (size_t)q_first(sp.s());
+            range = n > 0 ? (uint32_t)(((n - 1) * p.Hq + G) * D * sizeof(T)) : 0u;
+            row = tm.j16 < n * G
+                      ? (uint32_t)(((tm.j16 / G) * p.Hq + tm.j16 % G) * D * sizeof(T))
+                      : kOOB;
+        }
+        const char* base = (const char*)p.q + (first_row * p.Hq + (size_t)sp.h() * G) * D * sizeof(T);
+        const rsrc_t r = make_rsrc(base, want ? range : 0u);
 #pragma unroll
         for (int kk = 0; kk < TM::KS; kk++) {
             const int d0 = TM::kFp8 ? (kk >> 1) * 64 + 16 * tm.g4 + (kk & 1) * 8 : 32 * kk + 8 * tm.g4;
@@ -428,6 +457,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     // consumer's span: its stream, length, end tile, chunk and flags
     int c_key = ps.key, c_L = ps.L, c_t1 = ps.t1, c_chunk = ps.chunk, c_flags = ps.flags;
     int crt = ps.t0;
+    // MULTI: this lane's column's last visible token in the consumer's
+    // sequence (-1: none)
+    auto column_limit = [&](int s, int L) {
+        const int n = q_count(s);
+        return tm.j16 < n * G ? L - n + tm.j16 / G : -1;
+    };
+    int c_pc = MULTI ? column_limit(c_key >> 12, c_L) : 0;
     typename TM::Acc acc;
     tm.reset(acc);
     producer_advance();
@@ -437,7 +473,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
 #pragma unroll
         for (int j = 0; j < DEPTH; j++) {
             const int tc = crt + j;
-            if (j == 0 || tc < c_t1) tm.consume(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j]);
+            if (j == 0 || tc < c_t1) {
+                if constexpr (MULTI)
+                    tm.template consume<true>(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j],
+                                              c_pc - (tc << 4));
+                else
+                    tm.consume(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j]);
+            }
             const int tp = prt + j;
             const int plim = has_ps && tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1;
             tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j]);
@@ -448,14 +490,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
         crt += DEPTH;
         if (crt >= c_t1) {
             if (c_flags & kLast) {
-                const size_t row0 = (size_t)(c_key >> 12) * p.Hq + (size_t)(c_key & 4095) * G;
-                const size_t e0 = ((size_t)c_chunk * 2 + ((c_flags & kSlot1) ? 1 : 0)) * G;
-                tm.finish(
-                    acc, G, (c_flags & kComplete) != 0, p.v_scale,
-                    [&](int head) { return (T*)p.out + (row0 + head) * D; },
-                    [&](int head) { return p.ws_m + e0 + head; },
-                    [&](int head) { return p.ws_l + e0 + head; },
-                    [&](int head) { return p.ws_o + (e0 + head) * D; });
+                const size_t e0 = ((size_t)c_chunk * 2 + ((c_flags & kSlot1) ? 1 : 0)) * ncol;
+                if constexpr (MULTI) {
+                    const int cs = c_key >> 12, ch = c_key & 4095;
+                    const size_t r0 = (size_t)q_first(cs);
+                    const bool complete = (c_flags & kComplete) != 0;
+                    tm.finish_each(
+                        acc, q_count(cs) * G, [&](int) { return complete; }, p.v_scale,
+                        [&](int c) {
+                            return (T*)p.out + ((r0 + c / G) * p.Hq + (size_t)ch * G + c % G) * D;
+                        },
+                        [&](int c) { return p.ws_m + e0 + c; },
+                        [&](int c) { return p.ws_l + e0 + c; },
+                        [&](int c) { return p.ws_o + (e0 + c) * D; });
+                } else {
+                    const size_t row0 = (size_t)(c_key >> 12) * p.Hq + (size_t)(c_key & 4095) * G;
+                    tm.finish(
+                        acc, G, (c_flags & kComplete) != 0, p.v_scale,
+                        [&](int head) { return (T*)p.out + (row0 + head) * D; },
+                        [&](int head) { return p.ws_m + e0 + head; },
+                        [&](int head) { return p.ws_l + e0 + head; },
+                        [&](int head) { return p.ws_o + (e0 + head) * D; });
+                }
             }
             if (!has_ps) break;
             c_key = ps.key;
@@ -464,6 +520,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             c_chunk = ps.chunk;
             c_flags = ps.flags;
             crt = ps.t0;
+            if constexpr (MULTI) c_pc = column_limit(c_key >> 12, c_L);
             if (c_flags & kFirst) {
                 // requested when the producer entered this segment
 #pragma unroll
@@ -492,23 +549,29 @@ constexpr int pipeline_depth() {
     return PAIR ? 4 : (D == 64 ? 8 : 6);
 }
 
-inline size_t lds_bytes(int S) { return (size_t)(2 * S + 1) * sizeof(int); }
+inline size_t lds_bytes(int S, bool multi) {
+    return (size_t)((multi ? 3 : 2) * S + (multi ? 2 : 1)) * sizeof(int);
+}
 
 template <class Q, class C, int D, bool PAIR>
 hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
     const dim3 grid((unsigned)((p.nW + kWaves - 1) / kWaves)), block(64 * kWaves);
     void* args[] = {const_cast<DecodeParams*>(&p)};
-    return hipLaunchKernel(
-        reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>()>),
-        grid, block, args, lds_bytes(p.S), st);
+    const bool multi = p.q_start != nullptr;
+    const void* k =
+        multi ? reinterpret_cast<const void*>(
+                    decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), true>)
+              : reinterpret_cast<const void*>(
+                    decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false>);
+    return hipLaunchKernel(k, grid, block, args, lds_bytes(p.S, multi), st);
 }
 
 template <class Q, class C, int D, bool PAIR>
 int resident_k(int S) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>()>,
-            64 * kWaves, lds_bytes(S)) != hipSuccess)
+            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false>,
+            64 * kWaves, lds_bytes(S, true)) != hipSuccess)
         return 0;
     // one workgroup per CU = one wavefront per SIMD, also where the
     // registers would hold two (head_dim 64)

@@ -60,6 +60,11 @@ struct ReduceParams {
     const int32_t* ws_pre; // balanced mode: tile prefix of the sequences [S + 1]
     const int32_t* lens;
     int S, Hq, Hkv, D, P, P_max, len_cap;
+    // balanced multi-query: rows are (query token, head), S counts query
+    // tokens; the sequences' query_start [S_seq + 1] maps a token to its
+    // sequence (nullptr: decode rows)
+    const int32_t* q_start;
+    int S_seq;
 };
 
 // ---- balanced split-K ------------------------------------------------------

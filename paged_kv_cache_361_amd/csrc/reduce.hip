@@ -142,7 +142,11 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
 
 // ---- balanced split ---------------------------------------------------------
 
-template <class O, int D, int WPR>
+// MULTI: rows are (query token, head) of a balanced multi-query call; a
+// token's column in its stream is (token - query_start[s]) * G + head % G,
+// and a token placed before its sequence (its column saw nothing) gets a
+// zero row.
+template <class O, int D, int WPR, bool MULTI>
 __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReduceParams p) {
     constexpr int RPB = kWaves / WPR;
     const int lane = threadIdx.x & 63;
@@ -155,24 +159,49 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
     const int Hkv = hdr[kHdrHkv];
     const int G = hdr[kHdrG];
     const int T = hdr[kHdrT];
-    // A workspace not written by a balanced decode of this shape: write
+    const int S = MULTI ? p.S_seq : p.S;
+    // A workspace not written by a balanced call of this shape: write
     // nothing rather than follow its indices.
     if (hdr[kHdrMagic] != kBalancedMagic || nW < 1 || nW > kBalancedMaxWaves || G < 1 ||
-        Hkv != p.Hkv || Hkv * G != p.Hq || T < 0 || p.ws_pre[p.S] != T)
+        Hkv != p.Hkv || Hkv * G != p.Hq || T < 0 || p.ws_pre[S] != T)
         return;
     const Sched q = make_sched(T, nW);
-    const int s = row / p.Hq;
     const int hq = row % p.Hq;
     const int h = hq / G;
-    const int g = hq % G;
+    int s = row / p.Hq, col = hq % G, ncol = G;
+    typedef typename O::T OT;
+    auto zero_row = [&]() {
+        if (sub == 0)
+            for (int d = lane; d < D; d += 64) ((OT*)p.out)[(size_t)row * D + d] = O::narrow(0.0f);
+    };
+    if constexpr (MULTI) {
+        const int tok = row / p.Hq;
+        if (tok >= p.q_start[S]) return;        // past the batch's query tokens
+        int lo = 0, hi = S;                     // q_start[lo] <= tok < q_start[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (p.q_start[mid] <= tok) lo = mid;
+            else hi = mid;
+        }
+        s = lo;
+        const int QPG = 16 / G;
+        const int n = min(p.q_start[s + 1] - p.q_start[s], QPG);
+        const int j = tok - p.q_start[s];
+        if (j >= n) return;                     // not served by the balanced kernel
+        col = j * G + hq % G;
+        ncol = QPG * G;
+        int L = p.lens[s];
+        L = L < p.len_cap ? L : p.len_cap;
+        if (L - n + j < 0) {                    // its column saw no token
+            zero_row();
+            return;
+        }
+    }
     const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
     if (p0 < 0 || p1 < p0 || p1 > T || (p1 - p0) % Hkv != 0) return;
     const int nt = (p1 - p0) / Hkv;
     if (nt == 0) {                              // no tokens: a zero row
-        if (sub == 0) {
-            typedef typename O::T OT;
-            for (int d = lane; d < D; d += 64) ((OT*)p.out)[(size_t)row * D + d] = O::narrow(0.0f);
-        }
+        zero_row();
         return;
     }
     const int g0 = p0 + h * nt;                 // first tile of stream (s, h)
@@ -184,7 +213,7 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
         p, c1 - c0 + 1,
         [&](int e) {
             const int slot = e == 0 ? slot0 : 0;
-            return ((size_t)(c0 + e) * 2 + slot) * G + g;
+            return ((size_t)(c0 + e) * 2 + slot) * ncol + col;
         },
         (size_t)row, wave, sub);
 }
@@ -195,11 +224,15 @@ hipError_t launch_w(const ReduceParams& p, bool wide, hipStream_t st) {
     const dim3 block(64 * kWaves);
     if (wide) {
         const dim3 grid((unsigned)rows);
-        if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 4>, grid, block, st, p);
+        if (BAL && p.q_start)
+            return launch_kernel(reduce_balanced_kernel<O, D, 4, true>, grid, block, st, p);
+        if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 4, false>, grid, block, st, p);
         return launch_kernel(reduce_kernel<O, D, 4>, grid, block, st, p);
     }
     const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
-    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 1>, grid, block, st, p);
+    if (BAL && p.q_start)
+        return launch_kernel(reduce_balanced_kernel<O, D, 1, true>, grid, block, st, p);
+    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 1, false>, grid, block, st, p);
     return launch_kernel(reduce_kernel<O, D, 1>, grid, block, st, p);
 }
 

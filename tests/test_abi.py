@@ -169,7 +169,9 @@ def multi_args(**kw):
     (dict(qdt=0, cdt=0), -4), (dict(Hq=64, Hkv=2), -4), (dict(D=96), -4), (dict(bs=12), -4),
     (dict(out=FAKE + 8), -6), (dict(qstart=FAKE + 2), -6),
     (dict(S=1 << 20, max_q=1 << 20, Hkv=8, Hq=8), -2),
-    (dict(P=-1), -2), (dict(P=24), -2), (dict(P=16, bs=32), -2),
+    (dict(P=-2), -2), (dict(P=24), -2), (dict(P=16, bs=32), -2),
+    (dict(P=-1), -4), (dict(P=-1, max_q=4), -5), (dict(P=-1, max_q=4, S=8193, NB=10 ** 6), -4),
+    (dict(P=-1, max_q=4, ws=FAKE, ws_bytes=4096), -5),
     (dict(P=64), -5), (dict(P=64, ws=FAKE, ws_bytes=1024), -5),
     (dict(P=64, ws=FAKE + 4, ws_bytes=1 << 40), -6),
 ])
@@ -186,6 +188,10 @@ def test_multi_workspace_bytes_layout(pkv):
         up(4 * S * Qm)
     assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, 0) == 0
     assert pkv.multi_workspace_bytes(0, Qm, Hq, D, L, P) == 0
+    # balanced: header, S + 1 prefix words, 16 columns per chunk slot
+    n = 2 * (5 * 2048 + 8) * 16
+    assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, -1) == up(256 + 4 * (S + 1)) + 2 * up(4 * n) + \
+        4 * n * D
 
 
 def mixed_args(**kw):

@@ -223,3 +223,64 @@ def test_wide_rows_equal_single_token_calls():
             assert np.array_equal(from_dev(o1)[0], out[a + i]), (s, i)
             checked += 1
     assert checked >= 6
+
+
+# ---- balanced split (verification: at most 16 / G query tokens) -------------
+
+def run_balanced(mc, ws=None, d=None, calls=3):
+    """Several calls on one workspace must agree bit for bit (they cut the
+    batch into the same chunks)."""
+    c = mc.case
+    if ws is None:
+        ws = multi_workspace(mc, pkv.PARTITION_BALANCED)
+    outs = []
+    for _ in range(calls):
+        o, d = run_multi(mc, pkv.PARTITION_BALANCED, ws, d)
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.array_equal(np.nan_to_num(o, nan=7.0), np.nan_to_num(outs[0], nan=7.0)), \
+            "balanced multi-query: calls on one workspace disagree"
+    return outs[0], d
+
+
+@pytest.mark.parametrize("G,Hkv", [(4, 8), (1, 8), (8, 2), (16, 1)])
+def test_balanced_verify_ragged(G, Hkv):
+    """Drafts of 0..16/G tokens, some longer than the sequence."""
+    mc = ragged(40, 0, 16 // G, 610 + G, Hq=G * Hkv, Hkv=Hkv, lmin=1, lmax=900)
+    out, _ = run_balanced(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+@pytest.mark.parametrize("bs,cache", [(8, "bf16"), (32, "fp8"), (16, "f16")])
+def test_balanced_verify_block_sizes(bs, cache):
+    dtype = "f16" if cache == "f16" else "bf16"
+    mc = ragged(24, 1, 4, 620 + bs, dtype=dtype, cache=cache, bs=bs, lmin=1, lmax=1200)
+    out, _ = run_balanced(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_balanced_verify_head_dim_64():
+    mc = ragged(30, 0, 4, 630, D=64, Hq=16, Hkv=4, lmin=1, lmax=700)
+    out, _ = run_balanced(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_balanced_verify_workspace_reused_by_a_smaller_batch():
+    """A workspace left by a larger batch (and one never written, all 0xFF)
+    gives the same rows as a fresh one; the result matches the split path."""
+    big = ragged(64, 2, 4, 640, lmin=100, lmax=2000)
+    small = ragged(9, 1, 4, 641, lmin=1, lmax=2000)
+    ws = multi_workspace(big, pkv.PARTITION_BALANCED, fill=0xFF)
+    out_big, _ = run_balanced(big, ws)
+    check(big, out_big, oracle_multi(big))
+    out_small, d = run_balanced(small, ws)
+    check(small, out_small, oracle_multi(small))
+    split, _ = run_multi(small, 64, d=d)
+    c = small.case
+    assert np.all(np.abs(out_small - split) <= 2 * TOL[c.cache_dtype] + 2 * half_ulp(split, c.q_dtype))
+
+
+def test_balanced_spec_verify_workload_full():
+    mc = workloads.spec_verify()
+    out, _ = run_balanced(mc, calls=2)
+    check(mc, out, oracle_multi(mc))
