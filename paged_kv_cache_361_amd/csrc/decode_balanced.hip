@@ -354,19 +354,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                                    (uint32_t)nblk * 4u);
         return (int)Buf<4>::load(r, (uint32_t)(sp.wb + lane) * 4u);
     };
+    // MULTI: column j16 is head j16 % G of query token j16 / G; its offset
+    // from the token group's first row, and the first query row and token
+    // count of the producer's sequence (kept beside its span, so the
+    // per-round request reads no LDS).
+    const int col_tok = MULTI ? tm.j16 / G : 0;
+    const uint32_t col_off =
+        MULTI ? (uint32_t)((col_tok * p.Hq + tm.j16 % G) * D * sizeof(T)) : 0u;
+    int ps_q0 = 0, ps_n = 0;
     // Query rows of the span's group as the B operand (heads past G read 0).
-    // MULTI: column j16 is head j16 % G of query token j16 / G.
     auto load_query = [&](const Span& sp, bool want, v8 (&qv)[TM::KS]) {
         size_t first_row = (size_t)sp.s();
         uint32_t range = (uint32_t)(G * D * sizeof(T));
         uint32_t row = (uint32_t)(tm.j16 * D * sizeof(T));
         if constexpr (MULTI) {
-            const int n = q_count(sp.s());
-            first_row = (size_t)q_first(sp.s());
-            range = n > 0 ? (uint32_t)(((n - 1) * p.Hq + G) * D * sizeof(T)) : 0u;
-            row = tm.j16 < n * G
-                      ? (uint32_t)(((tm.j16 / G) * p.Hq + tm.j16 % G) * D * sizeof(T))
-                      : kOOB;
+            first_row = (size_t)ps_q0;
+            range = ps_n > 0 ? (uint32_t)(((ps_n - 1) * p.Hq + G) * D * sizeof(T)) : 0u;
+            row = col_tok < ps_n ? col_off : kOOB;
         }
         const char* base = (const char*)p.q + (first_row * p.Hq + (size_t)sp.h() * G) * D * sizeof(T);
         const rsrc_t r = make_rsrc(base, want ? range : 0u);
@@ -379,6 +383,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
 
     Span ps, pn;
     walk_next(ps);                         // chunk w is not empty
+    if constexpr (MULTI) {
+        ps_q0 = q_first(ps.s());
+        ps_n = q_count(ps.s());
+    }
     v8 qb[TM::KS];                         // query of the consumer's segment
     load_query(ps, true, qb);
     int win = load_window(ps, true);
@@ -401,6 +409,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             has_ps = has_pn;
             if (has_ps) {
                 ps = pn;
+                if constexpr (MULTI) {
+                    ps_q0 = q_first(ps.s());
+                    ps_n = q_count(ps.s());
+                }
                 win = win_n;
                 prt = ps.t0;
                 hd = make_head<C, D>(p, ps.h());
@@ -461,7 +473,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     // sequence (-1: none)
     auto column_limit = [&](int s, int L) {
         const int n = q_count(s);
-        return tm.j16 < n * G ? L - n + tm.j16 / G : -1;
+        return col_tok < n ? L - n + col_tok : -1;
     };
     int c_pc = MULTI ? column_limit(c_key >> 12, c_L) : 0;
     typename TM::Acc acc;

@@ -142,10 +142,11 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
 
 // ---- balanced split ---------------------------------------------------------
 
-// MULTI: rows are (query token, head) of a balanced multi-query call; a
-// token's column in its stream is (token - query_start[s]) * G + head % G,
-// and a token placed before its sequence (its column saw nothing) gets a
-// zero row.
+// MULTI: rows of a balanced multi-query call, numbered (sequence s, query
+// token j < max_query_len of it, head) so that no search maps a row to its
+// sequence; the output row is (query_start[s] + j, head).  A token's column
+// in its stream is j * G + head % G, and a token placed before its sequence
+// (its column saw nothing) gets a zero row.
 template <class O, int D, int WPR, bool MULTI>
 __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReduceParams p) {
     constexpr int RPB = kWaves / WPR;
@@ -169,25 +170,21 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
     const int hq = row % p.Hq;
     const int h = hq / G;
     int s = row / p.Hq, col = hq % G, ncol = G;
+    size_t orow = (size_t)row;                  // output row
     typedef typename O::T OT;
     auto zero_row = [&]() {
         if (sub == 0)
-            for (int d = lane; d < D; d += 64) ((OT*)p.out)[(size_t)row * D + d] = O::narrow(0.0f);
+            for (int d = lane; d < D; d += 64) ((OT*)p.out)[orow * D + d] = O::narrow(0.0f);
     };
     if constexpr (MULTI) {
-        const int tok = row / p.Hq;
-        if (tok >= p.q_start[S]) return;        // past the batch's query tokens
-        int lo = 0, hi = S;                     // q_start[lo] <= tok < q_start[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (p.q_start[mid] <= tok) lo = mid;
-            else hi = mid;
-        }
-        s = lo;
+        const int maxq = p.S / S;               // p.S = num_seqs * max_query_len
+        s = row / (maxq * p.Hq);
+        const int j = (row / p.Hq) % maxq;
         const int QPG = 16 / G;
-        const int n = min(p.q_start[s + 1] - p.q_start[s], QPG);
-        const int j = tok - p.q_start[s];
-        if (j >= n) return;                     // not served by the balanced kernel
+        const int q0 = p.q_start[s];
+        const int n = min(p.q_start[s + 1] - q0, QPG);
+        if (j >= n) return;                     // no such query token
+        orow = (size_t)(q0 + j) * p.Hq + hq;
         col = j * G + hq % G;
         ncol = QPG * G;
         int L = p.lens[s];
@@ -215,7 +212,7 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
             const int slot = e == 0 ? slot0 : 0;
             return ((size_t)(c0 + e) * 2 + slot) * ncol + col;
         },
-        (size_t)row, wave, sub);
+        orow, wave, sub);
 }
 
 template <class O, int D, bool BAL>
