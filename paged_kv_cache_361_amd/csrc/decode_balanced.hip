@@ -8,7 +8,7 @@
 // the streams are laid end to end (sequence-major, then KV head) and the
 // resulting T tiles are cut into chunks by the guided schedule of
 // kernels.hpp: nW chunks of the first size, nW of the second, then small
-// ones.  The grid holds as many wavefronts as the GPU runs at once (nW);
+// ones.  The grid holds one wavefront per SIMD of the GPU (nW);
 // wave w works on chunk w, then takes chunks in order from a counter in the
 // workspace.  Waves of one GPU do not stream at one rate (on a loaded GPU
 // some take nearly twice as long as others over the same tiles), so the
