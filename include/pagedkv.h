@@ -180,9 +180,11 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          PKV_PARTITION_BALANCED; it also writes the zero rows of sequences
  *          with L <= 0.  The workspace needs no initialisation: its chunk
  *          counter carries the number of the call that last used it, and
- *          each call takes it over at its first request, whatever it held.
- *          Calls sharing one workspace must not overlap in time (use one
- *          stream).  Requires
+ *          each call takes it over at its first request, whatever it held;
+ *          the reduce returns it to zero, so a graph holding the decode and
+ *          its reduce replays correctly although the call number is frozen
+ *          in the graph.  Calls sharing one workspace must not overlap in
+ *          time (use one stream).  Requires
  *          num_seqs * num_kv_heads * ceil(max_seq_len / 16) < 2^31.
  *
  * pkv_decode_workspace_bytes gives the workspace size for either split mode.

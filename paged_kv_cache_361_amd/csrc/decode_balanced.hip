@@ -30,7 +30,9 @@
 // workspace for the reduce.  The chunk counter needs no reset before the
 // call (no memset, so the call can be captured in a graph): it carries the
 // number of the call that owns it, and the call's first request takes it
-// over (kernels.hpp).
+// over (kernels.hpp).  The reduce that follows returns it to zero, which is
+// what lets a replayed graph, whose call number never changes, take it over
+// again.
 //
 // Pipeline.  The matrix-core tile of tile_mfma.hpp runs on a ring of DEPTH
 // tile buffers.  Segments are cut into spans of at most 64 blocks (one

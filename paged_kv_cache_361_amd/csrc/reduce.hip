@@ -154,8 +154,15 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = wave % WPR;
     const int row = blockIdx.x * RPB + wave / WPR;
-    if (row >= p.S * p.Hq) return;
     const int32_t* hdr = p.ws_hdr;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        // The decode kernel is done with the chunk counter: return it to 0,
+        // below any call's base, so that the next call takes it over even
+        // when it carries the same call number (a replayed graph freezes
+        // the number in the kernel's arguments).
+        *(unsigned long long*)(const_cast<int32_t*>(hdr) + kHdrCounter) = 0ull;
+    }
+    if (row >= p.S * p.Hq) return;
     const int nW = hdr[kHdrNW];
     const int Hkv = hdr[kHdrHkv];
     const int G = hdr[kHdrG];

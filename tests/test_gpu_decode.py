@@ -527,3 +527,43 @@ def test_split_decode_replays_in_a_graph(P):
         d.decode("mfma", P, workspace=ws)      # eager calls between replays
         torch.cuda.synchronize()
         assert torch.equal(d.out.view(torch.uint8), eager.view(torch.uint8))
+
+
+def test_balanced_graph_replays_track_changing_inputs():
+    """Replays of a captured balanced decode + reduce, back to back with no
+    eager call between them and new queries before each, equal eager calls
+    on the same inputs bit for bit (the reduce hands the chunk counter back,
+    so a replay's frozen call number still takes it over)."""
+    c = small_gqa(seed=97, S=48)
+    d = DevCase(c)
+    d.write()
+    P = BAL
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
+    ws_eager = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, P)
+    out_eager = torch.empty_like(d.out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pkv.paged_attention_decode(d.out, d.query, d.k_cache, d.v_cache, d.tables, d.lens,
+                                       scale=c.scale, max_seq_len=c.max_seq_len,
+                                       partition_size=P, workspace=ws, algo="mfma", stream=s)
+            pkv.paged_attention_reduce(d.out, ws, d.lens, num_kv_heads=c.Hkv,
+                                       max_seq_len=c.max_seq_len, partition_size=P, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(98)
+    for step in range(5):
+        d.query.copy_(torch.randn(d.query.shape, generator=gen, device="cuda").to(d.query.dtype))
+        d.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pkv.paged_attention_decode(out_eager, d.query, d.k_cache, d.v_cache, d.tables, d.lens,
+                                   scale=c.scale, max_seq_len=c.max_seq_len, partition_size=P,
+                                   workspace=ws_eager, algo="mfma")
+        pkv.paged_attention_reduce(out_eager, ws_eager, d.lens, num_kv_heads=c.Hkv,
+                                   max_seq_len=c.max_seq_len, partition_size=P)
+        torch.cuda.synchronize()
+        assert torch.equal(d.out.view(torch.uint8), out_eager.view(torch.uint8)), step

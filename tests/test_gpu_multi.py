@@ -284,3 +284,40 @@ def test_balanced_spec_verify_workload_full():
     mc = workloads.spec_verify()
     out, _ = run_balanced(mc, calls=2)
     check(mc, out, oracle_multi(mc))
+
+
+def test_balanced_verify_graph_replays_track_changing_inputs():
+    """As for decode: back-to-back replays of a captured balanced
+    verification call with new queries each time equal eager calls."""
+    mc = ragged(40, 1, 4, 650, lmin=1, lmax=900)
+    c = mc.case
+    d = DevCase(c)
+    d.write()
+    q = to_dev(mc.query, c.q_dtype)
+    qs = torch.from_numpy(mc.query_start).cuda()
+    out = torch.empty_like(q)
+    out_eager = torch.empty_like(q)
+    ws = multi_workspace(mc, pkv.PARTITION_BALANCED)
+    ws_eager = multi_workspace(mc, pkv.PARTITION_BALANCED)
+    kw = dict(scale=c.scale, max_seq_len=c.max_seq_len, max_query_len=mc.max_query_len,
+              partition_size=pkv.PARTITION_BALANCED)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pkv.paged_attention_multi(out, q, d.k_cache, d.v_cache, d.tables, d.lens, qs,
+                                      workspace=ws, stream=s, **kw)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(651)
+    for step in range(5):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(q.dtype))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        pkv.paged_attention_multi(out_eager, q, d.k_cache, d.v_cache, d.tables, d.lens, qs,
+                                  workspace=ws_eager, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), out_eager.view(torch.uint8)), step
