@@ -217,7 +217,13 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     // long query runs without a split: 2 or 4 column blocks per wavefront
     const int nb = partition_size != 0 || max_query_len <= qpg ? 1
                    : (max_query_len >= 4 * qpg ? 4 : 2);
-    const int64_t groups = (max_query_len + (int64_t)qpg * nb - 1) / ((int64_t)qpg * nb);
+    // longer runs of 16-bit queries and caches: the LDS-staged kernel
+    const int ptok = prefill_tokens_per_group(G);
+    const bool staged = partition_size == 0 && 2 * max_query_len >= ptok &&
+                        prefill_supported(q_dtype, cache_dtype, head_dim, G);
+    const int64_t groups =
+        staged ? (max_query_len + (int64_t)ptok - 1) / ptok
+               : (max_query_len + (int64_t)qpg * nb - 1) / ((int64_t)qpg * nb);
     const int64_t cap = (int64_t)max_blocks_per_seq * block_size;
     const int len_cap = (int)(cap < max_seq_len ? cap : max_seq_len);
     MultiWs w;
@@ -308,6 +314,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         p.ws_o = (float*)((char*)workspace + w.off_o);
         p.ws_len = (int32_t*)((char*)workspace + w.off_len);
     }
+    if (staged) return launch_status(launch_prefill(q_dtype, cache_dtype, p, stream));
     hipError_t e = launch_multi_query(q_dtype, cache_dtype, p, stream);
     if (e != hipSuccess || partition_size == 0) return launch_status(e);
     // merge the partials of the rows (query token, query head)

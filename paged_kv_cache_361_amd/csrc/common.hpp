@@ -109,8 +109,35 @@ __device__ inline int group_sum_int(int x) {
 
 // Sum / max across lanes that differ only in bits >= log2(STRIDE): combines
 // the 64/STRIDE lanes {l, l+STRIDE, ...} that hold the same column.
+// Stride 16 uses the gfx950 lane-swap instructions instead of LDS
+// permutes: v_permlane16_swap / v_permlane32_swap of a value with itself
+// return, in one order or the other, this lane's value and that of lane
+// l ^ 16 (resp. l ^ 32), so the max or the two-term sum of the pair is the
+// exchange's result, bit for bit (IEEE addition is commutative).
+__device__ inline float swap_sum16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float swap_sum32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float swap_max16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap_max32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int STRIDE>
 __device__ inline float strided_sum(float x) {
+    if constexpr (STRIDE == 16) return swap_sum32(swap_sum16(x));
 #pragma unroll
     for (int o = STRIDE; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
     return x;
@@ -118,6 +145,7 @@ __device__ inline float strided_sum(float x) {
 
 template <int STRIDE>
 __device__ inline float strided_max(float x) {
+    if constexpr (STRIDE == 16) return swap_max32(swap_max16(x));
 #pragma unroll
     for (int o = STRIDE; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
     return x;

@@ -188,6 +188,12 @@ hipError_t launch_decode_mixed(int qdt, int cdt, const DecodeParams& p, hipStrea
 int decode_balanced_waves_per_cu(int qdt, int cdt, int D, int bs, int S);
 hipError_t launch_decode_balanced(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 hipError_t launch_multi_query(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
+// Long query runs without a split, K/V staged in LDS (prefill.hip): query
+// tokens per workgroup, the type combinations served, and the launch (one
+// workgroup per (sequence, KV head, max_groups group)).
+int prefill_tokens_per_group(int G);
+bool prefill_supported(int qdt, int cdt, int D, int G);
+hipError_t launch_prefill(int qdt, int cdt, const DecodeParams& p, hipStream_t st);
 hipError_t launch_reduce(int out_dt, const ReduceParams& p, hipStream_t st);
 hipError_t launch_reduce_balanced(int out_dt, const ReduceParams& p, hipStream_t st);
 

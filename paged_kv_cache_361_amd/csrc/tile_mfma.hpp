@@ -327,11 +327,13 @@ struct TileMath {
         }
 
         // ---- online softmax: tile max over the 16 tokens of each head ----
+        // exp2 is the bare v_exp_f32 (results under 2^-126 flush to zero, a
+        // weight far below what the sum can register); alpha is 0 at first.
         float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
         mx = strided_max<16>(mx);
         const float m_new = mx > a.m + kTau ? mx : a.m;
         if (__any(m_new != a.m)) {
-            const float alpha = m_new == a.m ? 1.0f : exp2f(a.m - m_new);  // 0 at first
+            const float alpha = m_new == a.m ? 1.0f : __builtin_amdgcn_exp2f(a.m - m_new);
             a.l *= alpha;
             // accumulator rows are heads 4*g4 + r; their alpha lives in lane 4*g4 + r
 #pragma unroll
@@ -345,7 +347,7 @@ struct TileMath {
         float pz[4];
 #pragma unroll
         for (int r = 0; r < 4; r++)
-            pz[r] = (CAUSAL && z[r] == -INFINITY) ? 0.0f : exp2f(z[r] - a.m);
+            pz[r] = (CAUSAL && z[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[r] - a.m);
         a.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
 
         // ---- weights as the A operand, value rows as the B operand ----

@@ -321,3 +321,28 @@ def test_balanced_verify_graph_replays_track_changing_inputs():
                                   workspace=ws_eager, **kw)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.uint8), out_eager.view(torch.uint8)), step
+
+
+# ---- long query runs through the LDS-staged kernel ------------------------------
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_prefill_block_sizes(bs):
+    """Chunks of 30..90 tokens over 8- and 32-token blocks (16-bit caches go
+    through the LDS-staged kernel)."""
+    mc = ragged(10, 30, 90, 660 + bs, bs=bs, lmin=90, lmax=700)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_prefill_tokens_before_the_sequence():
+    """Chunks longer than the sequence: the leading query tokens see nothing
+    and get zero rows; stages past the context load zeros."""
+    mc = ragged(12, 40, 100, 670, lmin=1, lmax=60)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
+def test_prefill_f16_head_dim_64():
+    mc = ragged(8, 20, 80, 680, dtype="f16", cache="f16", D=64, Hq=8, Hkv=4, lmin=50, lmax=500)
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
