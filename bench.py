@@ -17,6 +17,8 @@ Prints ONE JSON line on stdout; progress goes to stderr.
           runs on, against the MI355X HBM peak of 8 TB/s
   cpu_baseline  the CPU oracle on this host, on a bounded sample of the same
           workload
+  max_abs_err_vs_oracle  the oracle's sampled rows against the device output
+          of the last step, with the tolerance of the cache type
 """
 from __future__ import annotations
 
@@ -196,20 +198,50 @@ def record_traffic(args) -> int:
     return 0
 
 
-def cpu_baseline(c, budget_s: float = 20.0) -> dict:
+def unique_kv_bytes(c) -> int:
+    """K+V bytes of the distinct pool slots the tables reach: where sequences
+    share prefix blocks, the bytes one launch could fetch from HBM at least."""
+    L = c.seq_lens.astype(np.int64)
+    slots = [c.block_tables[s, np.arange(L[s]) // c.bs].astype(np.int64) * c.bs
+             + np.arange(L[s]) % c.bs for s in range(c.S) if L[s] > 0]
+    n = np.unique(np.concatenate(slots)).size if slots else 0
+    return int(n) * c.Hkv * c.D * E[c.cache_dtype] * 2
+
+
+def host_append(c) -> None:
+    """The step's cache writes, applied to the host pool by the oracle, so
+    that the oracle sees what the device pool holds after a step."""
+    import oracle
+    if c.slot_mapping.size:
+        oracle.reshape_and_cache(c.new_key, c.new_value, c.k_cache, c.v_cache, c.slot_mapping,
+                                 src_dtype=c.src_dtype, cache_dtype=c.cache_dtype,
+                                 k_scale=c.k_scale, v_scale=c.v_scale)
+
+
+# Output tolerance against the oracle: 5e-3 for 16-bit (and fp32) caches,
+# 3e-2 for fp8 caches (the oracle dequantises the same codes).
+TOL = {"f32": 5e-3, "f16": 5e-3, "bf16": 5e-3, "fp8": 3e-2}
+
+
+def cpu_baseline(c, gpu_out=None, budget_s: float = 20.0):
     """The CPU oracle (as it stands) on the first sequences of the workload:
-    a probe on a few sequences sizes a sample of about `budget_s`."""
+    a probe on a few sequences sizes a sample of about `budget_s`.  With
+    `gpu_out` (the device output as float64 [S, Hq, D]) the sampled rows are
+    also compared with it; returns (baseline, comparison or None)."""
     import oracle
     threads = oracle.max_threads()
     kw = dict(q_dtype=c.q_dtype, cache_dtype=c.cache_dtype, scale=c.scale,
               k_scale=c.k_scale, v_scale=c.v_scale, threads=threads)
+    last = {}
 
     def run(n):
         sub_rows = np.arange(n * c.Hq, dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
-                            rows=sub_rows, **kw)
-        return time.perf_counter() - t0
+        r = oracle.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                                rows=sub_rows, **kw)
+        t = time.perf_counter() - t0
+        last["n"], last["ref"] = n, r
+        return t
 
     n = min(8, c.S)
     t = run(n)
@@ -230,13 +262,22 @@ def cpu_baseline(c, budget_s: float = 20.0) -> dict:
     sub.seq_lens = c.seq_lens[:n]
     sub.slot_mapping = c.slot_mapping[:0]
     nbytes = decode_bytes(sub, 0)["decode_kernel"]
-    return {"value": round(nbytes / t / 1e12, 6), "unit": "TB/s", "cores": threads,
+    base = {"value": round(nbytes / t / 1e12, 6), "unit": "TB/s", "cores": threads,
             "kind": "oracle",
             "tokens_per_s_per_layer": round(n / t, 2),
             "seconds": round(t, 3),
             "sample": "decode of the first %d of %d sequences (%d tokens, all %d query "
                       "heads), gather + fp64 softmax attention, OpenMP over rows; mean "
                       "of %d run(s)" % (n, c.S, tok, c.Hq, reps)}
+    cmp = None
+    if gpu_out is not None:
+        m = last["n"]
+        err = float(np.max(np.abs(gpu_out[:m] - last["ref"][:m]))) if m else 0.0
+        tol = TOL[c.cache_dtype]
+        cmp = {"max_abs_err": err, "tol": tol, "within_tol": bool(err <= tol),
+               "rows": m * c.Hq, "of_rows": c.S * c.Hq,
+               "sample": "the oracle's rows above against the output of the last step"}
+    return base, cmp
 
 
 # Split used when --partition is not given: the fastest measured on MI355X
@@ -385,9 +426,10 @@ def bench_multi(args) -> int:
         while True:               # query tokens of the first sequence(s), about 10-20 s
             rows = np.arange(n * c.Hq, dtype=np.int32)
             t = time.perf_counter()
-            oracle.paged_multi(mc.query, kc, vc, c.block_tables, c.seq_lens, mc.query_start,
-                               q_dtype=c.q_dtype, cache_dtype=c.cache_dtype, scale=c.scale,
-                               rows=rows, threads=threads)
+            ref = oracle.paged_multi(mc.query, kc, vc, c.block_tables, c.seq_lens,
+                                     mc.query_start, q_dtype=c.q_dtype,
+                                     cache_dtype=c.cache_dtype, scale=c.scale, rows=rows,
+                                     threads=threads)
             t = time.perf_counter() - t
             if t > 5.0 or n >= total_q:
                 break
@@ -397,6 +439,13 @@ def bench_multi(args) -> int:
             "kind": "oracle", "seconds": round(t, 3),
             "sample": "the first %d of %d query tokens, all %d query heads, gather + fp64 "
                       "softmax attention, OpenMP over rows" % (n, total_q, c.Hq)}
+        gpu = out[:n].float().cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(gpu - ref[:n])))
+        tol = TOL[c.cache_dtype]
+        res["max_abs_err_vs_oracle"] = {
+            "max_abs_err": err, "tol": tol, "within_tol": bool(err <= tol),
+            "rows": n * c.Hq, "of_rows": total_q * c.Hq,
+            "sample": "the oracle's rows above against the output of the last call"}
     print(json.dumps(res), flush=True)
     return 0
 
@@ -757,9 +806,16 @@ def main() -> int:
                      "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": traffic},
     }
+    kv_u = unique_kv_bytes(c)
+    if kv_u != nb["kv"]:
+        # shared prefix blocks: a launch need fetch each distinct slot once
+        res["kv_unique_bytes"] = kv_u
+        res["decode_TBps_on_unique_kv"] = round(kv_u / dec_s / 1e12, 4)
     if args.cpu_baseline == "on":
         log("timing the CPU oracle ...")
-        res["cpu_baseline"] = cpu_baseline(c)
+        host_append(c)
+        gpu = out.float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"], res["max_abs_err_vs_oracle"] = cpu_baseline(c, gpu)
     print(json.dumps(res), flush=True)
     return 0
 
