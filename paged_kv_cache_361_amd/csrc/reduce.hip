@@ -13,105 +13,144 @@
 //                     1 of chunk c0 + e (see decode_balanced.hip), found from
 //                     the tile prefix and the header the decode call wrote.
 //
-// Work layout.  A row is served by WPR wavefronts (WPR = 1 for short rows, 4
-// when rows have many entries).  Lane (kg = lane / 16, c = lane % 16) of wave
-// `sub` owns output columns [c*CW, c*CW + CW) and the entries e = j, j + 4*WPR,
-// j + 8*WPR, ... with slot j = 4*sub + kg; each entry's CW columns are one
-// contiguous load, and the loads of four entries are issued together, the
-// first four before M is known.  M and the denominator are computed by every
-// wave from the m and l values (tiny); the per-slot sums meet through lane
-// shuffles and, for WPR = 4, through LDS.
+// Work layout.  A row is served by WPR wavefronts (WPR = 1 for short rows,
+// 4 or 8 when rows have many entries; with WPR > 1 a workgroup is one row).
+// Lane (kg = lane / 16, c = lane % 16) of wave `sub` owns output columns
+// [c*CW, c*CW + CW) of the entries e = j, j + 4*WPR, j + 8*WPR, ... with
+// slot j = 4*sub + kg.  A slot keeps a running reference max, sum and output
+// over its entries (the online-softmax update of the decode, once per entry),
+// loading batch(WPR) entries per round with all their loads issued together,
+// so a row of n entries takes ceil(n / (4 * WPR * batch(WPR))) rounds of
+// memory latency.  The slots then meet at the row's max: lane shuffles within a
+// wave, LDS across waves.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace pkv {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kUnroll = 4;
+constexpr int kWaves = 4;      // waves per workgroup of one-wave rows
 
-// Merges n >= 2 entries into one output row.  idx(e) maps entry e to its
-// index in the m/l arrays (o rows at idx * D).
+// Entries per slot loaded per round: 3 for one-wave rows (a row of up to 12
+// entries in one round; four would not fit the register budget below
+// without spilling), 8 for rows served by several waves (long rows).
+constexpr int batch(int WPR) { return WPR > 1 ? 8 : 3; }
+
+// Waves per SIMD each kernel is compiled to fit (a register budget): eight
+// for one-wave rows, so that a batch of 8192 rows (2048 workgroups of four
+// waves) is resident at once on 256 CUs; four for the wide rows (two
+// workgroups of eight waves per CU: 512 long rows at once).
+constexpr int waves_per_simd(int WPR) { return WPR > 1 ? 4 : 8; }
+
+// Waves per workgroup of a kernel serving rows with WPR waves each.
+constexpr int wg_waves(int WPR) { return WPR > 1 ? WPR : kWaves; }
+
+// Merges n >= 1 entries into one output row.  idx(e) maps entry e to its
+// index in the m/l arrays (o rows at idx * D).  A row whose entries hold no
+// weight (every m = -inf) is written as zeros.
 template <class O, int D, int WPR, class Idx>
-__device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t row,
-                                 int wave, int sub) {
+__device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t row, int sub) {
     constexpr int CW = D / 16;                 // columns per lane
     constexpr int SLOTS = 4 * WPR;             // entry slots per row
+    constexpr int NP = WPR > 1 ? WPR : 1;
+    constexpr int kBatch = batch(WPR);
     typedef float colv __attribute__((ext_vector_type(CW)));
-    __shared__ colv part_sum[WPR > 1 ? kWaves : 1][16];
+    __shared__ colv part_sum[NP][16];
+    __shared__ float part_m[NP], part_l[NP];
 
     const int lane = threadIdx.x & 63;
     const int kg = lane >> 4;
     const int c = lane & 15;
     const int j = 4 * sub + kg;
 
-    // Everything a short row needs is requested before anything waits: the
-    // first 64 (m, l) pairs and the first round of this lane's partial
-    // outputs (which do not depend on M).  Out-of-range slots read entry 0
-    // and get weight 0.
-    const size_t i0 = lane < n ? idx(lane) : 0;
-    const float m0 = lane < n ? p.ws_m[i0] : -INFINITY;
-    const float l0 = lane < n ? p.ws_l[i0] : 0.0f;
-    colv o[kUnroll];
-    float mo[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; u++) {
-        const int e = j + u * SLOTS;
-        const size_t ie = idx(e < n ? e : 0);
-        o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
-        mo[u] = p.ws_m[ie];
-    }
-
-    // M and the denominator over all entries (lanes stride by 64).
-    float M = m0;
-    for (int e = lane + 64; e < n; e += 64) M = fmaxf(M, p.ws_m[idx(e)]);
-    M = group_max<64>(M);
-    const float Ml = M * kLog2e;
-    float den = lane < n ? exp2f(fmaf(m0, kLog2e, -Ml)) * l0 : 0.0f;
-    for (int e = lane + 64; e < n; e += 64) {
-        const size_t ie = idx(e);
-        den += exp2f(fmaf(p.ws_m[ie], kLog2e, -Ml)) * p.ws_l[ie];
-    }
-    den = group_sum<64>(den);
-
-    // Weighted sum of this lane's slot over its columns, kUnroll entries per
-    // round.
+    // Running state of this lane's slot: reference max (log2 units), the sum
+    // of the entries' l and the output columns, both scaled to it.
+    float m_run = -INFINITY, l_run = 0.0f;
     colv acc = colv{};
-    for (int e0 = j; e0 < n; e0 += SLOTS * kUnroll) {
-        if (e0 != j) {
+    for (int e0 = j; e0 < n; e0 += SLOTS * kBatch) {
+        colv o[kBatch];
+        float m[kBatch], l[kBatch];
 #pragma unroll
-            for (int u = 0; u < kUnroll; u++) {
-                const int e = e0 + u * SLOTS;
+        for (int u = 0; u < kBatch; u++) {     // the round's loads, all at once
+            const int e = e0 + u * SLOTS;
+            if constexpr (WPR > 1) {
+                // long rows: entries past n get no weight and issue no loads
+                o[u] = colv{};
+                m[u] = -INFINITY;
+                l[u] = 0.0f;
+                if (e < n) {
+                    const size_t ie = idx(e);
+                    o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+                    m[u] = p.ws_m[ie];
+                    l[u] = p.ws_l[ie];
+                }
+            } else {
+                // short rows: straight-line loads (entries past n reread entry
+                // 0, a cache hit, and get no weight), cheaper than branching
+                // around each of a few loads
                 const size_t ie = idx(e < n ? e : 0);
                 o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
-                mo[u] = p.ws_m[ie];
+                m[u] = p.ws_m[ie];
+                l[u] = p.ws_l[ie];
+                if (e >= n) m[u] = -INFINITY;
             }
         }
+        // Keep every load of the round ahead of the arithmetic: otherwise the
+        // scheduler issues the o loads only once the m values are back, which
+        // costs a second memory round trip per round.
+        __builtin_amdgcn_sched_barrier(0);
+        float bm = m_run;
 #pragma unroll
-        for (int u = 0; u < kUnroll; u++) {
-            const int e = e0 + u * SLOTS;
-            const float w = e < n ? exp2f(fmaf(mo[u], kLog2e, -Ml)) : 0.0f;
+        for (int u = 0; u < kBatch; u++) {
+            m[u] *= kLog2e;
+            bm = fmaxf(bm, m[u]);
+        }
+        const float ref = bm == -INFINITY ? 0.0f : bm;
+        const float f = exp2f(m_run - ref);
+        l_run *= f;
+#pragma unroll
+        for (int q = 0; q < CW; q++) acc[q] *= f;
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const float w = exp2f(m[u] - ref);
+            l_run = fmaf(w, l[u], l_run);
 #pragma unroll
             for (int q = 0; q < CW; q++) acc[q] = fmaf(w, o[u][q], acc[q]);
         }
+        m_run = bm;
     }
-    // Combine the four slots of this wave (lanes c, c+16, c+32, c+48).
-#pragma unroll
-    for (int q = 0; q < CW; q++) acc[q] = strided_sum<16>(acc[q]);
+
+    // The row's max over all slots, then every slot rescaled to it and summed:
+    // the four slots of a wave (lanes c, c+16, c+32, c+48) by lane shuffles,
+    // the waves of a row through LDS.
+    float M = group_max<64>(m_run);
     if constexpr (WPR > 1) {
-        if (kg == 0) part_sum[wave][c] = acc;
+        if (lane == 0) part_m[sub] = M;
         __syncthreads();
-        if (wave != 0 || kg != 0) return;
+        M = part_m[0];
+#pragma unroll
+        for (int w = 1; w < WPR; w++) M = fmaxf(M, part_m[w]);
+    }
+    const float f = exp2f(m_run - (M == -INFINITY ? 0.0f : M));
+    float den = strided_sum<16>(l_run * f);
+#pragma unroll
+    for (int q = 0; q < CW; q++) acc[q] = strided_sum<16>(acc[q] * f);
+    if constexpr (WPR > 1) {
+        if (kg == 0) part_sum[sub][c] = acc;
+        if (lane == 0) part_l[sub] = den;
+        __syncthreads();
+        if (sub != 0 || kg != 0) return;
 #pragma unroll
         for (int w = 1; w < WPR; w++) {
             const colv x = part_sum[w][c];
 #pragma unroll
             for (int q = 0; q < CW; q++) acc[q] += x[q];
+            den += part_l[w];
         }
     } else {
         if (kg != 0) return;
     }
-    const float inv = 1.0f / den;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     typedef typename O::T OT;
     typedef OT ovec __attribute__((ext_vector_type(CW)));
     ovec r;
@@ -123,8 +162,9 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
 // ---- fixed partitions -------------------------------------------------------
 
 template <class O, int D, int WPR>
-__global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
-    constexpr int RPB = kWaves / WPR;          // rows per workgroup
+__global__ __launch_bounds__(64 * wg_waves(WPR)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(WPR))))
+void reduce_kernel(ReduceParams p) {
+    constexpr int RPB = wg_waves(WPR) / WPR;   // rows per workgroup
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = wave % WPR;
     const int row = blockIdx.x * RPB + wave / WPR;   // s * Hq + hq
@@ -136,8 +176,7 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
     const int nparts = L > 0 ? (L + p.P - 1) / p.P : 0;
     if (nparts <= 1) return;
     const size_t base = (size_t)row * p.P_max;
-    merge_row<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, wave,
-                         sub);
+    merge_row<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, sub);
 }
 
 // ---- balanced split ---------------------------------------------------------
@@ -148,8 +187,9 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_kernel(ReduceParams p) {
 // in its stream is j * G + head % G, and a token placed before its sequence
 // (its column saw nothing) gets a zero row.
 template <class O, int D, int WPR, bool MULTI>
-__global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReduceParams p) {
-    constexpr int RPB = kWaves / WPR;
+__global__ __launch_bounds__(64 * wg_waves(WPR)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(WPR))))
+void reduce_balanced_kernel(ReduceParams p) {
+    constexpr int RPB = wg_waves(WPR) / WPR;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = wave % WPR;
@@ -163,20 +203,38 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
         *(unsigned long long*)(const_cast<int32_t*>(hdr) + kHdrCounter) = 0ull;
     }
     if (row >= p.S * p.Hq) return;
+    const int S = MULTI ? p.S_seq : p.S;
+    const int maxq = MULTI ? p.S / S : 1;       // MULTI: p.S = num_seqs * max_query_len
+    const int s = row / (maxq * p.Hq);
+    const int j = MULTI ? (row / p.Hq) % maxq : 0;
+    // Every word the row needs, requested together before any of them is
+    // looked at (one memory round trip): the header, the prefix total, the
+    // sequence's prefix entries and, for MULTI, its query range and length.
+    // All of them lie inside the workspace and the arrays the call passed.
+    const int magic = hdr[kHdrMagic];
     const int nW = hdr[kHdrNW];
     const int Hkv = hdr[kHdrHkv];
     const int G = hdr[kHdrG];
     const int T = hdr[kHdrT];
-    const int S = MULTI ? p.S_seq : p.S;
-    // A workspace not written by a balanced call of this shape: write
-    // nothing rather than follow its indices.
-    if (hdr[kHdrMagic] != kBalancedMagic || nW < 1 || nW > kBalancedMaxWaves || G < 1 ||
-        Hkv != p.Hkv || Hkv * G != p.Hq || T < 0 || p.ws_pre[S] != T)
-        return;
+    const int preS = p.ws_pre[S];
+    const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
+    const int q0 = MULTI ? p.q_start[s] : 0;
+    const int q1 = MULTI ? p.q_start[s + 1] : 0;
+    const int Lraw = MULTI ? p.lens[s] : 0;
+    __builtin_amdgcn_sched_barrier(0);          // all of them issued before any wait
+    // A workspace not written by a balanced call of this shape (or inputs
+    // breaking the call's contract): write nothing rather than follow its
+    // indices.  One condition of every word, combined without short cuts, so
+    // that no load is deferred behind a test of another.
+    const bool bad = (magic != kBalancedMagic) | (nW < 1) | (nW > kBalancedMaxWaves) |
+                     (G < 1) | (Hkv != p.Hkv) | (Hkv * G != p.Hq) | (T < 0) | (preS != T) |
+                     (p0 < 0) | (p1 < p0) | (p1 > T) | ((p1 - p0) % max(Hkv, 1) != 0) |
+                     (MULTI & ((q1 < q0) | (Lraw < 0)));
+    if (bad) return;
     const Sched q = make_sched(T, nW);
     const int hq = row % p.Hq;
     const int h = hq / G;
-    int s = row / p.Hq, col = hq % G, ncol = G;
+    int col = hq % G, ncol = G;
     size_t orow = (size_t)row;                  // output row
     typedef typename O::T OT;
     auto zero_row = [&]() {
@@ -184,25 +242,18 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
             for (int d = lane; d < D; d += 64) ((OT*)p.out)[orow * D + d] = O::narrow(0.0f);
     };
     if constexpr (MULTI) {
-        const int maxq = p.S / S;               // p.S = num_seqs * max_query_len
-        s = row / (maxq * p.Hq);
-        const int j = (row / p.Hq) % maxq;
         const int QPG = 16 / G;
-        const int q0 = p.q_start[s];
-        const int n = min(p.q_start[s + 1] - q0, QPG);
+        const int n = min(q1 - q0, QPG);
         if (j >= n) return;                     // no such query token
         orow = (size_t)(q0 + j) * p.Hq + hq;
         col = j * G + hq % G;
         ncol = QPG * G;
-        int L = p.lens[s];
-        L = L < p.len_cap ? L : p.len_cap;
+        const int L = Lraw < p.len_cap ? Lraw : p.len_cap;
         if (L - n + j < 0) {                    // its column saw no token
             zero_row();
             return;
         }
     }
-    const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
-    if (p0 < 0 || p1 < p0 || p1 > T || (p1 - p0) % Hkv != 0) return;
     const int nt = (p1 - p0) / Hkv;
     if (nt == 0) {                              // no tokens: a zero row
         zero_row();
@@ -219,40 +270,40 @@ __global__ __launch_bounds__(64 * kWaves) void reduce_balanced_kernel(ReducePara
             const int slot = e == 0 ? slot0 : 0;
             return ((size_t)(c0 + e) * 2 + slot) * ncol + col;
         },
-        orow, wave, sub);
+        orow, sub);
+}
+
+template <class O, int D, int WPR, bool BAL>
+hipError_t launch_r(const ReduceParams& p, hipStream_t st) {
+    const long rows = (long)p.S * p.Hq;
+    constexpr int RPB = wg_waves(WPR) / WPR;
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(64 * wg_waves(WPR));
+    if (BAL && p.q_start)
+        return launch_kernel(reduce_balanced_kernel<O, D, WPR, true>, grid, block, st, p);
+    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, WPR, false>, grid, block, st, p);
+    return launch_kernel(reduce_kernel<O, D, WPR>, grid, block, st, p);
 }
 
 template <class O, int D, bool BAL>
-hipError_t launch_w(const ReduceParams& p, bool wide, hipStream_t st) {
-    const long rows = (long)p.S * p.Hq;
-    const dim3 block(64 * kWaves);
-    if (wide) {
-        const dim3 grid((unsigned)rows);
-        if (BAL && p.q_start)
-            return launch_kernel(reduce_balanced_kernel<O, D, 4, true>, grid, block, st, p);
-        if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 4, false>, grid, block, st, p);
-        return launch_kernel(reduce_kernel<O, D, 4>, grid, block, st, p);
-    }
-    const dim3 grid((unsigned)((rows + kWaves - 1) / kWaves));
-    if (BAL && p.q_start)
-        return launch_kernel(reduce_balanced_kernel<O, D, 1, true>, grid, block, st, p);
-    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, 1, false>, grid, block, st, p);
-    return launch_kernel(reduce_kernel<O, D, 1>, grid, block, st, p);
+hipError_t launch_w(const ReduceParams& p, int wpr, hipStream_t st) {
+    if (wpr >= 8) return launch_r<O, D, 8, BAL>(p, st);
+    if (wpr >= 4) return launch_r<O, D, 4, BAL>(p, st);
+    return launch_r<O, D, 1, BAL>(p, st);
 }
 
 template <class O, bool BAL>
-hipError_t launch_d(const ReduceParams& p, bool wide, hipStream_t st) {
-    if (p.D == 64) return launch_w<O, 64, BAL>(p, wide, st);
-    if (p.D == 128) return launch_w<O, 128, BAL>(p, wide, st);
+hipError_t launch_d(const ReduceParams& p, int wpr, hipStream_t st) {
+    if (p.D == 64) return launch_w<O, 64, BAL>(p, wpr, st);
+    if (p.D == 128) return launch_w<O, 128, BAL>(p, wpr, st);
     return hipErrorInvalidValue;
 }
 
 template <bool BAL>
-hipError_t launch_o(int out_dt, const ReduceParams& p, bool wide, hipStream_t st) {
+hipError_t launch_o(int out_dt, const ReduceParams& p, int wpr, hipStream_t st) {
     switch (out_dt) {
-    case kF32: return launch_d<F32, BAL>(p, wide, st);
-    case kF16: return launch_d<F16, BAL>(p, wide, st);
-    case kBF16: return launch_d<BF16, BAL>(p, wide, st);
+    case kF32: return launch_d<F32, BAL>(p, wpr, st);
+    case kF16: return launch_d<F16, BAL>(p, wpr, st);
+    case kBF16: return launch_d<BF16, BAL>(p, wpr, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -260,13 +311,14 @@ hipError_t launch_o(int out_dt, const ReduceParams& p, bool wide, hipStream_t st
 }  // namespace
 
 hipError_t launch_reduce(int out_dt, const ReduceParams& p, hipStream_t st) {
-    return launch_o<false>(out_dt, p, p.P_max > 32, st);
+    // waves per row by the most partitions a row can have
+    return launch_o<false>(out_dt, p, p.P_max > 128 ? 8 : (p.P_max > 32 ? 4 : 1), st);
 }
 
 hipError_t launch_reduce_balanced(int out_dt, const ReduceParams& p, hipStream_t st) {
-    // Few rows (long contexts, each row split over many waves): four waves
-    // per row.
-    return launch_o<true>(out_dt, p, (long)p.S * p.Hq <= 2048, st);
+    // Few rows (long contexts, each row split over many chunks): eight
+    // waves per row.
+    return launch_o<true>(out_dt, p, (long)p.S * p.Hq <= 2048 ? 8 : 1, st);
 }
 
 }  // namespace pkv
