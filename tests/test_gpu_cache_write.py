@@ -1,8 +1,9 @@
 """reshape_and_cache on the GPU against the oracle writer: bit-exact.
 
 Covers the same-type bit copy for every cache type, the E4M3 quantiser over
-every bf16 and f16 bit pattern at three scales, skipped slots (negative, past
-the pool) and bytes outside the written slots (canary)."""
+every bf16 and f16 bit pattern at three scales and over f32 quotients close to
+every rounding point, skipped slots (negative, past the pool) and bytes
+outside the written slots (canary)."""
 import numpy as np
 import pytest
 import torch
@@ -75,6 +76,30 @@ def test_fp8_quantiser_f32_sample():
     kc0 = np.zeros((T, 1, Hkv, D), np.uint8)
     vc0 = np.zeros((T, 1, Hkv, D), np.uint8)
     kg, vg, ko, vo = _run_both(x, y, "f32", "fp8", kc0, vc0, slots, 0.37, 1.0)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+@pytest.mark.parametrize("scale", [0.37, 0.0103, 3.7])
+def test_fp8_quantiser_near_halfway_points(scale):
+    """f32 sources whose quotient x / scale sweeps +-20 ulps around every
+    halfway point between adjacent normal E4M3 magnitudes (and around the
+    2^-6 edge of the subnormal codes): the writer divides exactly only near
+    those points, and its bytes must match the oracle's IEEE divide."""
+    vals = oracle.e4m3_decode(np.arange(0x08, 0x7F, dtype=np.uint8))   # 2^-6 .. 448
+    mids = np.concatenate([(vals[:-1] + vals[1:]) / 2, [vals[0]]])
+    base = (mids * scale).astype(np.float32)
+    steps = np.arange(-20, 21, dtype=np.int64)
+    bits = base.view(np.int32).astype(np.int64)[:, None] + steps[None, :]
+    x = bits.astype(np.int32).view(np.float32).ravel()
+    x = np.concatenate([x, -x])
+    Hkv, D = 2, 64
+    T = -(-x.size // (Hkv * D))
+    x = np.resize(x, T * Hkv * D).reshape(T, Hkv, D)
+    y = np.ascontiguousarray(x[::-1])
+    slots = np.arange(T, dtype=np.int64)
+    kc0 = np.zeros((T, 1, Hkv, D), np.uint8)
+    vc0 = np.zeros((T, 1, Hkv, D), np.uint8)
+    kg, vg, ko, vo = _run_both(x, y, "f32", "fp8", kc0, vc0, slots, scale, scale)
     assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
 
 
