@@ -107,7 +107,24 @@ def decode_bytes(c, P: int, nW: int = 0) -> dict:
 
 
 # Source file each profiled kernel is compiled from.
-KERNEL_SOURCE = {"decode_balanced_kernel": "decode_balanced.hip"}
+KERNEL_SOURCE = {"decode_balanced_kernel": "decode_balanced.hip",
+                 "decode_mfma_kernel": "decode_mfma.hip"}
+
+
+def decode_kernel_name(P: int) -> str:
+    """The kernel a decode call of split P runs for 16-bit and fp8 caches."""
+    return "decode_balanced_kernel" if P < 0 else "decode_mfma_kernel"
+
+
+def traffic_key(args, bs: int) -> str:
+    """Name of a workload's counter record: the workload, the block size of
+    the shared-prefix workload, and the partition size when one is forced."""
+    key = args.workload
+    if args.workload == "shared-prefix-fp8":
+        key += "-bs%d" % bs
+    if args.partition is not None:
+        key += "-P%d" % args.partition
+    return key
 
 
 def kernel_sources(top: str) -> list:
@@ -148,43 +165,49 @@ def traffic_from_profiles(workload: str, launch_bytes: float):
         rec = json.load(open(path)).get(workload)
     except (ValueError, AttributeError):
         return None
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    if not rec or rec.get("kernel") not in KERNEL_SOURCE:
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash(rec["kernel"]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
 def _counter_means(path: str, kernel: str):
-    """Mean counter value (KiB) per dispatch of `kernel`, and the largest
-    value read for a device copy (the calibration copy)."""
+    """Mean counter value (KiB) per dispatch of `kernel`, and the value read
+    for the calibration copy: the last device copy dispatched before the
+    kernel's first dispatch (bench.py makes it after the pools' uploads and
+    copies, which can be larger)."""
     import csv
-    vals, copies = [], []
-    with open(path) as f:
-        for row in csv.DictReader(f):
-            name, v = row["Kernel_Name"], float(row["Counter_Value"])
-            if kernel + "<" in name:
-                vals.append(v)
-            elif "copyBuffer" in name:
-                copies.append(v)
-    if not vals or not copies:
-        raise SystemExit("%s: no %s or copy dispatches" % (path, kernel))
-    return sum(vals) / len(vals), max(copies), len(vals)
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    vals, calib = [], None
+    for row in rows:
+        name, v = row["Kernel_Name"], float(row["Counter_Value"])
+        if kernel + "<" in name:
+            vals.append(v)
+        elif "copyBuffer" in name and not vals:
+            calib = v
+    if not vals or calib is None:
+        raise SystemExit("%s: no %s dispatch, or no copy before it" % (path, kernel))
+    return sum(vals) / len(vals), calib, len(vals)
 
 
 def record_traffic(args) -> int:
-    """Writes HBM bytes per launch of the balanced decode kernel from two
-    counter runs.  Each counter is scaled by what it reads for the plain
-    device copy of --copy-calib-mib MiB (that many bytes fetched and
-    written)."""
+    """Writes HBM bytes per launch of the workload's decode kernel (balanced
+    or fixed partitions, as the run used) from two counter runs.  Each
+    counter is scaled by what it reads for the plain device copy of
+    --copy-calib-mib MiB (that many bytes fetched and written)."""
     if not args.copy_calib_mib:
         raise SystemExit("--record-traffic needs the --copy-calib-mib the runs used")
-    kernel = "decode_balanced_kernel"
+    P = DEFAULT_PARTITION[args.workload] if args.partition is None else args.partition
+    kernel = decode_kernel_name(P)
     known_kib = args.copy_calib_mib * 1024.0
     fetch, fcopy, n = _counter_means(args.record_traffic[0], kernel)
     write, wcopy, _ = _counter_means(args.record_traffic[1], kernel)
     fs, wsc = known_kib / fcopy, known_kib / wcopy
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
-    data[args.workload] = {
+    key = traffic_key(args, args.bs)
+    data[key] = {
         "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
         "hbm_bytes_per_launch": int(round((fetch * fs + write * wsc) * 1024)),
         "fetch_size_kib": round(fetch, 1), "fetch_scale": round(fs, 4),
@@ -194,7 +217,7 @@ def record_traffic(args) -> int:
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
-    print(json.dumps(data[args.workload]))
+    print(json.dumps(data[key]))
     return 0
 
 
@@ -763,13 +786,9 @@ def main() -> int:
     value = nb["step"] / step_s / 1e12
     achieved = nb["decode_kernel"] / dec_s / 1e9
     wl = WORKLOAD_NAMES[args.workload]
-    key = args.workload
     if args.workload == "shared-prefix-fp8":
         wl += ", bs %d" % c.bs
-        key += "-bs%d" % c.bs
-    if args.partition is not None:
-        key += "-P%d" % P
-    traffic = traffic_from_profiles(key, nb["decode_kernel"])
+    traffic = traffic_from_profiles(traffic_key(args, c.bs), nb["decode_kernel"])
     res = {
         "metric": METRIC,
         "value": round(value, 4),
