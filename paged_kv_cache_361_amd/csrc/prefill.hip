@@ -11,15 +11,20 @@
 //     multi_query.hip does;
 //   - the context the workgroup's last token sees is walked in stages of
 //     kStageTok tokens: all threads load a stage's K and V rows (through
-//     the block table, rows past the context read as zeros) into one of two
-//     LDS buffers, one barrier per stage, and every wave reads its 16-token
+//     the block table, with buffer loads; rows past the context read as
+//     zeros) into one of two LDS buffers, one barrier per stage, and every
+//     wave reads its 16-token
 //     tiles from LDS in the lane layout of tile_mfma.hpp and runs the same
 //     causal tile step;
 //   - the next stage's rows are loaded into registers while the current one
 //     is computed, and written to the other buffer after it.
 // So a 512-token chunk reads its context from memory once per kTok query
 // tokens instead of once per wave, and the waves hold no ring of tiles in
-// flight: at two column blocks per wave two waves fit on a SIMD.
+// flight: at two column blocks per wave two waves fit on a SIMD.  The tile
+// step is bound by vector instructions, so a wave widens and permutes a
+// tile's value rows once for both its column blocks, and skips the causal
+// mask on tiles every one of its columns sees whole (all but the last few
+// of a long context).
 // LDS rows are padded by 16 bytes so that the 16 rows a tile's K slices come
 // from fall in distinct banks.
 #include "tile_mfma.hpp"
@@ -55,7 +60,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     typedef typename TM::vraw vraw;
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const TM tm;
-    const int lane = tm.lane;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -104,6 +108,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     typename TM::Acc acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) tm.reset(acc[b]);
+    // The last token every live column of this wave sees: tiles up to it
+    // need no causal mask (columns past the wave's tokens are never written).
+    int vis = INT_MAX;
+#pragma unroll
+    for (int b = 0; b < NB; b++) vis = min(vis, tm.j16 < ncols[b] ? pc[b] : INT_MAX);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) vis = min(vis, __shfl_xor(vis, o, 64));
+    vis = __builtin_amdgcn_readfirstlane(vis);
 
     // ---- stage loads: thread tid moves kLoads 16-byte pieces per stage ----
     const int32_t* table = p.tables + (size_t)s * p.max_blocks;
@@ -111,23 +123,38 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     const size_t pool_row = (size_t)p.Hkv * SH::kRow;      // bytes between slots
     const size_t head_off = (size_t)h * SH::kRow;
     u32x4 stage[SH::kLoads];
+    // Piece j of thread tid is K (or V) row t, 16-byte chunk tid % kChunks.
+    // The 64 lanes of a wave cover 64 / kChunks consecutive, aligned rows
+    // (4 at D = 128, 8 at D = 64), so they lie in one block for every block
+    // size: one wave-uniform table entry (a scalar load) and one buffer
+    // descriptor per piece.  Rows at or past wg_end take an offset past the
+    // descriptor and read zeros, with no branch around the load (a branch
+    // would make the loop wait for every load in flight).
+    static_assert(64 % SH::kChunks == 0 && 64 / SH::kChunks <= 8, "a wave's rows in one block");
+    const int lane_row = (tid & 63) / SH::kChunks;
+    const uint32_t lane_chunk = (uint32_t)((tid & 63) % SH::kChunks) * 16u;
+    const uint32_t blk_bytes = (uint32_t)p.bs * (uint32_t)pool_row;
     auto load_stage = [&](int t0) {
+        // the wave's first row of piece j
+        auto row0 = [&](int j) {
+            return t0 + ((j * 64 * kWaves + wave * 64) % (kStageTok * SH::kChunks)) / SH::kChunks;
+        };
+        uint32_t blk[SH::kLoads];
+#pragma unroll
+        for (int j = 0; j < SH::kLoads; j++)   // all table entries first, one wait
+            blk[j] = (uint32_t)table[min(row0(j), wg_end - 1) >> bs_shift];
 #pragma unroll
         for (int j = 0; j < SH::kLoads; j++) {
-            const int idx = j * 64 * kWaves + tid;
-            const int kv = idx / (kStageTok * SH::kChunks);          // 0: K, 1: V
-            const int rem = idx % (kStageTok * SH::kChunks);
-            const int t = t0 + rem / SH::kChunks;
-            const int chunk = rem % SH::kChunks;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (t < wg_end) {
-                const uint32_t blk = (uint32_t)table[t >> bs_shift];
-                const uint32_t b = blk < (uint32_t)p.NB ? blk : (uint32_t)p.NB - 1u;
-                const char* base = (const char*)(kv ? p.v : p.k);
-                v = *(const u32x4*)(base + ((size_t)b * p.bs + (t & (p.bs - 1))) * pool_row +
-                                    head_off + (size_t)chunk * 16);
-            }
-            stage[j] = v;
+            const int kv = (j * 64 * kWaves + wave * 64) / (kStageTok * SH::kChunks);   // 0: K, 1: V
+            const int tw = row0(j);
+            const uint32_t b = blk[j] < (uint32_t)p.NB ? blk[j] : (uint32_t)p.NB - 1u;
+            const rsrc_t r = make_rsrc((const char*)(kv ? p.v : p.k) + (size_t)b * blk_bytes,
+                                       blk_bytes);
+            const int t = tw + lane_row;
+            const uint32_t off = t < wg_end ? (uint32_t)(t & (p.bs - 1)) * (uint32_t)pool_row +
+                                                  (uint32_t)head_off + lane_chunk
+                                            : kOOB;
+            stage[j] = Buf<16>::load(r, off);
         }
     };
     auto store_stage = [&](int buf) {
@@ -159,26 +186,38 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         store_stage(0);
     }
     __syncthreads();
-    for (int st = 0; st < nstage; st++) {
-        const int buf = st & 1;
-        const int t0 = st * kStageTok;
-        const bool more = st + 1 < nstage;
-        if (more) load_stage(t0 + kStageTok);              // in flight during the tiles
+    // Stages [st0, st1), every tile with the causal limits (MASK) or, for
+    // stages all of whose tokens every column of this wave sees, without.
+    // Each call passes one barrier per stage, so waves that split the
+    // stages differently still meet at every barrier.
+    auto run_stages = [&](int st0, int st1, auto mask) {
+        constexpr bool MASK = decltype(mask)::value;
+        for (int st = st0; st < st1; st++) {
+            const int buf = st & 1;
+            const int t0 = st * kStageTok;
+            const bool more = st + 1 < nstage;
+            if (more) load_stage(t0 + kStageTok);          // in flight during the tiles
 #pragma unroll
-        for (int tile = 0; tile < kStageTok / 16; tile++) {
-            const int tt = t0 + 16 * tile;
-            if (tt < t_end) {                              // wave-uniform
-                typename TM::Tile tl;
-                read_tile(buf, tile, tl);
+            for (int tile = 0; tile < kStageTok / 16; tile++) {
+                const int tt = t0 + 16 * tile;
+                if (tt < t_end) {                          // wave-uniform
+                    typename TM::Tile tl;
+                    read_tile(buf, tile, tl);
 #pragma unroll
-                for (int b = NB - 1; b >= 0; b--)
-                    tm.template consume<true>(acc[b], qb[b], p.scale_log2, t_end - 1 - tt, tl,
-                                              pc[b] - tt);
+                    for (int b = NB - 1; b >= 0; b--)
+                        tm.template consume<true, MASK>(acc[b], qb[b], p.scale_log2,
+                                                        t_end - 1 - tt, tl, pc[b] - tt);
+                }
             }
+            if (more) store_stage(buf ^ 1);                // read by no wave since the
+            __syncthreads();                               // last barrier
         }
-        if (more) store_stage(buf ^ 1);                    // read by no wave since the
-        __syncthreads();                                   // last barrier
-    }
+    };
+    // stage st is seen whole by every live column when st * kStageTok +
+    // kStageTok - 1 <= vis
+    const int nfull = vis >= kStageTok - 1 ? min(nstage, (vis + 1) / kStageTok) : 0;
+    run_stages(0, nfull, std::false_type{});
+    run_stages(nfull, nstage, std::true_type{});
 
 #pragma unroll
     for (int b = 0; b < NB; b++)

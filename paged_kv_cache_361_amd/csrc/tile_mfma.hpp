@@ -299,9 +299,53 @@ struct TileMath {
     // query tokens as well as heads, and column lane%16 also drops the rows
     // past clim (its own limit within the tile); a column can then have
     // seen no token yet, so weights of dropped rows are forced to zero.
-    template <bool CAUSAL = false>
+    // MASK = false: the caller knows that every column it keeps sees every
+    // row of the tile, so no limit is applied (the same result, fewer
+    // vector instructions).
+    template <bool CAUSAL = false, bool MASK = true>
     __device__ inline void consume(Acc& a, const v8 (&qb)[KS], float scale_log2, int lim,
                                    const Tile& cur, int clim = 0) const {
+        const f32x4 sc = scores(qb, cur);
+        v4 p_hi, p_lo;
+        weights<CAUSAL, MASK>(a, sc, scale_log2, lim, clim, p_hi, p_lo);
+        vrow vr[4];
+        value_rows(cur, vr);
+#pragma unroll
+        for (int n = 0; n < NT; n++) {
+            const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
+            a.o[n] = M::pv(p_hi, b, a.o[n]);
+        }
+        if constexpr (M::kSplitP) {
+#pragma unroll
+            for (int n = 0; n < NT; n++) {
+                const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
+                a.o[n] = M::pv(p_lo, b, a.o[n]);
+            }
+        }
+    }
+
+  private:
+    // The tile's four value rows of this lane (rows 4*g4 .. 4*g4+3, columns
+    // NT*j16 ..), widened to the matrix-core type.
+    __device__ inline void value_rows(const Tile& cur, vrow (&vr)[4]) const {
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            if constexpr (kFp8) {
+                const uint32_t* w = (const uint32_t*)&cur.v[r];
+#pragma unroll
+                for (int q = 0; q < NT / 4; q++) {
+                    const v4 x = M::from_fp8x4(w[q]);
+#pragma unroll
+                    for (int e = 0; e < 4; e++) vr[r][4 * q + e] = x[e];
+                }
+            } else {
+                vr[r] = __builtin_bit_cast(vrow, cur.v[r]);
+            }
+        }
+    }
+
+    // Scores of the tile's 16 rows against the 16 B columns.
+    __device__ inline f32x4 scores(const v8 (&qb)[KS], const Tile& cur) const {
         f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < KL; i++) {
@@ -318,12 +362,20 @@ struct TileMath {
                 sc = M::qk(__builtin_bit_cast(v8, cur.k[i]), qb[i], sc);
             }
         }
+        return sc;
+    }
+
+    // Masking, online softmax update of (m, l, o), and the weights as the A
+    // operand (bf16 hi + lo pair where the type needs it).
+    template <bool CAUSAL, bool MASK>
+    __device__ inline void weights(Acc& a, const f32x4& sc, float scale_log2, int lim, int clim,
+                                   v4& p_hi, v4& p_lo) const {
         float z[4];
         const int rlim = CAUSAL ? (clim < lim ? clim : lim) : lim;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const float x = sc[r] * scale_log2;
-            z[r] = (4 * g4 + r <= rlim) ? x : -INFINITY;
+            z[r] = (!MASK || 4 * g4 + r <= rlim) ? x : -INFINITY;
         }
 
         // ---- online softmax: tile max over the 16 tokens of each head ----
@@ -347,45 +399,19 @@ struct TileMath {
         float pz[4];
 #pragma unroll
         for (int r = 0; r < 4; r++)
-            pz[r] = (CAUSAL && z[r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[r] - a.m);
+            pz[r] = (CAUSAL && MASK && z[r] == -INFINITY) ? 0.0f
+                                                          : __builtin_amdgcn_exp2f(z[r] - a.m);
         a.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
 
-        // ---- weights as the A operand, value rows as the B operand ----
-        v4 p_hi, p_lo;
+        // ---- weights as the A operand ----
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             p_hi[r] = (T)pz[r];
             if constexpr (M::kSplitP) p_lo[r] = (T)(pz[r] - (float)p_hi[r]);
         }
-        vrow vr[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            if constexpr (kFp8) {
-                const uint32_t* w = (const uint32_t*)&cur.v[r];
-#pragma unroll
-                for (int q = 0; q < NT / 4; q++) {
-                    const v4 x = M::from_fp8x4(w[q]);
-#pragma unroll
-                    for (int e = 0; e < 4; e++) vr[r][4 * q + e] = x[e];
-                }
-            } else {
-                vr[r] = __builtin_bit_cast(vrow, cur.v[r]);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NT; n++) {
-            const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
-            a.o[n] = M::pv(p_hi, b, a.o[n]);
-        }
-        if constexpr (M::kSplitP) {
-#pragma unroll
-            for (int n = 0; n < NT; n++) {
-                const v4 b = v4{vr[0][n], vr[1][n], vr[2][n], vr[3][n]};
-                a.o[n] = M::pv(p_lo, b, a.o[n]);
-            }
-        }
     }
 
+  public:
     // Epilogue.  Lane (g4, j16) holds accumulator rows head = 4*g4 + r and
     // columns NT*j16 + n.  For every head < G, `out_row(head)` (when final)
     // receives the normalised row in the query type; otherwise `m_at(head)`,
