@@ -617,6 +617,44 @@ def bench_mixed(args) -> int:
                      "unit": "GB/s", "frac": round(dec_bytes / dec_s / 1e9 / PEAK_GBPS, 4),
                      "traffic": None},
     }
+    if args.cpu_baseline == "on":
+        import oracle
+        log("timing the CPU oracle ...")
+        host_append(c)
+        threads = oracle.max_threads()
+
+        def run(n):
+            t = time.perf_counter()
+            r = oracle.paged_decode_mixed(c.query, c.k_cache, c.v_cache, c.block_tables,
+                                          c.seq_lens, mc.seq_bs, q_dtype=c.q_dtype,
+                                          cache_dtype=c.cache_dtype, scale=c.scale,
+                                          rows=np.arange(n * c.Hq, dtype=np.int32),
+                                          threads=threads)
+            return time.perf_counter() - t, r
+
+        n = min(8, c.S)
+        t, ref = run(n)
+        if t < 5.0 and n < c.S:           # size the sample to about 20 s
+            per_tok = t / max(int(c.seq_lens[:n].sum()), 1)
+            cum = np.cumsum(c.seq_lens.astype(np.int64))
+            n = int(min(c.S, max(n, np.searchsorted(cum, 20.0 / per_tok) + 1)))
+            t, ref = run(n)
+        sub = c.copy()
+        sub.S, sub.seq_lens, sub.slot_mapping = n, c.seq_lens[:n], c.slot_mapping[:0]
+        nbytes = decode_bytes(sub, 0)["decode_kernel"]
+        res["cpu_baseline"] = {
+            "value": round(nbytes / t / 1e12, 6), "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "tokens_per_s_per_layer": round(n / t, 2), "seconds": round(t, 3),
+            "sample": "decode of the first %d of %d sequences (%d tokens, all %d query heads), "
+                      "gather by each sequence's block size + fp64 softmax attention, OpenMP "
+                      "over rows" % (n, c.S, int(c.seq_lens[:n].sum()), c.Hq)}
+        gpu = out[:n].float().cpu().numpy().astype(np.float64)
+        err = float(np.max(np.abs(gpu - ref[:n])))
+        tol = TOL[c.cache_dtype]
+        res["max_abs_err_vs_oracle"] = {
+            "max_abs_err": err, "tol": tol, "within_tol": bool(err <= tol), "rows": n * c.Hq,
+            "of_rows": c.S * c.Hq,
+            "sample": "the oracle's rows above against the output of the last step"}
     print(json.dumps(res), flush=True)
     return 0
 
