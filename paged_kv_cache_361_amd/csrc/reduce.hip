@@ -17,12 +17,16 @@
 // 4 or 8 when rows have many entries; with WPR > 1 a workgroup is one row).
 // Lane (kg = lane / 16, c = lane % 16) of wave `sub` owns output columns
 // [c*CW, c*CW + CW) of the entries e = j, j + 4*WPR, j + 8*WPR, ... with
-// slot j = 4*sub + kg.  A slot keeps a running reference max, sum and output
-// over its entries (the online-softmax update of the decode, once per entry),
-// loading batch(WPR) entries per round with all their loads issued together,
-// so a row of n entries takes ceil(n / (4 * WPR * batch(WPR))) rounds of
-// memory latency.  The slots then meet at the row's max: lane shuffles within a
-// wave, LDS across waves.
+// slot j = 4*sub + kg.
+//   One wave (merge_short): the row max and the denominator come from one
+//   (m, l) pair per lane by wave-wide reductions, and the slots' first four
+//   entries are loaded at the same time; short rows need no more.
+//   Several waves (merge_row): a slot keeps a running reference max, sum and
+//   output over its entries (the online-softmax update of the decode, once
+//   per entry), loading kBatch entries per round with all their loads issued
+//   together, so a row of n entries takes ceil(n / (4 * WPR * kBatch))
+//   rounds of memory latency; the slots then meet at the row's max through
+//   lane shuffles and LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,10 +35,8 @@ namespace {
 
 constexpr int kWaves = 4;      // waves per workgroup of one-wave rows
 
-// Entries per slot loaded per round: 3 for one-wave rows (a row of up to 12
-// entries in one round; four would not fit the register budget below
-// without spilling), 8 for rows served by several waves (long rows).
-constexpr int batch(int WPR) { return WPR > 1 ? 8 : 3; }
+// Entries per slot that merge_row loads per round.
+constexpr int kBatch = 8;
 
 // Waves per SIMD each kernel is compiled to fit (a register budget): eight
 // for one-wave rows, so that a batch of 8192 rows (2048 workgroups of four
@@ -45,15 +47,16 @@ constexpr int waves_per_simd(int WPR) { return WPR > 1 ? 4 : 8; }
 // Waves per workgroup of a kernel serving rows with WPR waves each.
 constexpr int wg_waves(int WPR) { return WPR > 1 ? WPR : kWaves; }
 
-// Merges n >= 1 entries into one output row.  idx(e) maps entry e to its
-// index in the m/l arrays (o rows at idx * D).  A row whose entries hold no
-// weight (every m = -inf) is written as zeros.
+// Merges n >= 1 entries into one output row served by WPR > 1 waves (one
+// workgroup).  idx(e) maps entry e to its index in the m/l arrays (o rows at
+// idx * D).  A row whose entries hold no weight (every m = -inf) is written
+// as zeros.
 template <class O, int D, int WPR, class Idx>
 __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t row, int sub) {
+    static_assert(WPR > 1, "one-wave rows take merge_short");
     constexpr int CW = D / 16;                 // columns per lane
     constexpr int SLOTS = 4 * WPR;             // entry slots per row
-    constexpr int NP = WPR > 1 ? WPR : 1;
-    constexpr int kBatch = batch(WPR);
+    constexpr int NP = WPR;
     typedef float colv __attribute__((ext_vector_type(CW)));
     __shared__ colv part_sum[NP][16];
     __shared__ float part_m[NP], part_l[NP];
@@ -73,26 +76,14 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
 #pragma unroll
         for (int u = 0; u < kBatch; u++) {     // the round's loads, all at once
             const int e = e0 + u * SLOTS;
-            if constexpr (WPR > 1) {
-                // long rows: entries past n get no weight and issue no loads
-                o[u] = colv{};
-                m[u] = -INFINITY;
-                l[u] = 0.0f;
-                if (e < n) {
-                    const size_t ie = idx(e);
-                    o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
-                    m[u] = p.ws_m[ie];
-                    l[u] = p.ws_l[ie];
-                }
-            } else {
-                // short rows: straight-line loads (entries past n reread entry
-                // 0, a cache hit, and get no weight), cheaper than branching
-                // around each of a few loads
-                const size_t ie = idx(e < n ? e : 0);
+            o[u] = colv{};                     // entries past n: no weight, no loads
+            m[u] = -INFINITY;
+            l[u] = 0.0f;
+            if (e < n) {
+                const size_t ie = idx(e);
                 o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
                 m[u] = p.ws_m[ie];
                 l[u] = p.ws_l[ie];
-                if (e >= n) m[u] = -INFINITY;
             }
         }
         // Keep every load of the round ahead of the arithmetic: otherwise the
@@ -124,31 +115,25 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
     // the four slots of a wave (lanes c, c+16, c+32, c+48) by lane shuffles,
     // the waves of a row through LDS.
     float M = group_max<64>(m_run);
-    if constexpr (WPR > 1) {
-        if (lane == 0) part_m[sub] = M;
-        __syncthreads();
-        M = part_m[0];
+    if (lane == 0) part_m[sub] = M;
+    __syncthreads();
+    M = part_m[0];
 #pragma unroll
-        for (int w = 1; w < WPR; w++) M = fmaxf(M, part_m[w]);
-    }
+    for (int w = 1; w < WPR; w++) M = fmaxf(M, part_m[w]);
     const float f = exp2f(m_run - (M == -INFINITY ? 0.0f : M));
     float den = strided_sum<16>(l_run * f);
 #pragma unroll
     for (int q = 0; q < CW; q++) acc[q] = strided_sum<16>(acc[q] * f);
-    if constexpr (WPR > 1) {
-        if (kg == 0) part_sum[sub][c] = acc;
-        if (lane == 0) part_l[sub] = den;
-        __syncthreads();
-        if (sub != 0 || kg != 0) return;
+    if (kg == 0) part_sum[sub][c] = acc;
+    if (lane == 0) part_l[sub] = den;
+    __syncthreads();
+    if (sub != 0 || kg != 0) return;
 #pragma unroll
-        for (int w = 1; w < WPR; w++) {
-            const colv x = part_sum[w][c];
+    for (int w = 1; w < WPR; w++) {
+        const colv x = part_sum[w][c];
 #pragma unroll
-            for (int q = 0; q < CW; q++) acc[q] += x[q];
-            den += part_l[w];
-        }
-    } else {
-        if (kg != 0) return;
+        for (int q = 0; q < CW; q++) acc[q] += x[q];
+        den += part_l[w];
     }
     const float inv = den > 0.0f ? 1.0f / den : 0.0f;
     typedef typename O::T OT;
@@ -157,6 +142,91 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
 #pragma unroll
     for (int q = 0; q < CW; q++) r[q] = O::narrow(acc[q] * inv);
     *(ovec*)((OT*)p.out + row * D + c * CW) = r;
+}
+
+// merge_row for rows served by one wave (WPR = 1), with n up to a few dozen
+// entries.  Everything such a row needs is requested before anything waits:
+// the first 64 (m, l) pairs, one per lane, and the first four entries of
+// this lane's slot (the output columns do not depend on the row max).  The
+// row max and the denominator come from the (m, l) pairs by wave-wide
+// reductions, then the slots' weighted sums meet by lane shuffles.  On the
+// short rows of a decode batch this is about 1 us faster per call than the
+// running-max merge, which long rows need.  Out-of-range slots read entry 0
+// and get weight 0.
+template <class O, int D, class Idx>
+__device__ inline void merge_short(const ReduceParams& p, int n, Idx idx, size_t row) {
+    constexpr int CW = D / 16;                 // columns per lane
+    constexpr int SLOTS = 4;                   // entry slots per row
+    constexpr int U = 4;                       // entries per slot per round
+    typedef float colv __attribute__((ext_vector_type(CW)));
+
+    const int lane = threadIdx.x & 63;
+    const int j = lane >> 4;                   // this lane's slot
+    const int c = lane & 15;
+
+    const size_t i0 = lane < n ? idx(lane) : 0;
+    const float m0 = lane < n ? p.ws_m[i0] : -INFINITY;
+    const float l0 = lane < n ? p.ws_l[i0] : 0.0f;
+    colv o[U];
+    float mo[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int e = j + u * SLOTS;
+        const size_t ie = idx(e < n ? e : 0);
+        o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+        mo[u] = p.ws_m[ie];
+    }
+
+    // M and the denominator over all entries (lanes stride by 64).
+    float M = m0;
+    for (int e = lane + 64; e < n; e += 64) M = fmaxf(M, p.ws_m[idx(e)]);
+    M = group_max<64>(M);
+    const float Ml = M == -INFINITY ? 0.0f : M * kLog2e;
+    float den = lane < n ? exp2f(fmaf(m0, kLog2e, -Ml)) * l0 : 0.0f;
+    for (int e = lane + 64; e < n; e += 64) {
+        const size_t ie = idx(e);
+        den += exp2f(fmaf(p.ws_m[ie], kLog2e, -Ml)) * p.ws_l[ie];
+    }
+    den = group_sum<64>(den);
+
+    // Weighted sum of this lane's slot, U entries per round.
+    colv acc = colv{};
+    for (int e0 = j; e0 < n; e0 += SLOTS * U) {
+        if (e0 != j) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int e = e0 + u * SLOTS;
+                const size_t ie = idx(e < n ? e : 0);
+                o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+                mo[u] = p.ws_m[ie];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int e = e0 + u * SLOTS;
+            const float w = e < n ? exp2f(fmaf(mo[u], kLog2e, -Ml)) : 0.0f;
+#pragma unroll
+            for (int q = 0; q < CW; q++) acc[q] = fmaf(w, o[u][q], acc[q]);
+        }
+    }
+    // the four slots of the wave (lanes c, c+16, c+32, c+48)
+#pragma unroll
+    for (int q = 0; q < CW; q++) acc[q] = strided_sum<16>(acc[q]);
+    if (j != 0) return;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    typedef typename O::T OT;
+    typedef OT ovec __attribute__((ext_vector_type(CW)));
+    ovec r;
+#pragma unroll
+    for (int q = 0; q < CW; q++) r[q] = O::narrow(acc[q] * inv);
+    *(ovec*)((OT*)p.out + row * D + c * CW) = r;
+}
+
+// One of the two merges, by the waves a row has.
+template <class O, int D, int WPR, class Idx>
+__device__ inline void merge(const ReduceParams& p, int n, Idx idx, size_t row, int sub) {
+    if constexpr (WPR == 1) merge_short<O, D>(p, n, idx, row);
+    else merge_row<O, D, WPR>(p, n, idx, row, sub);
 }
 
 // ---- fixed partitions -------------------------------------------------------
@@ -176,7 +246,7 @@ void reduce_kernel(ReduceParams p) {
     const int nparts = L > 0 ? (L + p.P - 1) / p.P : 0;
     if (nparts <= 1) return;
     const size_t base = (size_t)row * p.P_max;
-    merge_row<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, sub);
+    merge<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, sub);
 }
 
 // ---- balanced split ---------------------------------------------------------
@@ -264,7 +334,7 @@ void reduce_balanced_kernel(ReduceParams p) {
     const int c1 = chunk_of(q, g0 + nt - 1);
     if (c0 == c1) return;                       // one chunk held it: decode wrote the row
     const int slot0 = chunk_begin(q, c0) < g0 ? 1 : 0;
-    merge_row<O, D, WPR>(
+    merge<O, D, WPR>(
         p, c1 - c0 + 1,
         [&](int e) {
             const int slot = e == 0 ? slot0 : 0;
