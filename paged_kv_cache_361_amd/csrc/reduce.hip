@@ -277,10 +277,11 @@ void reduce_balanced_kernel(ReduceParams p) {
     const int maxq = MULTI ? p.S / S : 1;       // MULTI: p.S = num_seqs * max_query_len
     const int s = row / (maxq * p.Hq);
     const int j = MULTI ? (row / p.Hq) % maxq : 0;
-    // Every word the row needs, requested together before any of them is
-    // looked at (one memory round trip): the header, the prefix total, the
-    // sequence's prefix entries and, for MULTI, its query range and length.
-    // All of them lie inside the workspace and the arrays the call passed.
+    // Every word the row needs is loaded before any of them is tested: the
+    // header, the prefix total, the sequence's prefix entries and, for
+    // MULTI, its query range and length.  No load then waits behind a test of
+    // another.  All of them lie inside the workspace and the arrays the call
+    // passed.
     const int magic = hdr[kHdrMagic];
     const int nW = hdr[kHdrNW];
     const int Hkv = hdr[kHdrHkv];
@@ -291,7 +292,6 @@ void reduce_balanced_kernel(ReduceParams p) {
     const int q0 = MULTI ? p.q_start[s] : 0;
     const int q1 = MULTI ? p.q_start[s + 1] : 0;
     const int Lraw = MULTI ? p.lens[s] : 0;
-    __builtin_amdgcn_sched_barrier(0);          // all of them issued before any wait
     // A workspace not written by a balanced call of this shape (or inputs
     // breaking the call's contract): write nothing rather than follow its
     // indices.  One condition of every word, combined without short cuts, so
