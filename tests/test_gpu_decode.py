@@ -272,6 +272,24 @@ def test_zero_and_one_token_sequences(algo):
 
 
 @pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("P", [0, 64, 512])
+@_skip_unsupported
+def test_all_zero_length_batch(algo, P):
+    """No sequence holds a token, so the batch has no tiles at all: every row
+    of the output (filled with NaN first) is written as zeros, unsplit and
+    split."""
+    c = workloads.make_case("all-empty", 91, [1, 1, 1, 1], 16, 4, 128, 16,
+                            q_dtype="bf16", cache_dtype="bf16")
+    c.seq_lens[:] = 0
+    d = DevCase(c)
+    d.write()
+    d.out.fill_(float("nan"))
+    d.decode(algo, P)
+    torch.cuda.synchronize()
+    assert np.all(from_dev(d.out) == 0.0)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
 @_skip_unsupported
 def test_every_e4m3_code_decodes_exactly(algo):
     """L = 1 returns v_scale * decode(code) of the value row: with scale 1 and
@@ -364,7 +382,7 @@ def test_balanced_f32_is_unsupported():
 
 
 @pytest.mark.parametrize("lens", [[1], [3, 0, 17], [1, 1, 1, 0, 2], [16, 32, 48], [5000],
-                                  [0, 0, 700]])
+                                  [0, 0, 700], [0, 0, 0]])
 def test_balanced_small_batches(lens):
     """Far fewer tiles than waves (most waves idle), zero-length rows written by
     the reduce, one-token and tile-multiple lengths."""
