@@ -47,18 +47,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def balanced_split(lens: np.ndarray, Hkv: int, nW: int):
+def chunk_floor(cache_dtype: str, bs: int, D: int) -> int:
+    """Floor on the balanced split's later chunks: two rounds of the decode's
+    tile ring (10 tiles for fp8, else 6, or 8 at D = 64; half with 8-token
+    blocks)."""
+    pair = bs == 8
+    if E[cache_dtype] == 1:
+        depth = 5 if pair else 10
+    else:
+        depth = 4 if pair else (8 if D == 64 else 6)
+    return 2 * depth
+
+
+def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int):
     """The balanced split's pieces, replayed on the host: the streams
     (sequence, KV head) of 16-token tiles laid end to end and cut into chunks
     by the guided schedule (nW chunks of max(1, 4A/5) tiles, nW of
-    max(1, A/7), then max(4, A/16), A = T / nW).  Returns (number of streams
-    spread over several chunks, partial entries they write per query head)."""
+    max(A/7, F), then max(A/16, F), A = T / nW, F = max(floor, 4)).  Returns
+    (number of streams spread over several chunks, partial entries they write
+    per query head)."""
     nt = -(-np.maximum(lens.astype(np.int64), 0) // 16)
     T = int(nt.sum()) * Hkv
     if T == 0:
         return 0, 0
     A = T // nW
-    C1, C2, C3 = max(1, A * 4 // 5), max(1, A // 7), max(4, A // 16)
+    F = max(floor, 4)
+    C1, C2, C3 = max(1, A * 4 // 5), max(F, A // 7), max(F, A // 16)
     e1, e2 = min(nW * C1, T), min(nW * (C1 + C2), T)
 
     def chunk_of(x):
@@ -92,7 +106,8 @@ def decode_bytes(c, P: int, nW: int = 0) -> dict:
     elif P < 0:
         # a split (sequence, KV head) stream writes one entry per piece for each
         # query head of its group; its G output rows come from the reduce
-        split_streams, entries = balanced_split(L, c.Hkv, nW)
+        split_streams, entries = balanced_split(L, c.Hkv, nW,
+                                                chunk_floor(c.cache_dtype, c.bs, c.D))
         n_multi = split_streams / c.Hkv          # in units of whole sequences
         partials = entries * c.G * (c.D + 2) * 4
     # decode: K/V, Q, O of sequences it finishes, table, lengths, partials out

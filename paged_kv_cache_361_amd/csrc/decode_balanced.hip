@@ -272,7 +272,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     const TM tm;
     const int lane = tm.lane;
     const int w = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const Sched q = make_sched(__builtin_amdgcn_readfirstlane(pre[p.S]), p.nW);
+    // final chunks of at least two rounds of the ring
+    const Sched q = make_sched(__builtin_amdgcn_readfirstlane(pre[p.S]), p.nW, 2 * DEPTH);
     if (blockIdx.x == 0) {
         // what the reduce needs: the prefix and the schedule
         for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) p.ws_pre[i] = pre[i];
@@ -286,6 +287,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             hdr[kHdrC2] = q.C2;
             hdr[kHdrC3] = q.C3;
             hdr[kHdrChunks] = q.chunks;
+            hdr[kHdrFloor] = 2 * DEPTH;
         }
     }
     if (w >= q.chunks || w >= p.nW) return;

@@ -71,18 +71,22 @@ struct ReduceParams {
 //
 // The T tiles of a batch (16 tokens of one (sequence, KV head) stream each,
 // streams laid end to end) are cut into chunks by a guided schedule that
-// depends only on T and the grid size nW: nW chunks of C1 tiles (80% of an
-// even share A = T / nW), then nW chunks of C2 (A / 7), then chunks of
-// C3 = max(4, A / 16) up to T.  (Sizes measured best on MI355X for ragged
-// batches on a grid of one wave per SIMD; neighbouring choices were 1-15 us
-// slower per call.)  Chunk c starts at tile
+// depends only on T, the grid size nW and a floor F: nW chunks of C1 tiles
+// (80% of an even share A = T / nW), then nW chunks of C2 = max(A / 7, F),
+// then chunks of C3 = max(A / 16, F) up to T.  The decode sets F to two
+// rounds of its tile ring, so that a chunk's index and table window, which
+// arrive one after the other, are at hand before its first round is due.
+// (Sizes measured best on MI355X for ragged batches on a grid of one wave
+// per SIMD: neighbouring divisors were 1-15 us slower per call; on short fp8
+// runs, floors of 4 and 12 tiles were 16 and 6 us slower than 20, and 30 or
+// 40 slower again.)  Chunk c starts at tile
 // chunk_begin(c); the decode grid takes chunks 0..nW-1 statically and the
 // rest from a counter, and the reduce finds a stream's chunks with
 // chunk_of().
 //
 // Workspace: a 256-byte header, the exclusive tile prefix of the sequences
 // (S + 1 words) from byte 256, then (m, l, o) entries, two per query head of
-// the group per chunk.  Header words 0-8 describe the split for the reduce
+// the group per chunk.  Header words 0-9 describe the split for the reduce
 // (written by each decode call).  Words 32-33 (their own 128-byte line) hold
 // the chunk counter, a 64-bit word: high half the number of the call that
 // owns it, low half kCountTag | count.  Nothing resets it between calls: a
@@ -97,8 +101,10 @@ constexpr uint32_t kCountTag = 0xA5000000u;
 constexpr uint32_t kCountMask = 0x00FFFFFFu;
 enum BalancedHeader : int {
     kHdrMagic = 0, kHdrNW = 1, kHdrHkv = 2, kHdrG = 3, kHdrT = 4, kHdrC1 = 5, kHdrC2 = 6,
-    kHdrC3 = 7, kHdrChunks = 8, kHdrCounter = 32
+    kHdrC3 = 7, kHdrChunks = 8, kHdrFloor = 9, kHdrCounter = 32
 };
+// Largest chunk floor a decode sets (two rounds of its deepest ring).
+constexpr int kMaxChunkFloor = 64;
 // Upper bound on the persistent grid of the balanced kernel (wavefronts).
 constexpr int kBalancedMaxWaves = 2048;
 // Upper bound on the batch size of the balanced kernel (the tile prefix of
@@ -110,14 +116,15 @@ struct Sched {
     int e1, e2;            // first tiles of the second and third phases (capped at T)
 };
 
-__host__ __device__ inline Sched make_sched(int T, int nW) {
+__host__ __device__ inline Sched make_sched(int T, int nW, int floor) {
     Sched q;
     q.T = T;
     q.nW = nW;
     const int A = nW > 0 ? T / nW : 0;
     q.C1 = A * 4 / 5 > 1 ? A * 4 / 5 : 1;
-    q.C2 = A / 7 > 1 ? A / 7 : 1;
-    q.C3 = A / 16 > 4 ? A / 16 : 4;
+    if (floor < 4) floor = 4;
+    q.C2 = A / 7 > floor ? A / 7 : floor;
+    q.C3 = A / 16 > floor ? A / 16 : floor;
     const int64_t e1 = (int64_t)nW * q.C1;
     const int64_t e2 = e1 + (int64_t)nW * q.C2;
     q.e1 = (int)(e1 < T ? e1 : T);
@@ -147,8 +154,9 @@ __host__ __device__ inline int chunk_of(const Sched& q, int x) {
 
 // Most chunks any batch can produce on a grid of nW waves (the workspace
 // bound): phases one and two hold 2 nW chunks; C1 + C2 > 0.94 A - 2, so the
-// third covers fewer than (0.06 A + 3) nW tiles in chunks of max(4, A/16),
-// fewer than 2 nW + 1 chunks for every A.  The bound keeps room to spare.
+// third covers fewer than (0.06 A + 3) nW tiles in chunks of at least
+// max(4, A/16) (make_sched raises a floor below 4 to 4), fewer than
+// 2 nW + 1 chunks for every A.  The bound keeps room to spare.
 __host__ __device__ inline int64_t max_chunks(int nW) { return 5 * (int64_t)nW + 8; }
 
 // Launches a kernel whose only parameter is a parameter struct and returns

@@ -287,6 +287,7 @@ void reduce_balanced_kernel(ReduceParams p) {
     const int Hkv = hdr[kHdrHkv];
     const int G = hdr[kHdrG];
     const int T = hdr[kHdrT];
+    const int floor = hdr[kHdrFloor];
     const int preS = p.ws_pre[S];
     const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
     const int q0 = MULTI ? p.q_start[s] : 0;
@@ -298,10 +299,11 @@ void reduce_balanced_kernel(ReduceParams p) {
     // that no load is deferred behind a test of another.
     const bool bad = (magic != kBalancedMagic) | (nW < 1) | (nW > kBalancedMaxWaves) |
                      (G < 1) | (Hkv != p.Hkv) | (Hkv * G != p.Hq) | (T < 0) | (preS != T) |
+                     (floor < 1) | (floor > kMaxChunkFloor) |
                      (p0 < 0) | (p1 < p0) | (p1 > T) | ((p1 - p0) % max(Hkv, 1) != 0) |
                      (MULTI & ((q1 < q0) | (Lraw < 0)));
     if (bad) return;
-    const Sched q = make_sched(T, nW);
+    const Sched q = make_sched(T, nW, floor);
     const int hq = row % p.Hq;
     const int h = hq / G;
     int col = hq % G, ncol = G;

@@ -2,9 +2,10 @@
 
 The decode kernel lays the batch's 16-token tiles end to end per (sequence,
 KV head) stream and cuts them into chunks by a guided schedule that depends
-only on the tile count T and the grid size nW: nW chunks of
-C1 = max(1, 4A/5) tiles, nW of C2 = max(1, A/7), then chunks of
-C3 = max(4, A/16), with A = T / nW.  Inside a chunk a piece of a stream is a
+only on the tile count T, the grid size nW and a floor (two rounds of the
+decode's tile ring, 8 to 20 tiles): nW chunks of C1 = max(1, 4A/5) tiles, nW
+of C2 = max(A/7, F), then chunks of C3 = max(A/16, F), with A = T / nW and
+F = max(floor, 4).  Inside a chunk a piece of a stream is a
 segment: a whole stream writes its output, any other segment is the first
 (slot 0) or last (slot 1) of its chunk.  The reduce finds the chunks of a
 stream with chunk_of() and reads slot 1 of the first one when the stream
@@ -18,9 +19,10 @@ import numpy as np
 import pytest
 
 
-def sched(T, nW):
+def sched(T, nW, floor):
     A = T // nW
-    C1, C2, C3 = max(1, A * 4 // 5), max(1, A // 7), max(4, A // 16)
+    F = max(floor, 4)
+    C1, C2, C3 = max(1, A * 4 // 5), max(F, A // 7), max(F, A // 16)
     e1 = min(nW * C1, T)
     e2 = min(nW * C1 + nW * C2, T)
     if T <= 0:
@@ -63,21 +65,25 @@ def streams(lens, Hkv):
     return out, g
 
 
-CASES = [([3, 0, 17], 4, 2048), ([1], 4, 2048), ([0, 0, 700], 4, 64), ([5000], 1, 7),
-         ([16, 32, 48], 2, 5), ([1, 1, 1, 0, 2], 4, 3)]
+FLOORS = [8, 10, 12, 16, 20]
+CASES = [([3, 0, 17], 4, 2048, 12), ([1], 4, 2048, 20), ([0, 0, 700], 4, 64, 12),
+         ([0, 0, 700], 4, 64, 20), ([5000], 1, 7, 12), ([5000], 1, 7, 20),
+         ([16, 32, 48], 2, 5, 8), ([1, 1, 1, 0, 2], 4, 3, 10), ([0, 0, 0], 4, 64, 12)]
 
 
 def random_case(seed):
     rng = np.random.default_rng(seed)
     S = int(rng.integers(1, 300))
     lens = rng.integers(0, 3000, size=S).tolist()
-    return lens, int(rng.integers(1, 9)), int(rng.integers(1, 2049))
+    return (lens, int(rng.integers(1, 9)), int(rng.integers(1, 2049)),
+            FLOORS[int(rng.integers(0, len(FLOORS)))])
 
 
-@pytest.mark.parametrize("lens,Hkv,nW", CASES + [random_case(s) for s in range(40)])
-def test_split_properties(lens, Hkv, nW):
+@pytest.mark.parametrize("lens,Hkv,nW,floor", CASES + [random_case(s) for s in range(40)])
+def test_split_properties(lens, Hkv, nW, floor):
     strm, T = streams(lens, Hkv)
-    q = sched(T, nW)
+    q = sched(T, nW, floor)
+    assert q["C2"] >= max(floor, 4) and q["C3"] >= max(floor, 4)
     assert q["chunks"] <= 5 * nW + 8
     if T == 0:
         assert q["chunks"] == 0
@@ -112,9 +118,11 @@ def test_split_properties(lens, Hkv, nW):
         assert covered == g1 - g0
 
 
+@pytest.mark.parametrize("floor", [1, 4, 20, 64])
 @pytest.mark.parametrize("nW", [1, 2, 3, 7, 64, 512, 2048])
-def test_chunk_bound_over_all_sizes(nW):
+def test_chunk_bound_over_all_sizes(nW, floor):
     """The workspace is sized for 5 nW + 8 chunks: check every T up to a few
-    million (the phase sizes change with A = T / nW)."""
+    million (the phase sizes change with A = T / nW), for floors from below
+    the raised minimum of 4 to the largest the reduce accepts."""
     for T in list(range(1, 40000)) + list(range(40000, 4_000_000, 1009)):
-        assert sched(T, nW)["chunks"] <= 5 * nW + 8, T
+        assert sched(T, nW, floor)["chunks"] <= 5 * nW + 8, T
