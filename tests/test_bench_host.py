@@ -33,8 +33,31 @@ def test_traffic_keys():
         "shared-prefix-fp8-bs8"
     assert bench.traffic_key(ns(workload="long-context-gqa", partition=512), 32) == \
         "long-context-gqa-P512"
+    assert bench.traffic_key(ns(workload="shared-prefix-fp8", partition=-1), 16) == \
+        "shared-prefix-fp8-bs16-P-1"
     assert bench.decode_kernel_name(-1) == "decode_balanced_kernel"
     assert bench.decode_kernel_name(512) == "decode_mfma_kernel"
+
+
+def test_chunk_floor_is_two_rounds_of_the_ring():
+    """The floor bench.py replays the balanced split with: two rounds of the
+    decode's tile ring (10 tiles for fp8, 6 for 16-bit D = 128, 8 for D = 64,
+    half of that with 8-token blocks)."""
+    assert bench.chunk_floor("bf16", 16, 128) == 12
+    assert bench.chunk_floor("f16", 32, 64) == 16
+    assert bench.chunk_floor("fp8", 16, 128) == 20
+    assert bench.chunk_floor("fp8", 8, 128) == 10
+    assert bench.chunk_floor("bf16", 8, 128) == 8
+
+
+def test_balanced_split_replay_counts_split_streams():
+    """Two streams of 10 tiles on 2 waves: T = 20, A = 10, C1 = 8.  Stream 0
+    spans chunks 0-1 (tiles 0-7, 8-15); stream 1 spans chunks 1-2, the last
+    starting at tile 16 whatever the floor: 2 split streams, 4 entries."""
+    lens = np.array([160], np.int64)                 # 10 tiles per stream
+    assert bench.balanced_split(lens, 2, 2, 4) == (2, 4)
+    assert bench.balanced_split(lens, 2, 2, 20) == (2, 4)
+    assert bench.balanced_split(np.array([0], np.int64), 2, 2, 12) == (0, 0)
 
 
 def _write_csv(path, rows):
