@@ -261,6 +261,28 @@ def host_append(c) -> None:
 TOL = {"f32": 5e-3, "f16": 5e-3, "bf16": 5e-3, "fp8": 3e-2}
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the baseline's record."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cpus() -> dict:
+    """Logical CPUs of the host and those this process may run on."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 0
+    return {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count() or 0,
+            "usable_cpus": usable}
+
+
 def cpu_baseline(c, gpu_out=None, budget_s: float = 20.0):
     """The CPU oracle (as it stands) on the first sequences of the workload:
     a probe on a few sequences sizes a sample of about `budget_s`.  With
@@ -295,11 +317,14 @@ def cpu_baseline(c, gpu_out=None, budget_s: float = 20.0):
     if t < budget_s / 2:              # the whole workload is quick: repeat it
         reps = int(min(50, max(1, math.ceil(budget_s / 2 / t))))
         t = sum(run(n) for _ in range(reps)) / reps
-    sub = c.copy()
-    sub.S = n
-    sub.seq_lens = c.seq_lens[:n]
-    sub.slot_mapping = c.slot_mapping[:0]
-    nbytes = decode_bytes(sub, 0)["decode_kernel"]
+    def sample_bytes(n):
+        sub = c.copy()
+        sub.S = n
+        sub.seq_lens = c.seq_lens[:n]
+        sub.slot_mapping = c.slot_mapping[:0]
+        return decode_bytes(sub, 0)["decode_kernel"]
+
+    nbytes = sample_bytes(n)
     base = {"value": round(nbytes / t / 1e12, 6), "unit": "TB/s", "cores": threads,
             "kind": "oracle",
             "tokens_per_s_per_layer": round(n / t, 2),
@@ -307,6 +332,34 @@ def cpu_baseline(c, gpu_out=None, budget_s: float = 20.0):
             "sample": "decode of the first %d of %d sequences (%d tokens, all %d query "
                       "heads), gather + fp64 softmax attention, OpenMP over rows; mean "
                       "of %d run(s)" % (n, c.S, tok, c.Hq, reps)}
+    base.update(host_cpus())
+    # The same oracle on one thread, on the first sequences up to about a
+    # quarter of the budget (a probe on the first sequence sizes it).
+    kw1 = dict(kw, threads=1)
+
+    def run1(n1):
+        t0 = time.perf_counter()
+        oracle.paged_decode(c.query, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                            rows=np.arange(n1 * c.Hq, dtype=np.int32), **kw1)
+        return time.perf_counter() - t0
+
+    n1 = 1
+    t1 = run1(n1)
+    if t1 < budget_s / 8 and n1 < c.S:
+        per_tok = t1 / max(int(c.seq_lens[0]), 1)
+        cum = np.cumsum(c.seq_lens.astype(np.int64))
+        n1 = int(min(c.S, max(1, np.searchsorted(cum, budget_s / 4 / per_tok) + 1)))
+        t1 = run1(n1)
+    reps1 = 1
+    if t1 < budget_s / 8:             # the whole workload is quick: repeat it
+        reps1 = int(min(50, max(1, math.ceil(budget_s / 8 / max(t1, 1e-6)))))
+        t1 = sum(run1(n1) for _ in range(reps1)) / reps1
+    base["single_thread"] = {
+        "value": round(sample_bytes(n1) / t1 / 1e12, 6), "unit": "TB/s", "cores": 1,
+        "tokens_per_s_per_layer": round(n1 / t1, 2), "seconds": round(t1, 3),
+        "sample": "decode of the first %d sequences (%d tokens, all %d query heads), "
+                  "one thread; mean of %d run(s)" % (n1, int(c.seq_lens[:n1].sum()), c.Hq,
+                                                      reps1)}
     cmp = None
     if gpu_out is not None:
         m = last["n"]
@@ -477,6 +530,7 @@ def bench_multi(args) -> int:
             "kind": "oracle", "seconds": round(t, 3),
             "sample": "the first %d of %d query tokens, all %d query heads, gather + fp64 "
                       "softmax attention, OpenMP over rows" % (n, total_q, c.Hq)}
+        res["cpu_baseline"].update(host_cpus())
         gpu = out[:n].float().cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(gpu - ref[:n])))
         tol = TOL[c.cache_dtype]
@@ -663,6 +717,7 @@ def bench_mixed(args) -> int:
             "sample": "decode of the first %d of %d sequences (%d tokens, all %d query heads), "
                       "gather by each sequence's block size + fp64 softmax attention, OpenMP "
                       "over rows" % (n, c.S, int(c.seq_lens[:n].sum()), c.Hq)}
+        res["cpu_baseline"].update(host_cpus())
         gpu = out[:n].float().cpu().numpy().astype(np.float64)
         err = float(np.max(np.abs(gpu - ref[:n])))
         tol = TOL[c.cache_dtype]

@@ -18,7 +18,10 @@
  *   - Pointers are device pointers owned by the caller, except where noted.
  *     The library allocates, frees and synchronises nothing: each call
  *     validates its arguments on the host, enqueues kernels on `stream` and
- *     returns.  It keeps no state across calls, so calls are thread-safe.
+ *     returns.  The only state it keeps across calls is per-device facts
+ *     asked once and cached (compute-unit count, a kernel's occupancy) and
+ *     a counter that numbers balanced-split calls; both are atomics, so
+ *     calls are thread-safe.
  *   - Tensors are dense, row-major (C order), with the shapes given below.
  *     Device pointers must be 16-byte aligned.
  *   - Argument errors are reported by a negative pkv_status before anything
@@ -211,7 +214,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
 
 /*
  * pkv_paged_attention_decode_mixed - decode over a pool whose sequences use
- * different block sizes: "vLLM 推理引擎源码级拆解" §1.3 picks 8, 16 or 32
+ * different block sizes: "vLLM 0.5 深度拆解" §1.3 picks 8, 16 or 32
  * tokens per block per request (short requests small blocks, long ones
  * large).  The pages do not say how blocks of several sizes share memory;
  * this library's reading:

@@ -168,7 +168,7 @@ def paged_decode_mixed(query, k_cache, v_cache, block_tables, seq_lens, seq_bloc
                        threads: int = 0) -> np.ndarray:
     """paged_decode over a pool of pages (k_cache [num_pages, page, Hkv, D])
     whose sequences have blocks of seq_block_sizes[s] tokens, each that many
-    / page consecutive pages from the page the table names ("vLLM 推理引擎源码级拆解"
+    / page consecutive pages from the page the table names ("vLLM 0.5 深度拆解"
     §1.3 block sizes per request; the page layout is this library's reading)."""
     query = _c(query, _NP[q_dtype])
     k_cache = _c(k_cache, _NP[cache_dtype])

@@ -66,15 +66,36 @@ inline bool ws_layout(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max
 }
 
 // Resident wavefronts of the whole device for the balanced kernel serving
-// these types and shapes, capped at kBalancedMaxWaves.
-inline int balanced_grid_waves(int qdt, int cdt, int D, int bs, int S) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-        cus = 256;
-    int per_cu = decode_balanced_waves_per_cu(qdt, cdt, D, bs, S);
-    if (per_cu <= 0) per_cu = 4;
+// these types and shapes, capped at kBalancedMaxWaves.  The CU count and the
+// kernel's occupancy are asked once per device and kernel variant (with the
+// largest LDS the kernel takes, so the answer holds for every batch size)
+// and kept for the life of the process; a call then costs one hipGetDevice.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];                 // 0: not asked yet
+std::atomic<int> g_per_cu[kMaxDevices][2][2][2][3];  // [q f16/bf16][cache 16-bit/fp8][D][bs]
+
+inline int balanced_grid_waves(int qdt, int cdt, int D, int bs) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const bool cached = dev >= 0 && dev < kMaxDevices;
+    int cus = cached ? g_cus[dev].load(std::memory_order_relaxed) : 0;
+    if (cus <= 0) {
+        if (dev < 0 ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        if (cached) g_cus[dev].store(cus, std::memory_order_relaxed);
+    }
+    std::atomic<int>* slot =
+        cached ? &g_per_cu[dev][qdt == PKV_BF16][cdt == PKV_FP8_E4M3][D == 128]
+                          [bs == 8 ? 0 : (bs == 16 ? 1 : 2)]
+               : nullptr;
+    int per_cu = slot ? slot->load(std::memory_order_relaxed) : 0;
+    if (per_cu <= 0) {
+        per_cu = decode_balanced_waves_per_cu(qdt, cdt, D, bs, kBalancedMaxSeqs);
+        if (per_cu <= 0) per_cu = 4;
+        if (slot) slot->store(per_cu, std::memory_order_relaxed);
+    }
     const long n = (long)cus * per_cu;
     return (int)(n < kBalancedMaxWaves ? n : kBalancedMaxWaves);
 }
@@ -285,7 +306,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         p.ws_m = (float*)((char*)workspace + w.off_m);
         p.ws_l = (float*)((char*)workspace + w.off_l);
         p.ws_o = (float*)((char*)workspace + w.off_o);
-        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size, num_seqs);
+        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size);
         p.epoch = next_call_number();
         hipError_t e = launch_decode_balanced(q_dtype, cache_dtype, p, stream);
         if (e != hipSuccess) return launch_status(e);
@@ -574,7 +595,7 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
         if (algo == PKV_ALGO_VALU || !mfma_ok || num_seqs > kBalancedMaxSeqs)
             return PKV_ERR_UNSUPPORTED;
         p.P = 0;
-        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size, num_seqs);
+        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size);
         p.epoch = next_call_number();
         return launch_status(launch_decode_balanced(q_dtype, cache_dtype, p, stream));
     }

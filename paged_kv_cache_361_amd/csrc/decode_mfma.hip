@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
         [&](int head) { return p.ws_o + ((row0 + head) * p.P_max + part) * D; });
 }
 
-// Mixed block sizes ("vLLM 推理引擎源码级拆解" §1.3: 8, 16 or 32 tokens per
+// Mixed block sizes ("vLLM 0.5 深度拆解" §1.3: 8, 16 or 32 tokens per
 // block, chosen per request).  The pool is kept in pages of p.bs tokens, laid
 // out like a pool of p.bs-token blocks; a block of bs_s = seq_bs[s] tokens is
 // bs_s / p.bs consecutive pages, and table entries give its first page.  So

@@ -214,8 +214,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         }
     };
     // stage st is seen whole by every live column when st * kStageTok +
-    // kStageTok - 1 <= vis
-    const int nfull = vis >= kStageTok - 1 ? min(nstage, (vis + 1) / kStageTok) : 0;
+    // kStageTok - 1 <= vis.  A wave with no live column (nq == 0, the tail
+    // of a ragged chunk) consumes no tile and only passes the barriers; its
+    // vis is still INT_MAX, so the count is taken in 64 bits.
+    const int nfull =
+        vis >= kStageTok - 1 ? (int)min64(nstage, ((int64_t)vis + 1) / kStageTok) : 0;
     run_stages(0, nfull, std::false_type{});
     run_stages(nfull, nstage, std::true_type{});
 

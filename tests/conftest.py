@@ -25,3 +25,15 @@ def gpu_available() -> bool:
 def orc():
     import oracle
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst |gpu - oracle| / bound per test file of the GPU parity tests."""
+    try:
+        from gpu_case import RATIOS
+    except Exception:
+        return
+    if RATIOS:
+        terminalreporter.write_sep("-", "worst err/bound per file")
+        for f in sorted(RATIOS):
+            terminalreporter.write_line("%s: %.4f" % (f, RATIOS[f]))

@@ -67,7 +67,7 @@ def relabel(k_cache, v_cache, tables, rng):
 
 def build_mixed_pool(Ks, Vs, seq_bs, page, *, dtype, rng=None, spare_groups=2):
     """A pool of `page`-token pages where sequence s has blocks of seq_bs[s]
-    tokens, each seq_bs[s] / page consecutive pages ("vLLM 推理引擎源码级拆解"
+    tokens, each seq_bs[s] / page consecutive pages ("vLLM 0.5 深度拆解"
     §1.3 block sizes per request; pages are this library's layout for them).
     Each block is placed in its own piece of a shuffled 32-token group of
     pages, and its tokens are copied with one slice into the pool seen as

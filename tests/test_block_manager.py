@@ -44,6 +44,72 @@ def test_library_block_tables_from_the_pages(pkv):
         assert bm.block_table(i).tolist() == list(range(first, first + case["blocks"]))
 
 
+class _ModelOps:
+    """The model behind the calls the library's binding offers."""
+
+    def __init__(self, nb, bs):
+        self.m = BlockModel(nb, bs, prefix_cache=True)
+
+    def add(self, seq, toks):
+        try:
+            slots, cached = self.m.add_sequence(seq, toks)
+        except NoBlocks:
+            return None
+        return self.m.tables[seq], cached
+
+    def free(self, seq):
+        self.m.free_sequence(seq)
+
+
+class _LibOps:
+    def __init__(self, pkv, nb, bs):
+        self.pkv = pkv
+        self.bm = pkv.BlockManager(nb, bs, prefix_cache=True)
+
+    def add(self, seq, toks):
+        try:
+            _, cached = self.bm.add_sequence(seq, np.asarray(toks))
+        except self.pkv.PagedKVError as e:
+            assert e.status == -8
+            return None
+        return self.bm.block_table(seq).tolist(), cached
+
+    def free(self, seq):
+        self.bm.free(seq)
+
+
+def _lru_script(ops):
+    """Cached blocks that no table references are reclaimed least recently
+    used first ("vLLM 推理引擎源码级拆解" §4.2), after the free list is empty.
+    Expected tables written by hand.  The release order C, A, B, then a
+    prefix hit on A and A's release again, leaves the reclaim queue as
+    (C, B, A).  Lowest-id-first would evict A, first-release-first C then A,
+    most-recent-first A: only least-recently-used gives C, then B, with A
+    still cached."""
+    A, B, C = [0, 1, 2, 3], [10, 11, 12, 13], [20, 21, 22, 23]   # sequences 0, 1, 2
+    assert ops.add(0, A) == ([0], 0)
+    assert ops.add(1, B) == ([1], 0)
+    assert ops.add(2, C) == ([2], 0)
+    ops.free(2)
+    ops.free(0)
+    ops.free(1)                               # reclaim queue: 2, 0, 1
+    assert ops.add(3, A) == ([0], 4)         # prefix hit: block 0 leaves the queue
+    ops.free(3)                              # and rejoins it last: 2, 1, 0
+    assert ops.add(4, list(range(30, 38))) == ([3, 4], 0)   # free blocks come first
+    assert ops.add(5, [40, 41, 42, 43]) == ([2], 0)         # C's block, used longest ago
+    assert ops.add(6, [50, 51, 52, 53]) == ([1], 0)         # then B's
+    assert ops.add(7, A) == ([0], 4)          # A's block is still cached
+    assert ops.add(8, C) is None              # C's prefix is gone and the pool is full
+
+
+def test_model_reclaims_least_recently_used_cached_block():
+    _lru_script(_ModelOps(5, 4))
+
+
+def test_library_reclaims_least_recently_used_cached_block(pkv):
+    _lru_script(_LibOps(pkv, 5, 4))
+
+
 def check_invariants(m: BlockModel):
     # reference counts are the number of table entries naming a block
     count = [0] * m.NB

@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_361_amd as pkv
 import workloads
-from gpu_case import TOL, from_dev, half_ulp, to_dev
+from gpu_case import assert_within, bound, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -159,7 +159,7 @@ def test_block_manager_drives_decode():
                                        max_seq_len=int(lens.max()), partition_size=P)
         torch.cuda.synchronize()
         o = from_dev(out)
-        assert np.all(np.abs(o - ref) <= TOL[dtype] + half_ulp(ref, dtype))
+        assert_within(o, ref, bound(ref, dtype, dtype))
 
 
 def test_swap_round_trip_bit_exact():

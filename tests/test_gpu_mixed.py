@@ -1,5 +1,5 @@
 """Mixed block sizes on the GPU against the oracle: sequences with 8-, 16-
-and 32-token blocks over one pool of pages ("vLLM 推理引擎源码级拆解" §1.3
+and 32-token blocks over one pool of pages ("vLLM 0.5 深度拆解" §1.3
 picks the block size per request; a block is consecutive pages, this
 library's layout for them).  Everything goes through the C ABI."""
 import numpy as np
@@ -9,7 +9,7 @@ import torch
 import oracle
 import paged_kv_cache_361_amd as pkv
 import workloads
-from gpu_case import TOL, DevCase, from_dev, half_ulp, oracle_caches
+from gpu_case import TOL, DevCase, assert_within, bound, from_dev, oracle_caches
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +52,8 @@ def check(mc, out, ref, rows=None):
         S, Hq, D = ref.shape
         out = out.reshape(S * Hq, D)[rows]
         ref = ref.reshape(S * Hq, D)[rows]
-    assert np.isfinite(out).all(), "non-finite GPU output"
-    err = np.abs(out - ref) - (TOL[c.cache_dtype] + half_ulp(ref, c.q_dtype))
-    print("%s: max excess %.3g" % (c.name, float(err.max())), flush=True)
-    assert np.all(err <= 0), float(err.max())
+    ratio = assert_within(out, ref, bound(ref, c.cache_dtype, c.q_dtype))
+    print("%s: worst err/bound %.3g" % (c.name, ratio), flush=True)
 
 
 def random_sizes(choices):

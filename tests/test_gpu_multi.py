@@ -9,7 +9,8 @@ import torch
 import oracle
 import paged_kv_cache_361_amd as pkv
 import workloads
-from gpu_case import TOL, DevCase, from_dev, half_ulp, oracle_caches, to_dev
+from gpu_case import (TOL, DevCase, assert_within, bound, from_dev, oracle_caches,
+                      out_rounding, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,13 +58,10 @@ def check(mc, out, ref, rows=None):
         TQ, Hq, D = ref.shape
         out = out.reshape(TQ * Hq, D)[rows]
         ref = ref.reshape(TQ * Hq, D)[rows]
-    assert np.isfinite(out).all(), "non-finite GPU output"
-    # short contexts average few values, so |out| can exceed 1: allow the
-    # output's own rounding on top of the tolerance
-    bound = TOL[c.cache_dtype] + half_ulp(ref, c.q_dtype)
-    err = np.abs(out - ref) - bound
-    print("%s: max excess %.3g" % (c.name, float(err.max())), flush=True)
-    assert np.all(err <= 0), float(err.max())
+    # short contexts average few values, so |out| can exceed 1: there the
+    # output's own rounding is allowed on top of the tolerance
+    ratio = assert_within(out, ref, bound(ref, c.cache_dtype, c.q_dtype))
+    print("%s: worst err/bound %.3g" % (c.name, ratio), flush=True)
 
 
 def ragged(S, lo, hi, seed, dtype="bf16", cache="bf16", Hq=32, Hkv=8, D=128, bs=16,
@@ -188,7 +186,7 @@ def test_split_workspace_reused_by_a_smaller_batch():
     ref_unsplit, _ = run_multi(small, 0, d=d)
     c = small.case
     assert np.all(np.abs(out_small - ref_unsplit) <= 2 * TOL[c.cache_dtype] +
-                  2 * half_ulp(ref_unsplit, c.q_dtype))
+                  2 * out_rounding(ref_unsplit, c.q_dtype))
 
 
 def test_split_spec_verify_workload_full():
@@ -277,7 +275,8 @@ def test_balanced_verify_workspace_reused_by_a_smaller_batch():
     check(small, out_small, oracle_multi(small))
     split, _ = run_multi(small, 64, d=d)
     c = small.case
-    assert np.all(np.abs(out_small - split) <= 2 * TOL[c.cache_dtype] + 2 * half_ulp(split, c.q_dtype))
+    assert np.all(np.abs(out_small - split) <= 2 * TOL[c.cache_dtype] +
+                  2 * out_rounding(split, c.q_dtype))
 
 
 def test_balanced_spec_verify_workload_full():

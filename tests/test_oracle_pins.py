@@ -131,14 +131,19 @@ def test_constant_values_are_returned(orc):
 
 
 def test_two_tokens_closed_form(orc):
-    """L=2: out = v0 + sigmoid(z1 - z0) (v1 - v0) with z computed by hand."""
+    """L=2 with unequal scores: out = v0 + sigmoid(z1 - z0) (v1 - v0).
+
+    By hand: z0 = 2 * (0.5*1 + 0.75*0) = 1 and z1 = 2 * (0.5*0 + 0.75*2) = 3,
+    so the second token's weight is sigmoid(2) = 0.8807970779778823.  A
+    dropped scale gives sigmoid(1) = 0.73, swapped scores sigmoid(-2) =
+    0.12, and query components paired with the wrong key components
+    (z0 = 1.5, z1 = 2) sigmoid(0.5) = 0.62."""
     K = np.array([[[1.0, 0.0]], [[0.0, 2.0]]], np.float32)   # [2,1,2]
     V = np.array([[[3.0, -1.0]], [[-2.0, 5.0]]], np.float32)
-    q = np.array([[0.5, 0.25]], np.float32)
+    q = np.array([[0.5, 0.75]], np.float32)
     out = _single_seq(orc, K, V, q, bs=8, scale=2.0)[0]
-    z0, z1 = 2.0 * 0.5, 2.0 * 0.5
-    w1 = 1.0 / (1.0 + math.exp(z0 - z1))
-    expect = np.array([3.0 + w1 * (-5.0), -1.0 + w1 * 6.0])
+    w1 = 0.8807970779778823                                  # 1 / (1 + e^-2)
+    expect = np.array([3.0 + w1 * (-5.0), -1.0 + w1 * 6.0])   # v0 + w1 (v1 - v0)
     np.testing.assert_allclose(out, expect, rtol=0, atol=1e-15)
 
 

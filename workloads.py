@@ -249,7 +249,7 @@ def make_case(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, *,
 # --- mixed block sizes ---------------------------------------------------
 
 def block_size_for_length(L: int) -> int:
-    """Tokens per block by expected length, the thresholds of "vLLM 推理引擎源码级拆解"
+    """Tokens per block by expected length, the thresholds of "vLLM 0.5 深度拆解"
     §1.3 (short < 128: 8; medium < 2048: 16; long: 32); here the length
     itself stands in for the estimate."""
     return 8 if L < 128 else (16 if L < 2048 else 32)
