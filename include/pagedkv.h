@@ -59,7 +59,8 @@ typedef enum {
     PKV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
     PKV_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
     PKV_ERR_HIP = -7,         /* the HIP runtime reported a launch error */
-    PKV_ERR_NO_BLOCKS = -8    /* block manager: the pool has no block to give */
+    PKV_ERR_NO_BLOCKS = -8,   /* block manager: the pool has no block to give */
+    PKV_ERR_SCRATCH = -9      /* the call needs more than the fixed scratch array */
 } pkv_status;
 
 typedef enum {
@@ -211,6 +212,46 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
                                float v_scale, int32_t partition_size,
                                void* workspace, size_t workspace_bytes,
                                int32_t algo, hipStream_t stream);
+
+/*
+ * pkv_paged_attention_decode_noalloc - for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the balanced split of
+ * pkv_paged_attention_decode and its pkv_paged_attention_reduce in one
+ * call, with the workspace taken from a fixed array inside the library
+ * instead of from the caller.
+ *
+ * Arguments, what is computed and the errors are those of
+ * pkv_paged_attention_decode with partition_size = PKV_PARTITION_BALANCED
+ * and algo = PKV_ALGO_MFMA (f16/bf16 queries; f16/bf16/fp8 caches; head_dim
+ * 64 or 128; num_q_heads / num_kv_heads <= 16; num_seqs <= 8192), followed
+ * by the reduce on the same stream; `out` is complete when both kernels are
+ * done.  The results equal those of that decode + reduce pair bit for bit.
+ *
+ * The array is 64 MiB of device memory per GPU the library runs on, held
+ * until the process ends.  It needs, for a grid of nW = one wavefront per
+ * SIMD (1024 on MI355X), 256 B + 4 (num_seqs + 1) B rounded up to 256, then
+ * 2 (5 nW + 8) G entries of (head_dim + 2) floats (G = num_q_heads /
+ * num_kv_heads): about 21 MB at G = 4 and 43 MB at G = 8 for head_dim 128.
+ * A call that needs more returns PKV_ERR_SCRATCH with nothing enqueued.
+ * The call allocates and frees nothing: the array's device address is
+ * looked up once per device (PKV_ERR_HIP if HIP cannot give it).
+ *
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind; no call needs it cleared (the balanced chunk counter takes over
+ * whatever it finds, and the reduce returns it to zero).  Calls that
+ * overlap in time on one GPU, e.g. from two streams, race on the array and
+ * give wrong results: serialise them.
+ */
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, pkv_dtype q_dtype,
+                                       const void* k_cache, const void* v_cache,
+                                       pkv_dtype cache_dtype, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks,
+                                       int32_t max_seq_len, float scale, float k_scale,
+                                       float v_scale, hipStream_t stream);
 
 /*
  * pkv_paged_attention_decode_mixed - decode over a pool whose sequences use

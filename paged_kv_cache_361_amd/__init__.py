@@ -70,6 +70,9 @@ def _load():
                                                I32, I32, I32, I32, F, F, F, I32, P, SZ,
                                                I32, P]
     lib.pkv_paged_attention_decode.restype = I
+    lib.pkv_paged_attention_decode_noalloc.argtypes = [P, P, I, P, P, I, P, I32, P, I32, I32,
+                                                       I32, I32, I32, I32, I32, F, F, F, P]
+    lib.pkv_paged_attention_decode_noalloc.restype = I
     lib.pkv_paged_attention_multi.argtypes = [P, P, I, P, P, I, P, I32, P, P, I32, I32, I32,
                                               I32, I32, I32, I32, I32, F, F, F, I32, P, SZ,
                                               P]
@@ -186,6 +189,25 @@ def paged_attention_decode(out: torch.Tensor, query: torch.Tensor, k_cache: torc
         float(v_scale), int(partition_size), _ptr(workspace), ws_bytes, ALGO[algo],
         _stream(stream))
     _check("pkv_paged_attention_decode", rc)
+
+
+def paged_attention_decode_noalloc(out: torch.Tensor, query: torch.Tensor,
+                                   k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                   block_tables: torch.Tensor, seq_lens: torch.Tensor, *,
+                                   scale: float, max_seq_len: int, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, stream=None) -> None:
+    """The balanced-split decode and its reduce in one call, with the
+    workspace in the library's own fixed device array (no allocation);
+    arguments as paged_attention_decode.  Calls on one GPU must not overlap
+    in time."""
+    S, Hq, D = query.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    rc = _load().pkv_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(v_cache),
+        _dtype_code(k_cache), _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        S, Hq, Hkv, D, bs, NB, int(max_seq_len), float(scale), float(k_scale),
+        float(v_scale), _stream(stream))
+    _check("pkv_paged_attention_decode_noalloc", rc)
 
 
 def paged_attention_decode_mixed(out: torch.Tensor, query: torch.Tensor,

@@ -163,6 +163,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case PKV_ERR_HIP: return "HIP launch error";
     case PKV_ERR_NO_BLOCKS: return "no free block in the pool";
+    case PKV_ERR_SCRATCH: return "the call needs more than the library's fixed scratch array";
     default: return "unknown status";
     }
 }
@@ -504,17 +505,20 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
     return w.bytes;
 }
 
-int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
-                               const void* k_cache, const void* v_cache,
-                               pkv_dtype cache_dtype, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                               int32_t num_seqs, int32_t num_q_heads,
-                               int32_t num_kv_heads, int32_t head_dim,
-                               int32_t block_size, int32_t num_blocks,
-                               int32_t max_seq_len, float scale, float k_scale,
-                               float v_scale, int32_t partition_size,
-                               void* workspace, size_t workspace_bytes,
-                               int32_t algo, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks the arguments common to the decode entry points and fills the
+// parameter block (everything but the workspace pieces).  Returns a
+// negative status, with nothing enqueued, on a bad argument.
+int prepare_decode(void* out, const void* query, int q_dtype, const void* k_cache,
+                   const void* v_cache, int cache_dtype, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t num_blocks, int32_t max_seq_len, float scale,
+                   float k_scale, float v_scale, int32_t partition_size, int32_t algo,
+                   DecodeParams& p) {
     if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
     if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -534,7 +538,6 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
         ((uintptr_t)block_tables & 3u) || ((uintptr_t)seq_lens & 3u))
         return PKV_ERR_ALIGN;
 
-    DecodeParams p;
     p.out = out;
     p.q = query;
     p.k = k_cache;
@@ -567,6 +570,78 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    return PKV_OK;
+}
+
+// The balanced split's own limits: matrix-core types, the batch held in
+// LDS, tile counts 32-bit on the device.
+int balanced_supported(int q_dtype, int cache_dtype, const DecodeParams& p) {
+    const int64_t tiles = (int64_t)p.S * p.Hkv * ((p.len_cap + 15) / 16);
+    if (tiles > ((int64_t)1 << 31) - 1) return PKV_ERR_SHAPE;
+    if (!decode_mfma_supported(q_dtype, cache_dtype, p.D, p.G) || p.S > kBalancedMaxSeqs)
+        return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+// ---- the decode call that allocates nothing --------------------------------
+//
+// Its workspace is `scratch`, one file-scope device array of kScratchBytes.
+// HIP gives each GPU that loads the library its own copy at its own
+// address, held until the process ends.  In host code the array's name is
+// only a stand-in for the symbol: the device address of a GPU's copy comes
+// from hipGetSymbolAddress, asked once per device with that device current
+// and kept in g_scratch, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::atomic<char*> g_scratch[kMaxDevices];
+
+// This device's copy of `scratch` (nullptr if HIP cannot give it).
+char* scratch_on(int dev) {
+    char* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    void* d = nullptr;
+    if (hipGetSymbolAddress(&d, HIP_SYMBOL(scratch)) != hipSuccess || !d) {
+        (void)hipGetLastError();           // leave no sticky error behind
+        return nullptr;
+    }
+    g_scratch[dev].store((char*)d, std::memory_order_release);
+    return (char*)d;
+}
+
+// The balanced workspace sized for a grid of nW wavefronts (entries for
+// the chunk bound of that grid rather than of the largest one).
+inline size_t balanced_bytes_for_grid(int S, int G, int D, int nW, WsLayout* w) {
+    const size_t n = (size_t)2 * (size_t)max_chunks(nW) * (size_t)G;
+    w->P_max = 0;
+    w->off_pre = 256;
+    w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1), 256);
+    w->off_l = w->off_m + round_up(n * 4, 256);
+    w->off_o = w->off_l + round_up(n * 4, 256);
+    w->bytes = w->off_o + n * (size_t)D * 4;
+    return w->bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
+                               const void* k_cache, const void* v_cache,
+                               pkv_dtype cache_dtype, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_seq_len, float scale, float k_scale,
+                               float v_scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes,
+                               int32_t algo, hipStream_t stream) {
+    DecodeParams p;
+    const int rc = prepare_decode(out, query, q_dtype, k_cache, v_cache, cache_dtype,
+                                  block_tables, max_blocks_per_seq, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                  max_seq_len, scale, k_scale, v_scale, partition_size, algo, p);
+    if (rc != PKV_OK) return rc;
     const bool balanced = partition_size == PKV_PARTITION_BALANCED;
     if (partition_size != 0) {
         WsLayout w;
@@ -589,11 +664,9 @@ int pkv_paged_attention_decode(void* out, const void* query, pkv_dtype q_dtype,
     const bool mfma_ok = decode_mfma_supported(q_dtype, cache_dtype, head_dim, p.G);
     const bool valu_ok = decode_valu_supported(q_dtype, cache_dtype, head_dim, p.G);
     if (balanced) {
-        // Tile counts are 32-bit on the device.
-        const int64_t tiles = (int64_t)num_seqs * num_kv_heads * ((p.len_cap + 15) / 16);
-        if (tiles > ((int64_t)1 << 31) - 1) return PKV_ERR_SHAPE;
-        if (algo == PKV_ALGO_VALU || !mfma_ok || num_seqs > kBalancedMaxSeqs)
-            return PKV_ERR_UNSUPPORTED;
+        const int bal = balanced_supported(q_dtype, cache_dtype, p);
+        if (bal != PKV_OK) return bal;
+        if (algo == PKV_ALGO_VALU) return PKV_ERR_UNSUPPORTED;
         p.P = 0;
         p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size);
         p.epoch = next_call_number();
@@ -649,6 +722,62 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* works
     p.S_seq = num_seqs;
     if (balanced) return launch_status(launch_reduce_balanced(out_dtype, p, stream));
     return launch_status(launch_reduce(out_dtype, p, stream));
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, pkv_dtype q_dtype,
+                                       const void* k_cache, const void* v_cache,
+                                       pkv_dtype cache_dtype, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks,
+                                       int32_t max_seq_len, float scale, float k_scale,
+                                       float v_scale, hipStream_t stream) {
+    DecodeParams p;
+    int rc = prepare_decode(out, query, q_dtype, k_cache, v_cache, cache_dtype, block_tables,
+                            max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                            head_dim, block_size, num_blocks, max_seq_len, scale, k_scale,
+                            v_scale, PKV_PARTITION_BALANCED, PKV_ALGO_MFMA, p);
+    if (rc != PKV_OK) return rc;
+    rc = balanced_supported(q_dtype, cache_dtype, p);
+    if (rc != PKV_OK) return rc;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_HIP;
+    p.P = 0;
+    p.P_max = 1;
+    p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size);
+    WsLayout w;
+    if (balanced_bytes_for_grid(num_seqs, p.G, head_dim, p.nW, &w) > kScratchBytes)
+        return PKV_ERR_SCRATCH;
+    char* ws = scratch_on(dev);
+    if (!ws) return PKV_ERR_HIP;
+    p.ws_hdr = (int32_t*)ws;
+    p.ws_pre = (int32_t*)(ws + w.off_pre);
+    p.ws_m = (float*)(ws + w.off_m);
+    p.ws_l = (float*)(ws + w.off_l);
+    p.ws_o = (float*)(ws + w.off_o);
+    p.epoch = next_call_number();
+    hipError_t e = launch_decode_balanced(q_dtype, cache_dtype, p, stream);
+    if (e != hipSuccess) return launch_status(e);
+    // the reduce of the same split, on the same pieces of the array
+    ReduceParams r;
+    r.out = out;
+    r.ws_hdr = p.ws_hdr;
+    r.ws_pre = p.ws_pre;
+    r.ws_m = p.ws_m;
+    r.ws_l = p.ws_l;
+    r.ws_o = p.ws_o;
+    r.lens = seq_lens;
+    r.S = num_seqs;
+    r.Hq = num_q_heads;
+    r.Hkv = num_kv_heads;
+    r.D = head_dim;
+    r.P = 0;
+    r.P_max = 0;
+    r.len_cap = max_seq_len;
+    r.q_start = nullptr;
+    r.S_seq = num_seqs;
+    return launch_status(launch_reduce_balanced(q_dtype, r, stream));
 }
 
 }  // extern "C"
