@@ -110,17 +110,19 @@ def test_spec_verify_workload_full():
 
 
 def test_chunked_prefill_workload_sampled_rows():
-    """Chunks of 512 new tokens after 512..3072 cached ones: the oracle on a
-    sample of rows (first, last and random query tokens of every sequence)."""
+    """Chunks of 512 new tokens after 512..3072 cached ones: the oracle on
+    every query head of every 8th query token, the last ones and random
+    ones, in every sequence."""
     mc = workloads.chunked_prefill()
     c = mc.case
     rng = np.random.default_rng(540)
     toks = set()
     for s in range(c.S):
         a, b = int(mc.query_start[s]), int(mc.query_start[s + 1])
-        toks.update([a, b - 1])
-        toks.update(rng.integers(a, b, size=6).tolist())
-    rows = sorted(t * c.Hq + hq for t in toks for hq in (0, 3, 4, 17, 31))
+        toks.update(range(a, b, 8))
+        toks.update([a + 1, b - 1])
+        toks.update(rng.integers(a, b, size=8).tolist())
+    rows = sorted(t * c.Hq + hq for t in toks for hq in range(c.Hq))
     out, _ = run_multi(mc)
     check(mc, out, oracle_multi(mc, rows), rows)
 
@@ -195,32 +197,28 @@ def test_split_spec_verify_workload_full():
     check(mc, out, oracle_multi(mc))
 
 
-def test_wide_rows_equal_single_token_calls():
-    """Rows of a long query run (several column blocks per wavefront) equal,
-    bit for bit, one-token calls over each token's own prefix: the tiles a
-    column does not see add exact zeros."""
+def test_rows_unchanged_by_later_tokens_of_the_chunk():
+    """Causality inside a long query run: the rows of a chunk equal, bit for
+    bit, the same rows of a call whose chunk goes on for 8 more tokens (the
+    later tokens' keys reach the earlier rows' tiles only as exact zeros).
+    Both calls go through the LDS-staged kernel (chunks of 22..40 tokens)."""
     mc = ragged(3, 30, 40, 600, lmin=60, lmax=300)
     c = mc.case
-    out, d = run_multi(mc)
-    rng = np.random.default_rng(601)
-    checked = 0
-    for s in range(c.S):
-        a, b = int(mc.query_start[s]), int(mc.query_start[s + 1])
-        L, Qn = int(c.seq_lens[s]), b - a
-        for i in sorted(set(rng.integers(0, Qn, size=5).tolist()) | {0, Qn - 1}):
-            pos = L - Qn + i
-            if pos < 0:
-                continue
-            q1 = torch.from_numpy(np.ascontiguousarray(mc.query[a + i:a + i + 1]).view(np.int16)).view(torch.bfloat16).cuda()
-            o1 = torch.full_like(q1, float("nan"))
-            pkv.paged_attention_multi(o1, q1, d.k_cache, d.v_cache, d.tables[s:s + 1].contiguous(),
-                                      torch.tensor([pos + 1], dtype=torch.int32, device="cuda"),
-                                      torch.tensor([0, 1], dtype=torch.int32, device="cuda"),
-                                      scale=c.scale, max_seq_len=c.max_seq_len, max_query_len=1)
-            torch.cuda.synchronize()
-            assert np.array_equal(from_dev(o1)[0], out[a + i]), (s, i)
-            checked += 1
-    assert checked >= 6
+    full, d = run_multi(mc)
+    cut = 8
+    qn = np.diff(mc.query_start)
+    keep = qn - cut
+    qs = np.concatenate([[0], np.cumsum(keep)]).astype(np.int32)
+    rows = np.concatenate([np.arange(mc.query_start[s], mc.query_start[s] + keep[s])
+                           for s in range(c.S)])
+    q = to_dev(np.ascontiguousarray(mc.query[rows]), c.q_dtype)
+    out = torch.full(q.shape, float("nan"), dtype=q.dtype, device="cuda")
+    lens = torch.from_numpy((c.seq_lens - cut).astype(np.int32)).cuda()
+    pkv.paged_attention_multi(out, q, d.k_cache, d.v_cache, d.tables, lens,
+                              torch.from_numpy(qs).cuda(), scale=c.scale,
+                              max_seq_len=c.max_seq_len, max_query_len=int(keep.max()))
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(out), full[rows])
 
 
 # ---- balanced split (verification: at most 16 / G query tokens) -------------
