@@ -239,9 +239,10 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
     // long query runs without a split: 2 or 4 column blocks per wavefront
     const int nb = partition_size != 0 || max_query_len <= qpg ? 1
                    : (max_query_len >= 4 * qpg ? 4 : 2);
-    // longer runs of 16-bit queries and caches: the LDS-staged kernel
+    // runs of at least 64 / G tokens (two wavefronts' rows) of 16-bit
+    // queries and caches: the LDS-staged kernel
     const int ptok = prefill_tokens_per_group(G);
-    const bool staged = partition_size == 0 && 2 * max_query_len >= ptok &&
+    const bool staged = partition_size == 0 && G * max_query_len >= 64 &&
                         prefill_supported(q_dtype, cache_dtype, head_dim, G);
     const int64_t groups =
         staged ? (max_query_len + (int64_t)ptok - 1) / ptok

@@ -7,23 +7,27 @@
 // the block table; a token whose position is negative gets a zero row.
 //
 // Work layout.
-//   - A workgroup serves one (sequence, KV head) and 128 / G consecutive
-//     query tokens; each of its 4 waves owns 32 query rows, the (token,
-//     head) pairs of 32 / G tokens (GQA: the G heads of a token share the
-//     KV head, so every K/V byte a wave reads feeds G rows).
+//   - A workgroup (one per CU, 8 waves, two per SIMD) serves one (sequence,
+//     KV head) and 256 / G consecutive query tokens; each wave owns 32
+//     query rows, the (token, head) pairs of 32 / G tokens (GQA: the G
+//     heads of a token share the KV head, so every K/V byte a wave reads
+//     feeds G rows).
 //   - The context the workgroup's last token sees is walked in stages of 64
-//     keys.  A stage's K and V rows (through the block table; rows past the
-//     context read zeros) go to one of two LDS buffers, one barrier per
-//     stage; the next stage's rows are in flight during the current stage's
-//     arithmetic.  K is loaded straight into LDS by buffer loads with the
-//     LDS as destination (unpadded rows, 16-byte units XOR-swizzled by row);
-//     V passes through registers and is stored transposed (one LDS row per
-//     dimension d, the stage's keys along it), so that each lane's value
-//     operand of the PV product is one 16-byte LDS read.
+//     keys, each wave moving 8 of them (within one block for every block
+//     size).  K and V go straight from memory into one of three LDS buffers
+//     (buffer loads with the LDS as destination, no registers involved):
+//     stage st + 2 is requested while stage st is computed, so a stage has
+//     two stages of arithmetic to arrive.  One barrier per stage.
+//   - Rows are stored as in memory (no padding), their 16-byte units
+//     XOR-swizzled by row against bank conflicts.  V^T operands come from
+//     the gfx950 LDS transpose read.
 //   - Stages all of whose keys every row of a wave sees run in a loop
-//     without the causal mask, the rest in a second loop with it.
-//   - (Sequence, KV head) pairs are dealt to the XCDs round robin, all the
-//     groups of a pair on one XCD, longest contexts first.
+//     without the causal mask, the rest in a second loop with it (one loop
+//     holding both made the register allocator duplicate the accumulators).
+//   - (Sequence, KV head) pairs are dealt to the XCDs round robin, an XCD
+//     taking its pairs one after the other with all their groups together,
+//     so the groups reading a stage share the XCD's L2.
+//   - The block table entries the workgroup needs are cached in LDS.
 //
 // Per wave and 32-key sub-tile (v_mfma_f32_32x32x16_{bf16,f16}):
 //   S^T[key][row] = K[32 x D] Q^T[D x 32]: A = K rows from LDS (lane%32 =
@@ -34,19 +38,17 @@
 //   The result lands with lane%32 = query row and register r = key
 //     8 (r/4) + 4 g + r%4, which is exactly the B layout (P^T) of
 //   O^T[d][row] += V^T[d][keys] P^T[keys][row]: lane half g supplies keys
-//     {4g..4g+3, 8+4g..8+4g+3} of each 16-key step; the V^T rows keep each
-//     16-key group's quads in the order (0, 2, 1, 3), so those 8 keys are
-//     16 contiguous bytes.
+//     {4g..4g+3, 8+4g..8+4g+3} of each 16-key step, two transpose reads of
+//     4 consecutive key rows each.
 //   Every value of a lane's accumulators belongs to its own query row, so
 //   the softmax's rescale is a per-lane multiply; the row's max and sum
 //   combine the two lanes of a row (l and l ^ 32) with one lane swap.
 //
-// Softmax: base-2 scores (scale * log2 e folded), lazy rescale (the
-// reference max moves only when exceeded by more than 8), weights fed to
-// the PV product as bf16 hi + lo (~16 significant bits) for bf16 queries
+// Softmax: base-2 scores (scale * log2 e folded into one FMA), lazy rescale
+// (the reference max moves only when exceeded by more than 8), weights fed
+// to the PV product as bf16 hi + lo (~16 significant bits) for bf16 queries
 // and as f16 for f16 queries, so the only 8-bit rounding left is the stored
-// output.  Causal masking is applied only on the sub-tiles that reach past
-// the first position any of the wave's rows sees.
+// output.
 #include "tile_mfma.hpp"
 
 namespace pkv {
@@ -55,6 +57,7 @@ namespace {
 using namespace mfma;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <class Q>
 struct Mma32;
@@ -62,6 +65,7 @@ template <>
 struct Mma32<BF16> {
     typedef __bf16 T;
     typedef bf16x8 v8;
+    typedef bf16x4 v4;
     static constexpr bool kSplitP = true;
     __device__ static inline f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -71,78 +75,111 @@ template <>
 struct Mma32<F16> {
     typedef _Float16 T;
     typedef f16x8 v8;
+    typedef f16x4 v4;
     static constexpr bool kSplitP = false;
     __device__ static inline f32x16 mma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
 };
 
-constexpr int kWaves = 4;
-constexpr int kRows = 32;     // query rows per wave
-constexpr int kStage = 64;    // keys per LDS stage
-constexpr int kSub = 32;      // keys per matrix-core sub-tile
+constexpr int kWaves = 8;
+constexpr int kRows = 32;      // query rows per wave
+constexpr int kStage = 64;     // keys per LDS stage
+constexpr int kSub = 32;       // keys per matrix-core sub-tile
+constexpr int kBufs = 3;       // stage buffers in LDS
+constexpr int kTbl = 2048;     // block table entries cached in LDS
 
 template <int D>
 struct Shape {
     static constexpr int kRow = 2 * D;                 // bytes of one head's K or V row
-    static constexpr int kK = kStage * kRow;           // K of a stage (rows swizzled, unpadded)
-    static constexpr int kVStride = 2 * kStage + 16;   // V^T rows (one per d), padded
-    static constexpr int kV = D * kVStride;            // V^T of a stage
-    static constexpr int kBuf = kK + kV;
-    static constexpr int kLds = 2 * kBuf;              // double buffer
+    static constexpr int kK = kStage * kRow;           // K of a stage
+    static constexpr int kBuf = 2 * kK;                // K and V of a stage
+    static constexpr int kLds = kBufs * kBuf + kTbl * 4;
     static constexpr int kChunks = kRow / 16;          // 16-byte pieces of a row
-    // keys of one wave-wide 16-byte load (64 lanes): 4 at D = 128, 8 at D = 64
-    static constexpr int kKpl = 64 / kChunks;
-    // V rows each thread moves per stage (one 16-byte piece of each, the
-    // same piece): 4 at D = 128, 2 at D = 64
-    static constexpr int kKpt = kStage * kChunks / (64 * kWaves);
+    static constexpr int kKpl = 64 / kChunks;          // keys of one wave-wide load
+    static constexpr int kKpw = kStage / kWaves;       // keys each wave moves per stage
+    static constexpr int kLoads = kKpw / kKpl;         // loads per wave per stage, K (and V)
     static constexpr int kQS = D / 16;                 // QK instructions (16 d each)
     static constexpr int kNT = D / 32;                 // output tiles of 32 d
-    static_assert(kKpt * 64 * kWaves == kStage * kChunks, "stage split");
-    static_assert(kKpt == 2 || kKpt == 4, "a thread's keys lie in one quad");
+    static_assert(kLoads * kKpl == kKpw && kKpw == 8, "a wave's 8 keys in whole loads");
 };
 
-// Two 16-bit values, lo from a and hi from b, taken from the same half of
-// two dwords: half 0 the low halves, half 1 the high halves.
-__device__ inline uint32_t pair16(uint32_t a, uint32_t b, int half) {
-    return half ? (a >> 16) | (b & 0xFFFF0000u) : (a & 0xFFFFu) | (b << 16);
-}
-
-// Byte offset, among a V^T row's 128 key bytes, of key k of a stage.  Each
-// 16-key group is 32 bytes, 16 per lane half g of the value operand, which
-// takes keys {4g..4g+3, 8+4g..8+4g+3}; they are stored in the order
-// (4g, 4g+1, 8+4g, 9+4g, 4g+2, 4g+3, 10+4g, 11+4g), so that the two key
-// pairs (2j, 2j+1) and (8+2j, 9+2j) a thread moves are 8 adjacent bytes.
-// The weights are packed into the other operand in the same order.
-__device__ inline uint32_t vt_key(int k) {
-    const int kk = k & 15, w = kk & 3;
-    const int e = (w >> 1) * 4 + (kk >> 3) * 2 + (w & 1);
-    return (uint32_t)((k >> 4) * 32 + ((kk >> 2) & 1) * 16 + e * 2);
-}
-
-// K rows of a stage buffer are unpadded, their 16-byte units XORed with
-// row % KSW (the units per row, at most 16), so that the rows a score read
-// takes at once fall in distinct banks.
+// K rows of a stage buffer: 16-byte units XORed with row % KSW (the units
+// per row, at most 16), so that the rows a score read takes at once fall in
+// distinct banks.
 template <int ROW>
 constexpr int k_swizzle() { return ROW / 16 < 16 ? ROW / 16 : 16; }
 
-// Byte address of key byte `kb` of V^T row `row` in a stage buffer.  The
-// 16-byte unit is XORed with (row / 8) % 8: the stores of a wave write rows
-// 8 apart (which would all fall in one bank), the value reads of a wave read
-// 8 consecutive rows with one XOR (the row padding keeps those apart).
-template <int STRIDE>
-__device__ inline uint32_t vt_addr(int row, uint32_t kb) {
-    return (uint32_t)row * STRIDE + ((((kb >> 4) ^ ((uint32_t)row >> 3)) & 7u) << 4) + (kb & 15u);
+// V rows: units XORed with 2 (row % 4).  A value read takes 8 bytes from
+// each of 4 consecutive rows at the same columns (the transpose read),
+// which then fall in distinct banks.
+__device__ inline int v_swizzle(int row) { return (row & 3) << 1; }
+
+// s_waitcnt with only a vector-memory count (expcnt and lgkmcnt at their
+// maxima, so neither is waited for).
+template <int N>
+__device__ inline void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0xF70 | N);
 }
 
-// PAIR: 8-token blocks, so the 16 keys a wave loads span two blocks.
-template <class Q, int D, bool PAIR>
+// The value fragments of one 32-key sub-tile: transpose reads (2 per
+// operand; see the address sets in the kernel) from the 8 lane addresses
+// a[ii][rd][par] (flattened), output tile n at byte offset 128 (n / 2).
+// Written out together with their wait, so that the compiler does not take
+// them for reads of the stage loads still in flight into other buffers
+// (it would wait for all of those first).  r[ii][n][rd] flattened.
+template <int NT>
+__device__ inline void read_v_frags(u32x2 (&r)[4 * NT], const uint32_t (&a)[8]);
+template <>
+__device__ inline void read_v_frags<4>(u32x2 (&r)[16], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %18\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %19\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:128\n\t"
+        "ds_read_b64_tr_b16 %6, %17 offset:128\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:128\n\t"
+        "ds_read_b64_tr_b16 %8, %20\n\t"
+        "ds_read_b64_tr_b16 %9, %22\n\t"
+        "ds_read_b64_tr_b16 %10, %21\n\t"
+        "ds_read_b64_tr_b16 %11, %23\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:128\n\t"
+        "ds_read_b64_tr_b16 %13, %22 offset:128\n\t"
+        "ds_read_b64_tr_b16 %14, %21 offset:128\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+template <>
+__device__ inline void read_v_frags<2>(u32x2 (&r)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %10\n\t"
+        "ds_read_b64_tr_b16 %2, %9\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %14\n\t"
+        "ds_read_b64_tr_b16 %6, %13\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+template <class Q, int D>
 __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p) {
     typedef Shape<D> SH;
     typedef Mma32<Q> M;
     typedef typename M::T T;
     typedef typename M::v8 v8;
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    int* tbl_lds = (int*)(lds + kBufs * SH::kBuf);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int c = lane & 31;               // this lane's query row within the wave
@@ -150,21 +187,54 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // workgroup -> (sequence, KV head, group of query tokens).  Workgroups
-    // are dealt to the XCDs in turn (blockIdx % 8).  The (sequence, KV head)
-    // pairs are dealt to the XCDs round robin, so each XCD gets a share of
-    // every sequence's work, and all the groups of a pair run on one XCD,
-    // sharing its L2.  Each XCD takes the groups reading the longest
-    // contexts (the last query tokens) of all its pairs first.
+    // are dealt to the XCDs in turn (blockIdx % 8), and the (sequence, KV
+    // head) pairs round robin to the XCDs (pair % 8), so each XCD gets a
+    // share of every sequence's work.  Within an XCD, workgroup j (the j-th
+    // dispatched there) takes the j-th longest of the XCD's items (pair,
+    // group), by the keys it reads: the longest-first rule for jobs on
+    // identical machines, which keeps the CUs of the XCD busy to about the
+    // same end.  Items of one pair differ by a group's tokens, so a pair's
+    // groups run close together and share the stages in the XCD's L2.
+    // Every workgroup ranks the items itself (at most 512 per XCD, one per
+    // thread); with more, pair by pair, the longest group first.
     const int G = p.G;
     const int tpw = kRows / G;             // query tokens per wave
     const int tpg = kWaves * tpw;          // per workgroup
     const int pairs = p.S * p.Hkv;
-    const int per_xcd = (pairs + 7) / 8;   // pairs per XCD (the last ones short)
     const int xcd = (int)(blockIdx.x % 8);
     const int j = (int)(blockIdx.x / 8);
-    const int pair = (j % per_xcd) * 8 + xcd;
-    const int grp = p.max_groups - 1 - j / per_xcd;
-    if (pair >= pairs || grp < 0) return;  // whole workgroup
+    const int n_items = (pairs > xcd ? (pairs - xcd + 7) / 8 : 0) * p.max_groups;
+    if (j >= n_items) return;              // whole workgroup
+    int item = j;
+    if (n_items <= 64 * kWaves) {
+        int* key = tbl_lds;                // the table's space, free until filled
+        int w = -1;
+        if (tid < n_items) {
+            const int ps = ((tid / p.max_groups) * 8 + xcd) / p.Hkv;
+            const int qn = p.q_start[ps + 1] - p.q_start[ps];
+            const int base = (p.max_groups - 1 - tid % p.max_groups) * tpg;
+            if (base < qn) {
+                const int Ls = min(p.lens[ps], p.len_cap);
+                w = max(0, Ls - qn + min(base + tpg, qn));
+            }
+            key[tid] = w;
+        }
+        __syncthreads();
+        if (tid < n_items) {
+            int rank = 0;
+            for (int k = 0; k < n_items; k++) {
+                const int wk = key[k];
+                rank += (wk > w) | ((wk == w) & (k < tid));
+            }
+            if (rank == j) key[kTbl - 1] = tid;
+        }
+        __syncthreads();
+        item = __builtin_amdgcn_readfirstlane(key[kTbl - 1]);
+        __syncthreads();                   // before the table is filled
+    }
+    const int pair = (item / p.max_groups) * 8 + xcd;
+    const int grp = p.max_groups - 1 - item % p.max_groups;
+    if (pair >= pairs) return;             // whole workgroup
     const int h = pair % p.Hkv;
     const int s = pair / p.Hkv;
     const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[s]);
@@ -213,104 +283,56 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     wlast = __builtin_amdgcn_readfirstlane(wlast);
     wvis = __builtin_amdgcn_readfirstlane(wvis);
 
-    // ---- stage loads ----
-    // A wave moves the 16 consecutive, aligned keys 16 wave .. of a stage:
-    // one block, or two 8-token blocks (PAIR), whose table entries are
-    // wave-uniform, so every load has a scalar buffer descriptor.  Rows at
-    // or past wg_end take an out-of-range offset and read zeros.
-    //   K goes straight to LDS (buffer loads with the LDS as destination):
-    //   load r of the wave covers keys 16 wave + kKpl r .. + kKpl - 1 (one
-    //   block), lane i writing 16 bytes at i * 16 from the load's first row,
-    //   i.e. row i / kChunks, swizzled unit i % kChunks, which holds unit
-    //   (i % kChunks) ^ (row % 8) of the key's row.
-    //   V passes through registers to be transposed: thread (j = lane /
-    //   kChunks, ch = lane % kChunks) moves piece ch of the keys 2j, 2j+1
-    //   and, at head_dim 128, 8+2j, 9+2j of the wave's 16 (load r takes key
-    //   8 (r / 2) + 2j + r % 2, one block per load at head_dim 128).
+    // ---- block table entries in LDS ----
+    // Entries [tb0, tb0 + kTbl) of the sequence's table; a stage whose
+    // blocks pass the end has the next kTbl loaded first (all waves, at a
+    // stage boundary: rare, a 2048-block span).
     const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
+    const int nblk = wg_end > 0 ? ((wg_end - 1) >> bs_shift) + 1 : 0;
+    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
+    int tb0 = 0;
+    auto fill_table = [&](int b0) {
+        for (int i = tid; i < kTbl; i += 64 * kWaves)
+            tbl_lds[i] = b0 + i < nblk ? table[b0 + i] : 0;
+    };
+
+    // ---- stage loads ----
+    // Wave w moves keys 8 w .. 8 w + 7 of a stage (one block: block sizes
+    // are multiples of 8), so its table entry is wave-uniform and every
+    // load has a scalar buffer descriptor.  Load r covers keys 8 w + kKpl r
+    // .. + kKpl - 1, lane i writing 16 bytes at i * 16 from the load's first
+    // row: row i / kChunks, swizzled unit i % kChunks, holding unit
+    // (i % kChunks) ^ swizzle(row) of the key's row.  Rows at or past
+    // wg_end take an out-of-range offset and write zeros.
     const uint32_t pool_row = (uint32_t)p.Hkv * SH::kRow;       // bytes between slots
     const uint32_t blk_bytes = (uint32_t)p.bs * pool_row;
     const uint32_t head_off = (uint32_t)h * SH::kRow;
     const int lj = lane / SH::kChunks;
     const int ch = lane % SH::kChunks;
-    const int last_blk = wg_end > 0 ? (wg_end - 1) >> bs_shift : 0;
-    // the sequence's live table entries, read with buffer loads (a vector
-    // memory access, so waiting for one never waits for LDS traffic)
-    const rsrc_t tbl = make_rsrc((const char*)(p.tables + (size_t)s * p.max_blocks),
-                                 (uint32_t)(last_blk + 1) * 4u);
-    // table entries of the wave's blocks in stage st (requested one stage
-    // before they are used)
-    auto entry = [&](int st, int second) {
-        const int b = min(((st * kStage + 16 * wave) >> bs_shift) + second, last_blk);
-        return (int)Buf<4>::load(tbl, (uint32_t)b * 4u);
-    };
-    auto blk = [&](int e) {
-        const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(e);
-        return b < (uint32_t)p.NB ? b : (uint32_t)p.NB - 1u;
-    };
-    // in-block byte offset of key t (a key of this stage), or out of range
-    auto row_off = [&](int t) {
-        return t < wg_end ? (uint32_t)(t & (p.bs - 1)) * pool_row + head_off : kOOB;
-    };
-    constexpr int kVL = SH::kKpt;          // V loads per thread per stage
-    u32x4 vr[kVL];
-    auto load_stage = [&](int st, int ea, int eb, int buf) {
-        const uint32_t ba = blk(ea);
-        const uint32_t bb = PAIR ? blk(eb) : ba;
-        const rsrc_t rka = make_rsrc((const char*)p.k + (size_t)ba * blk_bytes, blk_bytes);
-        const rsrc_t rkb = make_rsrc((const char*)p.k + (size_t)bb * blk_bytes, blk_bytes);
-        const rsrc_t rva = make_rsrc((const char*)p.v + (size_t)ba * blk_bytes, blk_bytes);
-        const rsrc_t rvb = make_rsrc((const char*)p.v + (size_t)bb * blk_bytes, blk_bytes);
-        const int t0 = st * kStage + 16 * wave;
-        char* kdst = lds + buf * SH::kBuf + 16 * wave * SH::kRow;
+    auto load_stage = [&](int st, int buf) {
+        const int t0 = st * kStage + SH::kKpw * wave;
+        const int e = tbl_lds[min(t0 >> bs_shift, nblk - 1) - tb0];
+        const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane(e);
+        const uint32_t b = b0 < (uint32_t)p.NB ? b0 : (uint32_t)p.NB - 1u;
+        const rsrc_t rk = make_rsrc((const char*)p.k + (size_t)b * blk_bytes, blk_bytes);
+        const rsrc_t rv = make_rsrc((const char*)p.v + (size_t)b * blk_bytes, blk_bytes);
+        char* kdst = lds + buf * SH::kBuf + SH::kKpw * wave * SH::kRow;
+        char* vdst = kdst + SH::kK;
 #pragma unroll
-        for (int r = 0; r < 16 / SH::kKpl; r++) {
-            const int row = r * SH::kKpl + lj;         // within the wave's 16
-            const uint32_t u = (uint32_t)(ch ^ (row & (k_swizzle<SH::kRow>() - 1)));
-            const uint32_t off = row_off(t0 + row);
+        for (int r = 0; r < SH::kLoads; r++) {
+            const int row = SH::kKpw * wave + r * SH::kKpl + lj;   // within the stage
+            const int t = st * kStage + row;
+            const uint32_t off =
+                t < wg_end ? (uint32_t)(t & (p.bs - 1)) * pool_row + head_off : kOOB;
+            const uint32_t uk = (uint32_t)(ch ^ (row & (k_swizzle<SH::kRow>() - 1)));
+            const uint32_t uv = (uint32_t)(ch ^ v_swizzle(row));
+            const int dst = r * SH::kKpl * SH::kRow;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                PAIR && row >= 8 ? rkb : rka,
-                (__attribute__((address_space(3))) void*)(kdst + r * SH::kKpl * SH::kRow), 16,
-                off == kOOB ? kOOB : off + 16u * u, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < kVL; r++) {
-            if constexpr (SH::kKpt == 4) {
-                const int row = 8 * (r >> 1) + 2 * lj + (r & 1);
-                const uint32_t off = row_off(t0 + row);
-                vr[r] = Buf<16>::load(PAIR && r >= 2 ? rvb : rva,
-                                      off == kOOB ? kOOB : off + 16u * (uint32_t)ch);
-            } else {
-                // head_dim 64: keys 2j, 2j+1, j < 8, across both 8-token halves
-                const int row = 2 * lj + r;
-                const uint32_t off = row_off(t0 + row);
-                const uint32_t o = off == kOOB ? kOOB : off + 16u * (uint32_t)ch;
-                if constexpr (PAIR) {
-                    const bool second = row >= 8;
-                    vr[r] = Buf<16>::load(rva, second ? kOOB : o) |
-                            Buf<16>::load(rvb, second ? o : kOOB);
-                } else {
-                    vr[r] = Buf<16>::load(rva, o);
-                }
-            }
-        }
-    };
-    auto store_stage = [&](int buf) {
-        char* vb = lds + buf * SH::kBuf + SH::kK;
-        // V^T: dimension 8 ch + d, this thread's keys side by side
-        const uint32_t kofs = vt_key(16 * wave + 2 * lj);
-#pragma unroll
-        for (int d = 0; d < 8; d++) {
-            char* at = vb + vt_addr<SH::kVStride>(8 * ch + d, kofs);
-            const int w = d >> 1, half = d & 1;
-            if constexpr (SH::kKpt == 4) {
-                u32x2 x;
-                x[0] = pair16(vr[0][w], vr[1][w], half);
-                x[1] = pair16(vr[2][w], vr[3][w], half);
-                *(u32x2*)at = x;
-            } else {
-                *(uint32_t*)at = pair16(vr[0][w], vr[1][w], half);
-            }
+                rk, (__attribute__((address_space(3))) void*)(kdst + dst), 16,
+                off == kOOB ? kOOB : off + 16u * uk, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(vdst + dst), 16,
+                off == kOOB ? kOOB : off + 16u * uv, 0, 0, 0);
         }
     };
 
@@ -322,19 +344,35 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
 
     // Lane-constant LDS addresses of the operand reads, relative to a stage
     // buffer.  K: row c of a sub-tile, unit (D / 16) g + i of the score
-    // step i, swizzled.  V^T: row c of output tile 0, the lane half's 16
-    // bytes of 16-key step ii of sub-tile 0; the unit swizzle (row / 8) % 8
-    // splits into these lane bits (0-1) and a bit 2 that depends only on
-    // the tile n and the sub-tile, which the reads add as a constant.
-    uint32_t ka[SH::kQS], va[2];
+    // step i, swizzled.
+    uint32_t ka[SH::kQS];
 #pragma unroll
     for (int i = 0; i < SH::kQS; i++)
         ka[i] = (uint32_t)(c * SH::kRow) +
                 (uint32_t)((((D / 16) * g + i) ^ (c & (k_swizzle<SH::kRow>() - 1))) << 4);
+    // V^T fragments by transpose reads.  Two reads per operand (rd 0: keys
+    // 4g..4g+3, rd 1: keys 8+4g..8+4g+3 of the 16-key step ii); in lane
+    // group G16 = lane / 16 (half g = G16 / 2, 16 columns from 32 n + 16
+    // (G16 % 2)), lane s = 4 mr + tc addresses key row mr of the four and
+    // columns 4 tc .. 4 tc + 3.  With the swizzle 2 (row % 4) = 2 mr, the
+    // unit's bit 2 is (n % 2) ^ (mr / 2): two lane-constant address sets,
+    // by the parity of the output tile n; the rest is a constant offset.
+    uint32_t va[2][2][2];
+    {
+        const int G16 = lane >> 4, sl = lane & 15, mr = sl >> 2, tc = sl & 3;
 #pragma unroll
-    for (int ii = 0; ii < 2; ii++)
-        va[ii] = (uint32_t)(SH::kK + c * SH::kVStride) +
-                 (uint32_t)((((2 * ii + g) ^ (c >> 3)) & 3) << 4);
+        for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+            for (int rd = 0; rd < 2; rd++)
+#pragma unroll
+                for (int par = 0; par < 2; par++) {
+                    const int row = 16 * ii + 8 * rd + 4 * g + mr;
+                    const int unit = (tc >> 1) + 2 * ((G16 & 1) ^ (mr & 1)) +
+                                     4 * (par ^ (mr >> 1));
+                    va[ii][rd][par] = (uint32_t)(SH::kK + row * SH::kRow + 16 * unit +
+                                                 8 * (tc & 1));
+                }
+    }
 
     // One 32-key sub-tile u of the stage in LDS buffer `base`: scores, the
     // softmax update, the value products.
@@ -348,17 +386,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
 #pragma unroll
         for (int i = 0; i < SH::kQS; i++)
             kf[i] = *(const v8*)(base + ka[i] + u * kSub * SH::kRow);
+        // keep all the reads ahead of the products (otherwise the scheduler
+        // reuses one register tuple and waits for each read in turn)
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 sc = f32x16{};
 #pragma unroll
         for (int i = 0; i < SH::kQS; i++) sc = M::mma(kf[i], qf[i], sc);
-        // the value fragments, in flight during the softmax
+        // the value fragments, read while the score products run
         v8 vf[2][SH::kNT];
+        {
+            const uint32_t sb = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)base +
+                                (uint32_t)(u * kSub * SH::kRow);
+            uint32_t a[8];
 #pragma unroll
-        for (int ii = 0; ii < 2; ii++)
+            for (int i = 0; i < 8; i++) a[i] = sb + (&va[0][0][0])[i];
+            u32x2 r[4 * SH::kNT];
+            read_v_frags<SH::kNT>(r, a);
 #pragma unroll
-            for (int n = 0; n < SH::kNT; n++)
-                vf[ii][n] = *(const v8*)(base + va[ii] + 32 * n * SH::kVStride +
-                                         64 * ((u ^ n) & 1));
+            for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+                for (int n = 0; n < SH::kNT; n++) {
+                    const u32x2 lo = r[ii * 2 * SH::kNT + 2 * n], hi = r[ii * 2 * SH::kNT + 2 * n + 1];
+                    vf[ii][n] = __builtin_bit_cast(v8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                }
+        }
 
         float mx = -INFINITY;
 #pragma unroll
@@ -389,18 +440,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         l += ls;
 #pragma unroll
         for (int ii = 0; ii < 2; ii++) {
-            // element e of the operand is score register kPerm[e] of the
-            // 16-key step (the V^T key order above); pairs (2q, 2q+1)
-            constexpr int kPerm[8] = {0, 1, 4, 5, 2, 3, 6, 7};
+            // element e of the operand is score register 8 ii + e (keys
+            // 4g.. and 8 + 4g.. of the step, the order of the value reads)
             uint32_t hw[4], lw[4];
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const f32x2 x = {pz[8 * ii + kPerm[2 * q]], pz[8 * ii + kPerm[2 * q + 1]]};
+                const f32x2 x = {pz[8 * ii + 2 * q], pz[8 * ii + 2 * q + 1]};
                 if constexpr (M::kSplitP) {
                     hw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-                    const f32x2 h = {__builtin_bit_cast(float, hw[q] << 16),
-                                     __builtin_bit_cast(float, hw[q] & 0xFFFF0000u)};
-                    lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - h, bf16x2));
+                    const f32x2 hv = {__builtin_bit_cast(float, hw[q] << 16),
+                                      __builtin_bit_cast(float, hw[q] & 0xFFFF0000u)};
+                    lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hv, bf16x2));
                 } else {
                     hw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
                 }
@@ -416,38 +466,50 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         }
     };
 
+    // ---- the stage pipeline ----
+    // At the top of stage st the loads of stage st + 2 are issued into
+    // buffer (st + 2) % 3, last read during stage st - 1 (every wave has
+    // passed the barrier that ended it).  At the bottom, the wave waits for
+    // its loads of stage st + 1 (all but the kLoads K and kLoads V loads of
+    // stage st + 2, issued after them, in order) and meets the others: past
+    // that barrier every wave's rows of stage st + 1 are in LDS.
     const int nstage = (wg_end + kStage - 1) / kStage;
-    int ea = 0, eb = 0;
-    if (nstage > 0) {
-        load_stage(0, entry(0, 0), PAIR ? entry(0, 1) : 0, 0);
-        ea = entry(1, 0);
-        if constexpr (PAIR) eb = entry(1, 1);
-        store_stage(0);
-    }
+    fill_table(0);
     __syncthreads();
+    if (nstage > 0) load_stage(0, 0);
+    if (nstage > 1) load_stage(1, 1);
+    wait_vmcnt<0>();                       // stages 0 and 1 in LDS
+    __builtin_amdgcn_s_barrier();
     // Stages [st0, st1), every sub-tile with the causal limits (MASK) or,
     // for stages all of whose keys every row of the wave sees, without.
-    // The two kinds run in two loops rather than behind a branch in one, so
-    // each keeps one register assignment; every stage passes one barrier,
-    // so waves that split the stages differently still meet at each one.
+    // Every stage passes one barrier, so waves that split the stages
+    // differently still meet at each one.
     auto run_stages = [&](int st0, int st1, auto mask) {
         for (int st = st0; st < st1; st++) {
-            const int buf = st & 1;
-            // next stage's rows in flight during this stage's arithmetic
-            // (past the end they are all out of range and touch nothing; K
-            // lands in the other buffer, which no wave reads until the next
-            // barrier)
-            load_stage(st + 1, ea, eb, buf ^ 1);
-            ea = entry(st + 2, 0);
-            if constexpr (PAIR) eb = entry(st + 2, 1);
-            const char* base = lds + buf * SH::kBuf;
+            const int sn = st + 2;
+            if (sn < nstage) {
+                // the table span holding stage sn's blocks (workgroup-uniform)
+                const int last = min(((sn + 1) * kStage - 1) >> bs_shift, nblk - 1);
+                if (last >= tb0 + kTbl) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+                    tb0 = (sn * kStage) >> bs_shift;
+                    fill_table(tb0);
+                    __syncthreads();
+                }
+                load_stage(sn, sn % kBufs);
+            }
+            const char* base = lds + (st % kBufs) * SH::kBuf;
 #pragma unroll
             for (int u = 0; u < kStage / kSub; u++) {
                 const int kb = st * kStage + u * kSub;
                 if (kb <= wlast) sub_tile(base, u, kb, mask);            // wave-uniform
             }
-            store_stage(buf ^ 1);                  // read by no wave since the last barrier
-            __syncthreads();
+            // stage st + 1 in LDS: at most the 2 kLoads loads of stage st + 2
+            // may still be in flight
+            if (sn < nstage) wait_vmcnt<2 * SH::kLoads>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
         }
     };
     // stage st is seen whole by every row of the wave when st * kStage +
@@ -479,11 +541,10 @@ template <class Q, int D>
 hipError_t launch_dd(const DecodeParams& p, hipStream_t st) {
     typedef Shape<D> SH;
     const long pairs = (long)p.S * p.Hkv;
-    const long wgs = (pairs + 7) / 8 * 8 * p.max_groups;   // per_xcd pairs x groups, x 8
+    const long wgs = (pairs + 7) / 8 * 8 * p.max_groups;   // per-XCD pairs x groups, x 8
     void* args[] = {const_cast<DecodeParams*>(&p)};
-    const void* k = p.bs == 8 ? reinterpret_cast<const void*>(prefill_kernel<Q, D, true>)
-                              : reinterpret_cast<const void*>(prefill_kernel<Q, D, false>);
-    return hipLaunchKernel(k, dim3((unsigned)wgs), dim3(64 * kWaves), args, SH::kLds, st);
+    return hipLaunchKernel(reinterpret_cast<const void*>(prefill_kernel<Q, D>),
+                           dim3((unsigned)wgs), dim3(64 * kWaves), args, SH::kLds, st);
 }
 
 }  // namespace
