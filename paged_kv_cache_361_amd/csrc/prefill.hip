@@ -438,30 +438,52 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
             ls += pz[r];
         }
         l += ls;
+        // element e of the operand of step ii is score register 8 ii + e
+        // (keys 4g.. and 8 + 4g.. of the step, the order of the value reads)
+        uint32_t hw[2][4];
 #pragma unroll
-        for (int ii = 0; ii < 2; ii++) {
-            // element e of the operand is score register 8 ii + e (keys
-            // 4g.. and 8 + 4g.. of the step, the order of the value reads)
-            uint32_t hw[4], lw[4];
+        for (int ii = 0; ii < 2; ii++)
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 const f32x2 x = {pz[8 * ii + 2 * q], pz[8 * ii + 2 * q + 1]};
-                if constexpr (M::kSplitP) {
-                    hw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-                    const f32x2 hv = {__builtin_bit_cast(float, hw[q] << 16),
-                                      __builtin_bit_cast(float, hw[q] & 0xFFFF0000u)};
-                    lw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hv, bf16x2));
-                } else {
-                    hw[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
-                }
+                if constexpr (M::kSplitP)
+                    hw[ii][q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+                else
+                    hw[ii][q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
             }
-            const v8 hi = __builtin_bit_cast(v8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++) {
+            const v8 hi = __builtin_bit_cast(v8, u32x4{hw[ii][0], hw[ii][1], hw[ii][2], hw[ii][3]});
 #pragma unroll
             for (int n = 0; n < SH::kNT; n++) o[n] = M::mma(vf[ii][n], hi, o[n]);
-            if constexpr (M::kSplitP) {
-                const v8 lo = __builtin_bit_cast(v8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+        }
+        if constexpr (M::kSplitP) {
+            // bf16 keeps 8 significant bits of a weight.  A lane whose
+            // largest weight here (at most that of its row's best key)
+            // exceeds 1/8 of its running sum also feeds the remainder
+            // p - bf16(p) (another 8 bits); below that share every weight
+            // ends at most 1/8 of the row's total, and the rounding of many
+            // such small weights stays far inside the tolerance.  The
+            // decision is the lane's own, so a row's arithmetic does not
+            // depend on the other rows of the wave.
+            const bool fine = __builtin_amdgcn_exp2f(mxs - m) > 0.125f * l;
+            if (__any(fine)) {
 #pragma unroll
-                for (int n = 0; n < SH::kNT; n++) o[n] = M::mma(vf[ii][n], lo, o[n]);
+                for (int ii = 0; ii < 2; ii++) {
+                    uint32_t lw[4];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const f32x2 x = {pz[8 * ii + 2 * q], pz[8 * ii + 2 * q + 1]};
+                        const f32x2 hv = {__builtin_bit_cast(float, hw[ii][q] << 16),
+                                          __builtin_bit_cast(float, hw[ii][q] & 0xFFFF0000u)};
+                        const uint32_t r =
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hv, bf16x2));
+                        lw[q] = fine ? r : 0u;
+                    }
+                    const v8 lo = __builtin_bit_cast(v8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+#pragma unroll
+                    for (int n = 0; n < SH::kNT; n++) o[n] = M::mma(vf[ii][n], lo, o[n]);
+                }
             }
         }
     };

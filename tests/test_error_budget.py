@@ -1,0 +1,110 @@
+"""Error budget of the 16-bit weights fed to the value products.
+
+The matrix-core kernels multiply bf16 value rows by weights p that must be
+bf16 too.  One bf16 keeps 8 significant bits of p, a relative rounding of
+up to 2^-9 per weight; the output then moves by up to
+2^-9 * sum_t w_t |v_t - out| (w_t the final softmax weight of key t), which
+for rows dominated by a few keys is of the order of the 5e-3 tolerance of
+bf16 caches.  The LDS-staged multi-query kernel therefore adds the
+remainder p - bf16(p) (another 8 bits) for every weight of a lane whose
+largest weight in a 32-key step exceeds 1/8 of the lane's running sum;
+below that share a weight ends at most 1/8 of its row's total.
+
+These tests model that arithmetic on the CPU (no GPU, no library): scores
+from bf16 queries and keys, base-2 weights against a lazily raised
+reference maximum (raised when a step's maximum exceeds it by more than 8),
+a lane's 16 keys of each 32-key step with its own running sum, bf16
+rounding by round-to-nearest-even, the output rounded to bf16, compared
+with float64 softmax attention under the test bound (5e-3, plus half a
+unit in the last place where |ref| >= 1).  They decide that one bf16
+weight alone does not fit at short rows, and that the rule above does, with
+margin, at every row length.
+"""
+import numpy as np
+
+TOL = 5e-3
+TAU = 8.0
+D = 128
+
+
+def bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even), as float32."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def bound(ref: np.ndarray) -> np.ndarray:
+    a = np.abs(ref)
+    return TOL + np.where(a >= 1, np.exp2(np.floor(np.log2(np.maximum(a, 1.0))) - 8), 0.0)
+
+
+def model(n: int, rows: int, rule: str, rng) -> float:
+    """Worst |out - ref| / bound over `rows` rows that see n keys each.
+    rule: "one" (bf16 weights only), "split" (always hi + lo) or "eighth"
+    (lo where the lane's largest weight exceeds 1/8 of its running sum)."""
+    q = bf16(rng.standard_normal((rows, D))).astype(np.float64)
+    k = bf16(rng.standard_normal((rows, n, D))).astype(np.float64)
+    v = bf16(rng.standard_normal((rows, n, D))).astype(np.float64)
+    s2 = np.einsum("rd,rnd->rn", q, k) / np.sqrt(D) * np.log2(np.e)
+    e = np.exp2(s2 - s2.max(1, keepdims=True))
+    ref = np.einsum("rn,rnd->rd", e, v) / e.sum(1, keepdims=True)
+
+    m = np.full(rows, -np.inf)
+    lanes = [np.zeros(rows), np.zeros(rows)]        # running sums of the lane pair
+    o = np.zeros((rows, D))
+    for k0 in range(0, n, 32):
+        step = s2[:, k0:k0 + 32]
+        mx = step.max(1)
+        m_new = np.where(mx > m + TAU, mx, m)
+        alpha = np.where(np.isinf(m), 0.0, np.exp2(m - m_new))
+        lanes = [x * alpha for x in lanes]
+        o *= alpha[:, None]
+        m = m_new
+        pm = np.exp2(mx - m)                          # the row's largest weight here
+        for g in range(2):                            # the two lanes of a row
+            sel = np.array([j for j in range(step.shape[1]) if (j // 4) % 2 == g], dtype=int)
+            if sel.size == 0:
+                continue
+            p = np.exp2(step[:, sel] - m[:, None]).astype(np.float32)
+            lanes[g] = lanes[g] + p.astype(np.float64).sum(1)
+            hi = bf16(p)
+            lo = bf16(p - hi)
+            if rule == "one":
+                w = hi
+            elif rule == "split":
+                w = hi.astype(np.float64) + lo
+            else:
+                fine = pm > lanes[g] / 8
+                w = hi.astype(np.float64) + np.where(fine[:, None], lo, 0.0)
+            o += np.einsum("rn,rnd->rd", w.astype(np.float64), v[:, k0 + sel])
+    out = bf16((o / (lanes[0] + lanes[1])[:, None]).astype(np.float32)).astype(np.float64)
+    return float((np.abs(out - ref) / bound(ref)).max())
+
+
+LENGTHS = [2, 3, 5, 8, 12, 24, 32, 48, 64, 128, 512, 1500]
+
+
+def rows_for(n: int) -> int:
+    return 3000 if n <= 64 else (600 if n <= 512 else 120)
+
+
+def test_one_bf16_weight_does_not_fit_short_rows():
+    """bf16 weights alone: some short rows leave the bound (or come within
+    a few percent of it), far above the rounding of the output itself."""
+    rng = np.random.default_rng(20)
+    worst = max(model(n, rows_for(n), "one", rng) for n in (2, 3, 5, 8, 12, 24, 32))
+    floor = max(model(n, rows_for(n), "split", rng) for n in (2, 3, 5, 8, 12, 24, 32))
+    print(f"one bf16 weight: worst err/bound {worst:.3f}; hi + lo: {floor:.3f}")
+    assert worst > 0.95 and floor < 0.7
+
+
+def test_eighth_rule_fits_every_row_length():
+    """The kernel's rule stays inside the bound at every length, within
+    0.1 of the always-split arithmetic at short rows and with more margin
+    at long ones."""
+    rng = np.random.default_rng(21)
+    for n in LENGTHS:
+        w = model(n, rows_for(n), "eighth", rng)
+        print(f"n={n}: worst err/bound {w:.3f}")
+        assert w <= 0.75, n
