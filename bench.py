@@ -435,6 +435,18 @@ def multi_cost(mc):
     return kv + qo + table, flops
 
 
+def settle_clocks(fn, seconds: float = 0.3) -> None:
+    """Untimed calls of fn until `seconds` of wall time have passed: the
+    GPU's clocks ramp up over the first tens of milliseconds of work, and a
+    short warmup would leave the first timed calls at a lower clock."""
+    import torch
+    t = time.perf_counter()
+    while time.perf_counter() - t < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_multi(args) -> int:
     import torch
     import paged_kv_cache_361_amd as pkv
@@ -469,6 +481,7 @@ def bench_multi(args) -> int:
     for i in range(W):
         call(i)
     torch.cuda.synchronize()
+    settle_clocks(lambda: call(0))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
     t0 = time.perf_counter()

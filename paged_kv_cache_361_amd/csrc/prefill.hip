@@ -104,16 +104,26 @@ struct Shape {
     static_assert(kLoads * kKpl == kKpw && kKpw == 8, "a wave's 8 keys in whole loads");
 };
 
-// K rows of a stage buffer: 16-byte units XORed with row % KSW (the units
-// per row, at most 16), so that the rows a score read takes at once fall in
-// distinct banks.
-template <int ROW>
-constexpr int k_swizzle() { return ROW / 16 < 16 ? ROW / 16 : 16; }
+// LDS serves 64 banks of 4 bytes; a 16-byte read takes 16 lanes at a
+// time, an 8-byte read 32.
+//
+// K rows of a stage buffer (2 D bytes each): 16-byte units XORed with
+// k_swizzle(row), so that the 16 rows of a score read's lanes cover all 64
+// banks: row % 16 for 256-byte rows, (row / 2) % 8 for 128-byte rows (two
+// rows per 64 banks).
+template <int D>
+__device__ inline int k_swizzle(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 
-// V rows: units XORed with 2 (row % 4).  A value read takes 8 bytes from
-// each of 4 consecutive rows at the same columns (the transpose read),
-// which then fall in distinct banks.
-__device__ inline int v_swizzle(int row) { return (row & 3) << 1; }
+// V: each load's block of kKpl keys (1 KiB, CHUNKS units per key) is
+// stored tile-major: unit u = 4 n + j (n the 32-column output tile, j < 4)
+// of key k of the block goes to slot (k / 4) 4 CHUNKS + 16 n + 4 (k % 4) + j.
+// A value read takes 8 bytes at the same columns from the 4 keys of a group
+// k / 4 (the transpose read): its 32 lanes then cover 256 contiguous bytes,
+// all 64 banks, and tile n is a constant 256 n bytes further.
+template <int CHUNKS>
+__device__ inline int v_slot(int k, int u) {
+    return (k >> 2) * 4 * CHUNKS + 16 * (u >> 2) + 4 * (k & 3) + (u & 3);
+}
 
 // s_waitcnt with only a vector-memory count (expcnt and lgkmcnt at their
 // maxima, so neither is waited for).
@@ -124,51 +134,51 @@ __device__ inline void wait_vmcnt() {
 }
 
 // The value fragments of one 32-key sub-tile: transpose reads (2 per
-// operand; see the address sets in the kernel) from the 8 lane addresses
-// a[ii][rd][par] (flattened), output tile n at byte offset 128 (n / 2).
-// Written out together with their wait, so that the compiler does not take
-// them for reads of the stage loads still in flight into other buffers
-// (it would wait for all of those first).  r[ii][n][rd] flattened.
+// operand; see the address sets in the kernel) from the 4 lane addresses
+// a[ii][rd] (flattened), output tile n at byte offset 256 n.  Written out
+// together with their wait, so that the compiler does not take them for
+// reads of the stage loads still in flight into other buffers (it would
+// wait for all of those first).  r[ii][n][rd] flattened.
 template <int NT>
-__device__ inline void read_v_frags(u32x2 (&r)[4 * NT], const uint32_t (&a)[8]);
+__device__ inline void read_v_frags(u32x2 (&r)[4 * NT], const uint32_t (&a)[4]);
 template <>
-__device__ inline void read_v_frags<4>(u32x2 (&r)[16], const uint32_t (&a)[8]) {
+__device__ inline void read_v_frags<4>(u32x2 (&r)[16], const uint32_t (&a)[4]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %18\n\t"
-        "ds_read_b64_tr_b16 %2, %17\n\t"
-        "ds_read_b64_tr_b16 %3, %19\n\t"
-        "ds_read_b64_tr_b16 %4, %16 offset:128\n\t"
-        "ds_read_b64_tr_b16 %5, %18 offset:128\n\t"
-        "ds_read_b64_tr_b16 %6, %17 offset:128\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:128\n\t"
-        "ds_read_b64_tr_b16 %8, %20\n\t"
-        "ds_read_b64_tr_b16 %9, %22\n\t"
-        "ds_read_b64_tr_b16 %10, %21\n\t"
-        "ds_read_b64_tr_b16 %11, %23\n\t"
-        "ds_read_b64_tr_b16 %12, %20 offset:128\n\t"
-        "ds_read_b64_tr_b16 %13, %22 offset:128\n\t"
-        "ds_read_b64_tr_b16 %14, %21 offset:128\n\t"
-        "ds_read_b64_tr_b16 %15, %23 offset:128\n\t"
+        "ds_read_b64_tr_b16 %1, %17\n\t"
+        "ds_read_b64_tr_b16 %2, %16 offset:256\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:256\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:512\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:512\n\t"
+        "ds_read_b64_tr_b16 %6, %16 offset:768\n\t"
+        "ds_read_b64_tr_b16 %7, %17 offset:768\n\t"
+        "ds_read_b64_tr_b16 %8, %18\n\t"
+        "ds_read_b64_tr_b16 %9, %19\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:256\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:256\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:512\n\t"
+        "ds_read_b64_tr_b16 %13, %19 offset:512\n\t"
+        "ds_read_b64_tr_b16 %14, %18 offset:768\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:768\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 }
 template <>
-__device__ inline void read_v_frags<2>(u32x2 (&r)[8], const uint32_t (&a)[8]) {
+__device__ inline void read_v_frags<2>(u32x2 (&r)[8], const uint32_t (&a)[4]) {
     asm volatile(
         "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %10\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %11\n\t"
-        "ds_read_b64_tr_b16 %4, %12\n\t"
-        "ds_read_b64_tr_b16 %5, %14\n\t"
-        "ds_read_b64_tr_b16 %6, %13\n\t"
-        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:256\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:256\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %11\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:256\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:256\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
         : "memory");
 }
 
@@ -300,15 +310,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     // Wave w moves keys 8 w .. 8 w + 7 of a stage (one block: block sizes
     // are multiples of 8), so its table entry is wave-uniform and every
     // load has a scalar buffer descriptor.  Load r covers keys 8 w + kKpl r
-    // .. + kKpl - 1, lane i writing 16 bytes at i * 16 from the load's first
-    // row: row i / kChunks, swizzled unit i % kChunks, holding unit
-    // (i % kChunks) ^ swizzle(row) of the key's row.  Rows at or past
-    // wg_end take an out-of-range offset and write zeros.
+    // .. + kKpl - 1, lane i writing 16 bytes at i * 16 from the load's
+    // first byte.  K: row i / kChunks, unit (i % kChunks) ^ k_swizzle(row)
+    // of the key's row.  V: lane i fills slot i of the tile-major block.
+    // Keys at or past wg_end take an out-of-range offset and write zeros.
     const uint32_t pool_row = (uint32_t)p.Hkv * SH::kRow;       // bytes between slots
     const uint32_t blk_bytes = (uint32_t)p.bs * pool_row;
     const uint32_t head_off = (uint32_t)h * SH::kRow;
     const int lj = lane / SH::kChunks;
     const int ch = lane % SH::kChunks;
+    // the V slot this lane fills (v_slot inverted): key vk of the block, unit vu
+    const int vrem = lane % (4 * SH::kChunks);
+    const int vk = 4 * (lane / (4 * SH::kChunks)) + ((vrem >> 2) & 3);
+    const int vu = 4 * (vrem >> 4) + (vrem & 3);
     auto load_stage = [&](int st, int buf) {
         const int t0 = st * kStage + SH::kKpw * wave;
         const int e = tbl_lds[min(t0 >> bs_shift, nblk - 1) - tb0];
@@ -320,19 +334,19 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         char* vdst = kdst + SH::kK;
 #pragma unroll
         for (int r = 0; r < SH::kLoads; r++) {
-            const int row = SH::kKpw * wave + r * SH::kKpl + lj;   // within the stage
-            const int t = st * kStage + row;
-            const uint32_t off =
-                t < wg_end ? (uint32_t)(t & (p.bs - 1)) * pool_row + head_off : kOOB;
-            const uint32_t uk = (uint32_t)(ch ^ (row & (k_swizzle<SH::kRow>() - 1)));
-            const uint32_t uv = (uint32_t)(ch ^ v_swizzle(row));
+            const int row0 = SH::kKpw * wave + r * SH::kKpl;     // within the stage
             const int dst = r * SH::kKpl * SH::kRow;
+            const int tk = st * kStage + row0 + lj;
+            const uint32_t uk = (uint32_t)(ch ^ k_swizzle<D>(row0 + lj));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rk, (__attribute__((address_space(3))) void*)(kdst + dst), 16,
-                off == kOOB ? kOOB : off + 16u * uk, 0, 0, 0);
+                tk < wg_end ? (uint32_t)(tk & (p.bs - 1)) * pool_row + head_off + 16u * uk : kOOB,
+                0, 0, 0);
+            const int tv = st * kStage + row0 + vk;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rv, (__attribute__((address_space(3))) void*)(vdst + dst), 16,
-                off == kOOB ? kOOB : off + 16u * uv, 0, 0, 0);
+                tv < wg_end ? (uint32_t)(tv & (p.bs - 1)) * pool_row + head_off + 16u * vu : kOOB,
+                0, 0, 0);
         }
     };
 
@@ -348,30 +362,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     uint32_t ka[SH::kQS];
 #pragma unroll
     for (int i = 0; i < SH::kQS; i++)
-        ka[i] = (uint32_t)(c * SH::kRow) +
-                (uint32_t)((((D / 16) * g + i) ^ (c & (k_swizzle<SH::kRow>() - 1))) << 4);
+        ka[i] = (uint32_t)(c * SH::kRow) + (uint32_t)((((D / 16) * g + i) ^ k_swizzle<D>(c)) << 4);
     // V^T fragments by transpose reads.  Two reads per operand (rd 0: keys
     // 4g..4g+3, rd 1: keys 8+4g..8+4g+3 of the 16-key step ii); in lane
     // group G16 = lane / 16 (half g = G16 / 2, 16 columns from 32 n + 16
-    // (G16 % 2)), lane s = 4 mr + tc addresses key row mr of the four and
-    // columns 4 tc .. 4 tc + 3.  With the swizzle 2 (row % 4) = 2 mr, the
-    // unit's bit 2 is (n % 2) ^ (mr / 2): two lane-constant address sets,
-    // by the parity of the output tile n; the rest is a constant offset.
-    uint32_t va[2][2][2];
+    // (G16 % 2)), lane s = 4 mr + tc addresses key mr of the four and
+    // columns 4 tc .. 4 tc + 3: unit 2 (G16 % 2) + tc / 2 of tile n, half
+    // tc % 2 of it.  The four keys start a V block's group of four.
+    uint32_t va[2][2];
     {
         const int G16 = lane >> 4, sl = lane & 15, mr = sl >> 2, tc = sl & 3;
 #pragma unroll
         for (int ii = 0; ii < 2; ii++)
 #pragma unroll
-            for (int rd = 0; rd < 2; rd++)
-#pragma unroll
-                for (int par = 0; par < 2; par++) {
-                    const int row = 16 * ii + 8 * rd + 4 * g + mr;
-                    const int unit = (tc >> 1) + 2 * ((G16 & 1) ^ (mr & 1)) +
-                                     4 * (par ^ (mr >> 1));
-                    va[ii][rd][par] = (uint32_t)(SH::kK + row * SH::kRow + 16 * unit +
-                                                 8 * (tc & 1));
-                }
+            for (int rd = 0; rd < 2; rd++) {
+                const int key = 16 * ii + 8 * rd + 4 * g + mr;
+                const int blk = key / SH::kKpl;
+                const int slot = v_slot<SH::kChunks>(key % SH::kKpl, 2 * (G16 & 1) + (tc >> 1));
+                va[ii][rd] = (uint32_t)(SH::kK + blk * SH::kKpl * SH::kRow + 16 * slot + 8 * (tc & 1));
+            }
     }
 
     // One 32-key sub-tile u of the stage in LDS buffer `base`: scores, the
@@ -397,9 +406,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         {
             const uint32_t sb = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)base +
                                 (uint32_t)(u * kSub * SH::kRow);
-            uint32_t a[8];
+            uint32_t a[4];
 #pragma unroll
-            for (int i = 0; i < 8; i++) a[i] = sb + (&va[0][0][0])[i];
+            for (int i = 0; i < 4; i++) a[i] = sb + (&va[0][0])[i];
             u32x2 r[4 * SH::kNT];
             read_v_frags<SH::kNT>(r, a);
 #pragma unroll
