@@ -661,6 +661,7 @@ def bench_mixed(args) -> int:
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    settle_clocks(lambda: step(0))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     t0 = time.perf_counter()
     for i in range(K):
