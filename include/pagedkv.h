@@ -178,8 +178,9 @@ int pkv_reshape_and_cache(const void* key, const void* value, pkv_dtype src_dtyp
  *          (sequence, KV head) pair that falls into one chunk is finished
  *          here; for every other pair each chunk's piece leaves its partials
  *          in `workspace` (layout private to the library: a header, the tile
- *          prefix of the sequences, then (m, l, o) entries as above, two per
- *          query head of the group per chunk), and pkv_paged_attention_reduce
+ *          prefix of the sequences, the first and last chunk of every
+ *          (sequence, KV head) pair, then (m, l, o) entries as above, two
+ *          per query head of the group per chunk), and pkv_paged_attention_reduce
  *          must run next on the same stream with partition_size =
  *          PKV_PARTITION_BALANCED; it also writes the zero rows of sequences
  *          with L <= 0.  The workspace needs no initialisation: its chunk
@@ -373,7 +374,8 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
 
 /*
  * pkv_multi_workspace_bytes - bytes of workspace pkv_paged_attention_multi
- * needs.  PKV_PARTITION_BALANCED: a 256-byte header, num_seqs + 1 words,
+ * needs.  PKV_PARTITION_BALANCED: a 256-byte header, num_seqs + 1 words
+ * and 2 * num_seqs * num_q_heads words (the chunk ranges of the streams),
  * then m, l [2 * (5 * 2048 + 8) * 16] and o [same][head_dim] float32 (each
  * part on a 256-byte boundary), whatever the lengths.  P > 0: with rows = num_seqs * max_query_len *
  * num_q_heads and P_max = ceil(max_seq_len / P), m and l [rows][P_max] and
@@ -390,9 +392,9 @@ size_t pkv_multi_workspace_bytes(int32_t num_seqs, int32_t max_query_len,
  * (layouts above) for partition_size > 0 or PKV_PARTITION_BALANCED; 0 when
  * partition_size == 0, a size is not positive or num_q_heads is not a
  * multiple of num_kv_heads.  The balanced size does not depend on the
- * lengths: a header, num_seqs + 1 words, and 2 * (5 * 2048 + 8) entries of
- * head_dim + 2 floats per query head of the group.  Host-only, touches no
- * device.
+ * lengths: a header, num_seqs + 1 + 2 * num_seqs * num_kv_heads words, and
+ * 2 * (5 * 2048 + 8) entries of head_dim + 2 floats per query head of the
+ * group.  Host-only, touches no device.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim,

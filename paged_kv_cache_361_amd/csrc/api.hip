@@ -35,9 +35,11 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace pieces for split-K.  Fixed partitions: P_max entries per row,
 // m at 0, l at off_l, o at off_o.  Balanced: a 256-byte header, the tile
-// prefix of the sequences (S + 1 words) at off_pre, then m, l and o for two
-// entries per query head of the group per chunk of the guided schedule,
-// sized for the largest grid (kBalancedMaxWaves) and its chunk bound.
+// prefix of the sequences (S + 1 words) at off_pre followed by the chunk
+// range of each (sequence, KV head) stream (2 words each), then m, l and o
+// for two entries per query head of the group per chunk of the guided
+// schedule, sized for the largest grid (kBalancedMaxWaves) and its chunk
+// bound.
 struct WsLayout {
     int P_max = 0;
     size_t off_pre = 0, off_m = 0, off_l = 0, off_o = 0, bytes = 0;
@@ -51,7 +53,7 @@ inline bool ws_layout(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t max
     if (P == PKV_PARTITION_BALANCED) {
         w->P_max = 0;
         w->off_pre = 256;
-        w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1), 256);
+        w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1) + 8 * (size_t)S * (size_t)Hkv, 256);
         n = (size_t)2 * (size_t)max_chunks(kBalancedMaxWaves) * (size_t)(Hq / Hkv);
     } else {
         if (P <= 0) return false;
@@ -120,13 +122,14 @@ inline bool multi_ws_layout(int S, int Qmax, int Hq, int D, int max_len, int P, 
     if (S <= 0 || Qmax <= 0 || Hq <= 0 || D <= 0 || max_len <= 0) return false;
     if (P == 0) return true;
     if (P == PKV_PARTITION_BALANCED) {
-        // the balanced layout: header, tile prefix, then entries of 16
-        // columns (query token, head) per chunk slot
+        // the balanced layout: header, tile prefix and stream chunk ranges
+        // (for up to Hq KV heads), then entries of 16 columns (query token,
+        // head) per chunk slot
         auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
         const int64_t n = 2 * max_chunks(kBalancedMaxWaves) * 16;
         w->P_max = 1;
         w->off_len = 256;                          // the tile prefix here
-        w->off_m = (size_t)up(256 + 4 * ((int64_t)S + 1));
+        w->off_m = (size_t)up(256 + 4 * ((int64_t)S + 1) + 8 * (int64_t)S * Hq);
         w->off_l = w->off_m + (size_t)up(4 * n);
         w->off_o = w->off_l + (size_t)up(4 * n);
         w->bytes = w->off_o + (size_t)(4 * n * D);
@@ -147,6 +150,12 @@ inline bool multi_ws_layout(int S, int Qmax, int Hq, int D, int max_len, int P, 
 }
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+// The group size of a reduce's rows and its log2 (-1 when not a power of 2).
+inline void set_group(ReduceParams& r) {
+    r.G = r.Hq / r.Hkv;
+    r.g_shift = (r.G & (r.G - 1)) == 0 ? __builtin_ctz((unsigned)r.G) : -1;
+}
 
 }  // namespace
 
@@ -329,6 +338,7 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
         r.len_cap = len_cap;
         r.q_start = query_start;
         r.S_seq = num_seqs;
+        set_group(r);
         return launch_status(launch_reduce_balanced(q_dtype, r, stream));
     }
     if (partition_size > 0) {
@@ -611,11 +621,11 @@ char* scratch_on(int dev) {
 
 // The balanced workspace sized for a grid of nW wavefronts (entries for
 // the chunk bound of that grid rather than of the largest one).
-inline size_t balanced_bytes_for_grid(int S, int G, int D, int nW, WsLayout* w) {
+inline size_t balanced_bytes_for_grid(int S, int Hkv, int G, int D, int nW, WsLayout* w) {
     const size_t n = (size_t)2 * (size_t)max_chunks(nW) * (size_t)G;
     w->P_max = 0;
     w->off_pre = 256;
-    w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1), 256);
+    w->off_m = round_up(w->off_pre + 4 * ((size_t)S + 1) + 8 * (size_t)S * (size_t)Hkv, 256);
     w->off_l = w->off_m + round_up(n * 4, 256);
     w->off_o = w->off_l + round_up(n * 4, 256);
     w->bytes = w->off_o + n * (size_t)D * 4;
@@ -721,6 +731,7 @@ int pkv_paged_attention_reduce(void* out, pkv_dtype out_dtype, const void* works
     p.len_cap = max_seq_len;
     p.q_start = nullptr;
     p.S_seq = num_seqs;
+    set_group(p);
     if (balanced) return launch_status(launch_reduce_balanced(out_dtype, p, stream));
     return launch_status(launch_reduce(out_dtype, p, stream));
 }
@@ -748,7 +759,7 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* query, pkv_dtype q
     p.P_max = 1;
     p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, block_size);
     WsLayout w;
-    if (balanced_bytes_for_grid(num_seqs, p.G, head_dim, p.nW, &w) > kScratchBytes)
+    if (balanced_bytes_for_grid(num_seqs, num_kv_heads, p.G, head_dim, p.nW, &w) > kScratchBytes)
         return PKV_ERR_SCRATCH;
     char* ws = scratch_on(dev);
     if (!ws) return PKV_ERR_HIP;
@@ -778,6 +789,7 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* query, pkv_dtype q
     r.len_cap = max_seq_len;
     r.q_start = nullptr;
     r.S_seq = num_seqs;
+    set_group(r);
     return launch_status(launch_reduce_balanced(q_dtype, r, stream));
 }
 

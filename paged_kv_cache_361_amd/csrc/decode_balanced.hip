@@ -157,7 +157,7 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
 // ---- decode ----------------------------------------------------------------
 
 // Span flags.
-enum : int { kFirst = 1, kLast = 2, kComplete = 4, kSlot1 = 8 };
+enum : int { kFirst = 1, kLast = 2, kComplete = 4, kSlot1 = 8, kStart = 16, kEnd = 32 };
 
 // A span: tiles [t0, t1) of stream (s, h) (packed in `key`), within one table
 // window starting at block wb, inside chunk `chunk`.  Wave-uniform; kept
@@ -167,7 +167,9 @@ struct Span {
     int L, t0, t1, wb, chunk;
     int flags;         // kFirst: first span of its segment; kLast: last;
                        // kComplete: the segment is the whole stream;
-                       // kSlot1: not the first segment of its chunk
+                       // kSlot1: not the first segment of its chunk;
+                       // (last span) kStart: the segment starts the stream,
+                       // kEnd: it ends it
     __device__ int s() const { return key >> 12; }
     __device__ int h() const { return key & 4095; }
 };
@@ -238,6 +240,8 @@ struct Walk {
         const bool last = (tile >= nt) || rem <= 0;
         if (last) {
             f |= kLast;
+            if (wf & 2) f |= kStart;
+            if (tile >= nt) f |= kEnd;
             if ((wf & 2) && tile >= nt) f |= kComplete;
             wf = 4;                        // closed; later segments use slot 1
         } else {
@@ -506,6 +510,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
         crt += DEPTH;
         if (crt >= c_t1) {
             if (c_flags & kLast) {
+                // the stream's chunk range, for the reduce: the segment that
+                // starts the stream gives the first chunk and its slot there,
+                // the one that ends it the last
+                if (lane == 0 && (c_flags & (kStart | kEnd))) {
+                    int32_t* rng = p.ws_pre + p.S + 1 +
+                                   2 * ((c_key >> 12) * p.Hkv + (c_key & 4095));
+                    if (c_flags & kStart)
+                        rng[0] = c_chunk | ((c_flags & kSlot1) ? (int32_t)0x80000000 : 0);
+                    if (c_flags & kEnd) rng[1] = c_chunk;
+                }
                 const size_t e0 = ((size_t)c_chunk * 2 + ((c_flags & kSlot1) ? 1 : 0)) * ncol;
                 if constexpr (MULTI) {
                     const int cs = c_key >> 12, ch = c_key & 4095;

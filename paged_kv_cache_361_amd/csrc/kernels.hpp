@@ -33,7 +33,9 @@ struct DecodeParams {
     float* ws_l;
     float* ws_o;
     int32_t* ws_hdr;       // balanced mode: header of the workspace
-    int32_t* ws_pre;       // balanced mode: tile prefix of the sequences [S + 1]
+    int32_t* ws_pre;       // balanced mode: tile prefix of the sequences [S + 1], then
+                           // per stream (s * Hkv + h) its first chunk (bit 31: the
+                           // chunk slot of its piece there) and its last chunk
     int nW;                // balanced mode: wavefronts of the persistent grid
     uint32_t epoch;        // balanced mode: this call's number (never repeats soon)
     const int32_t* q_start;  // multi-query: [S + 1] first query token of each sequence
@@ -57,9 +59,10 @@ struct ReduceParams {
     const float* ws_l;
     const float* ws_o;
     const int32_t* ws_hdr; // balanced mode: header written by the decode call
-    const int32_t* ws_pre; // balanced mode: tile prefix of the sequences [S + 1]
+    const int32_t* ws_pre; // balanced mode: tile prefix [S + 1] and stream chunk ranges
     const int32_t* lens;
     int S, Hq, Hkv, D, P, P_max, len_cap;
+    int G, g_shift;        // balanced mode: Hq / Hkv, and its log2 (-1: not a power of 2)
     // balanced multi-query: rows are (query token, head), S counts query
     // tokens; the sequences' query_start [S_seq + 1] maps a token to its
     // sequence (nullptr: decode rows)

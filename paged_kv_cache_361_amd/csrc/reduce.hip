@@ -251,11 +251,14 @@ void reduce_kernel(ReduceParams p) {
 
 // ---- balanced split ---------------------------------------------------------
 
-// MULTI: rows of a balanced multi-query call, numbered (sequence s, query
-// token j < max_query_len of it, head) so that no search maps a row to its
-// sequence; the output row is (query_start[s] + j, head).  A token's column
-// in its stream is j * G + head % G, and a token placed before its sequence
-// (its column saw nothing) gets a zero row.
+// Rows of a balanced call: the grid is (groups of RPB query heads, sequence,
+// query token), so a row's place needs no division.  The decode wrote, per
+// (sequence, KV head) stream, its first and last chunk (and the slot of its
+// piece in the first): entry e of the row is slot 0 or 1 of chunk c0 + e.
+// MULTI: rows of a multi-query call, (sequence s, query token j <
+// max_query_len of it, head); the output row is (query_start[s] + j, head),
+// a token's column in its stream is j * G + head % G, and a token placed
+// before its sequence (its column saw nothing) gets a zero row.
 template <class O, int D, int WPR, bool MULTI>
 __global__ __launch_bounds__(64 * wg_waves(WPR)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(WPR))))
 void reduce_balanced_kernel(ReduceParams p) {
@@ -263,33 +266,33 @@ void reduce_balanced_kernel(ReduceParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int sub = wave % WPR;
-    const int row = blockIdx.x * RPB + wave / WPR;
+    const int hq = blockIdx.x * RPB + wave / WPR;
+    const int s = blockIdx.y;
+    const int j = blockIdx.z;
     const int32_t* hdr = p.ws_hdr;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0 && threadIdx.x == 0) {
         // The decode kernel is done with the chunk counter: return it to 0,
         // below any call's base, so that the next call takes it over even
         // when it carries the same call number (a replayed graph freezes
         // the number in the kernel's arguments).
         *(unsigned long long*)(const_cast<int32_t*>(hdr) + kHdrCounter) = 0ull;
     }
-    if (row >= p.S * p.Hq) return;
+    if (hq >= p.Hq) return;
     const int S = MULTI ? p.S_seq : p.S;
-    const int maxq = MULTI ? p.S / S : 1;       // MULTI: p.S = num_seqs * max_query_len
-    const int s = row / (maxq * p.Hq);
-    const int j = MULTI ? (row / p.Hq) % maxq : 0;
+    const int h = p.g_shift >= 0 ? hq >> p.g_shift : hq / p.G;
+    const int gh = hq - h * p.G;                // head within the group
     // Every word the row needs is loaded before any of them is tested: the
-    // header, the prefix total, the sequence's prefix entries and, for
-    // MULTI, its query range and length.  No load then waits behind a test of
-    // another.  All of them lie inside the workspace and the arrays the call
-    // passed.
+    // header, the sequence's prefix entries, the stream's chunk range and,
+    // for MULTI, its query range and length.  All of them lie inside the
+    // workspace and the arrays the call passed.
     const int magic = hdr[kHdrMagic];
     const int nW = hdr[kHdrNW];
     const int Hkv = hdr[kHdrHkv];
     const int G = hdr[kHdrG];
-    const int T = hdr[kHdrT];
-    const int floor = hdr[kHdrFloor];
-    const int preS = p.ws_pre[S];
+    const int chunks = hdr[kHdrChunks];
     const int p0 = p.ws_pre[s], p1 = p.ws_pre[s + 1];
+    const int32_t* rng = p.ws_pre + S + 1 + 2 * (s * p.Hkv + h);
+    const int r0 = rng[0], r1 = rng[1];
     const int q0 = MULTI ? p.q_start[s] : 0;
     const int q1 = MULTI ? p.q_start[s + 1] : 0;
     const int Lraw = MULTI ? p.lens[s] : 0;
@@ -297,17 +300,14 @@ void reduce_balanced_kernel(ReduceParams p) {
     // breaking the call's contract): write nothing rather than follow its
     // indices.  One condition of every word, combined without short cuts, so
     // that no load is deferred behind a test of another.
+    const int c0 = r0 & 0x7FFFFFFF, c1 = r1;
     const bool bad = (magic != kBalancedMagic) | (nW < 1) | (nW > kBalancedMaxWaves) |
-                     (G < 1) | (Hkv != p.Hkv) | (Hkv * G != p.Hq) | (T < 0) | (preS != T) |
-                     (floor < 1) | (floor > kMaxChunkFloor) |
-                     (p0 < 0) | (p1 < p0) | (p1 > T) | ((p1 - p0) % max(Hkv, 1) != 0) |
+                     (G != p.G) | (Hkv != p.Hkv) | (chunks < 0) |
+                     ((int64_t)chunks > max_chunks(nW)) | (p1 < p0) |
                      (MULTI & ((q1 < q0) | (Lraw < 0)));
     if (bad) return;
-    const Sched q = make_sched(T, nW, floor);
-    const int hq = row % p.Hq;
-    const int h = hq / G;
-    int col = hq % G, ncol = G;
-    size_t orow = (size_t)row;                  // output row
+    int col = gh, ncol = G;
+    size_t orow = (size_t)s * p.Hq + hq;        // output row
     typedef typename O::T OT;
     auto zero_row = [&]() {
         if (sub == 0)
@@ -318,7 +318,7 @@ void reduce_balanced_kernel(ReduceParams p) {
         const int n = min(q1 - q0, QPG);
         if (j >= n) return;                     // no such query token
         orow = (size_t)(q0 + j) * p.Hq + hq;
-        col = j * G + hq % G;
+        col = j * G + gh;
         ncol = QPG * G;
         const int L = Lraw < p.len_cap ? Lraw : p.len_cap;
         if (L - n + j < 0) {                    // its column saw no token
@@ -326,16 +326,13 @@ void reduce_balanced_kernel(ReduceParams p) {
             return;
         }
     }
-    const int nt = (p1 - p0) / Hkv;
-    if (nt == 0) {                              // no tokens: a zero row
+    if (p1 == p0) {                             // no tokens: a zero row
         zero_row();
         return;
     }
-    const int g0 = p0 + h * nt;                 // first tile of stream (s, h)
-    const int c0 = chunk_of(q, g0);
-    const int c1 = chunk_of(q, g0 + nt - 1);
     if (c0 == c1) return;                       // one chunk held it: decode wrote the row
-    const int slot0 = chunk_begin(q, c0) < g0 ? 1 : 0;
+    if (c1 < c0 || c1 >= chunks) return;        // not ranges of this call
+    const int slot0 = (int)((uint32_t)r0 >> 31);
     merge<O, D, WPR>(
         p, c1 - c0 + 1,
         [&](int e) {
@@ -347,12 +344,19 @@ void reduce_balanced_kernel(ReduceParams p) {
 
 template <class O, int D, int WPR, bool BAL>
 hipError_t launch_r(const ReduceParams& p, hipStream_t st) {
-    const long rows = (long)p.S * p.Hq;
     constexpr int RPB = wg_waves(WPR) / WPR;
-    const dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(64 * wg_waves(WPR));
-    if (BAL && p.q_start)
-        return launch_kernel(reduce_balanced_kernel<O, D, WPR, true>, grid, block, st, p);
-    if (BAL) return launch_kernel(reduce_balanced_kernel<O, D, WPR, false>, grid, block, st, p);
+    const dim3 block(64 * wg_waves(WPR));
+    if (BAL) {
+        // (groups of query heads, sequences, query tokens per sequence)
+        const int seqs = p.q_start ? p.S_seq : p.S;
+        const dim3 grid((unsigned)((p.Hq + RPB - 1) / RPB), (unsigned)seqs,
+                        (unsigned)(p.q_start ? p.S / p.S_seq : 1));
+        if (p.q_start)
+            return launch_kernel(reduce_balanced_kernel<O, D, WPR, true>, grid, block, st, p);
+        return launch_kernel(reduce_balanced_kernel<O, D, WPR, false>, grid, block, st, p);
+    }
+    const long rows = (long)p.S * p.Hq;
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
     return launch_kernel(reduce_kernel<O, D, WPR>, grid, block, st, p);
 }
 

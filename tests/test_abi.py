@@ -65,13 +65,14 @@ def test_workspace_bytes_layout(pkv):
 
 def test_balanced_workspace_bytes(pkv):
     """Balanced split: a 256-byte header, the tile prefix of the sequences
-    (S + 1 words, padded to 256 bytes), then (m, l, o) entries for two pieces
-    per query head of the group per chunk, for the chunk bound 5 * 2048 + 8
-    of the largest grid; the lengths do not enter."""
+    (S + 1 words) and the chunk range of each (sequence, KV head) stream (2
+    words), padded to 256 bytes, then (m, l, o) entries for two pieces per
+    query head of the group per chunk, for the chunk bound 5 * 2048 + 8 of
+    the largest grid; the lengths do not enter."""
     Hq, Hkv, D, S = 32, 8, 128, 256
     n = 2 * (5 * 2048 + 8) * (Hq // Hkv)
     a = -(-4 * n // 256) * 256
-    off_m = -(-(256 + 4 * (S + 1)) // 256) * 256
+    off_m = -(-(256 + 4 * (S + 1) + 8 * S * Hkv) // 256) * 256
     expect = off_m + 2 * a + 4 * n * D
     B = pkv.PARTITION_BALANCED
     assert pkv.decode_workspace_bytes(S, Hq, Hkv, D, 4096, B) == expect
@@ -188,10 +189,11 @@ def test_multi_workspace_bytes_layout(pkv):
         up(4 * S * Qm)
     assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, 0) == 0
     assert pkv.multi_workspace_bytes(0, Qm, Hq, D, L, P) == 0
-    # balanced: header, S + 1 prefix words, 16 columns per chunk slot
+    # balanced: header, S + 1 prefix words, 2 words of chunk range per
+    # stream (for up to Hq KV heads), 16 columns per chunk slot
     n = 2 * (5 * 2048 + 8) * 16
-    assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, -1) == up(256 + 4 * (S + 1)) + 2 * up(4 * n) + \
-        4 * n * D
+    assert pkv.multi_workspace_bytes(S, Qm, Hq, D, L, -1) == \
+        up(256 + 4 * (S + 1) + 8 * S * Hq) + 2 * up(4 * n) + 4 * n * D
 
 
 def mixed_args(**kw):
