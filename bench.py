@@ -63,9 +63,11 @@ def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int):
     """The balanced split's pieces, replayed on the host: the streams
     (sequence, KV head) of 16-token tiles laid end to end and cut into chunks
     by the guided schedule (nW chunks of max(1, 4A/5) tiles, nW of
-    max(A/7, F), then max(A/16, F), A = T / nW, F = max(floor, 4)).  Returns
-    (number of streams spread over several chunks, partial entries they write
-    per query head)."""
+    max(A/7, F), then max(A/16, F), A = T / nW, F = max(floor, 4)), each cut
+    inside a stream moved to the nearer end of that stream when it lies
+    within a quarter of the smaller neighbouring chunk.  Returns (number of
+    streams spread over several chunks, partial entries they write per query
+    head)."""
     nt = -(-np.maximum(lens.astype(np.int64), 0) // 16)
     T = int(nt.sum()) * Hkv
     if T == 0:
@@ -73,18 +75,32 @@ def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int):
     A = T // nW
     F = max(floor, 4)
     C1, C2, C3 = max(1, A * 4 // 5), max(F, A // 7), max(F, A // 16)
-    e1, e2 = min(nW * C1, T), min(nW * (C1 + C2), T)
-
-    def chunk_of(x):
-        return np.where(x < e1, x // C1,
-                        np.where(x < e2, nW + (x - e1) // C2, 2 * nW + (x - e2) // C3))
-
+    if nW * C1 >= T:
+        chunks = -(-T // C1)
+    elif nW * (C1 + C2) >= T:
+        chunks = nW + -(-(T - nW * C1) // C2)
+    else:
+        chunks = 2 * nW + -(-(T - nW * (C1 + C2)) // C3)
+    c = np.arange(chunks + 1, dtype=np.int64)
+    plain = np.where(c <= nW, c * C1,
+                     np.where(c <= 2 * nW, nW * C1 + (c - nW) * C2,
+                              nW * (C1 + C2) + (c - 2 * nW) * C3))
+    plain = np.minimum(plain, T)
     g0 = (np.repeat(np.cumsum(nt) - nt, Hkv) * Hkv
           + np.tile(np.arange(Hkv), lens.size) * np.repeat(nt, Hkv))
     g1 = g0 + np.repeat(nt, Hkv)
     live = g1 > g0
-    c0 = chunk_of(g0)
-    c1 = chunk_of(np.maximum(g1 - 1, 0))
+    # move the inner cuts
+    lo_s, hi_s = g0[live], g1[live]
+    b = plain[1:-1]
+    d = np.minimum(b - plain[:-2], plain[2:] - b) // 4
+    k = np.searchsorted(lo_s, b, side="right") - 1
+    r = b - lo_s[k]
+    up = hi_s[k] - b
+    moved = np.where(r <= d, b - r, np.where(up <= d, b + up, b))
+    starts = np.concatenate([plain[:1], moved, plain[-1:]])
+    c0 = np.searchsorted(starts, g0, side="right") - 1
+    c1 = np.searchsorted(starts, np.maximum(g1 - 1, 0), side="right") - 1
     split = live & (c1 > c0)
     return int(split.sum()), int((c1 - c0 + 1)[split].sum())
 

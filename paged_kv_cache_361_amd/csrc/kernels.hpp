@@ -83,13 +83,16 @@ struct ReduceParams {
 // per SIMD: neighbouring divisors were 1-15 us slower per call; on short fp8
 // runs, floors of 4 and 12 tiles were 16 and 6 us slower than 20, and 30 or
 // 40 slower again.)  Chunk c starts at tile
-// chunk_begin(c); the decode grid takes chunks 0..nW-1 statically and the
-// rest from a counter, and the reduce finds a stream's chunks with
-// chunk_of().
+// chunk_begin(c), moved by the decode to a nearby stream end where one is
+// close; the decode grid takes chunks 0..nW-1 statically and the rest from
+// a counter, and records for every stream its first and last chunk, which
+// is how the reduce finds a stream's entries.
 //
 // Workspace: a 256-byte header, the exclusive tile prefix of the sequences
-// (S + 1 words) from byte 256, then (m, l, o) entries, two per query head of
-// the group per chunk.  Header words 0-9 describe the split for the reduce
+// (S + 1 words) from byte 256 followed by two words per (sequence, KV head)
+// stream (its first chunk, with the slot of its piece there in bit 31, and
+// its last chunk), then (m, l, o) entries, two per query head of the group
+// per chunk.  Header words 0-9 describe the split for the reduce
 // (written by each decode call).  Words 32-33 (their own 128-byte line) hold
 // the chunk counter, a 64-bit word: high half the number of the call that
 // owns it, low half kCountTag | count.  Nothing resets it between calls: a
@@ -146,13 +149,6 @@ __host__ __device__ inline int chunk_begin(const Sched& q, int c) {
     else if (c <= 2 * q.nW) b = (int64_t)q.nW * q.C1 + (int64_t)(c - q.nW) * q.C2;
     else b = (int64_t)q.nW * (q.C1 + q.C2) + (int64_t)(c - 2 * q.nW) * q.C3;
     return (int)(b < q.T ? b : q.T);
-}
-
-// Chunk holding tile x (0 <= x < T).
-__host__ __device__ inline int chunk_of(const Sched& q, int x) {
-    if (x < q.e1) return x / q.C1;
-    if (x < q.e2) return q.nW + (x - q.e1) / q.C2;
-    return 2 * q.nW + (x - q.e2) / q.C3;
 }
 
 // Most chunks any batch can produce on a grid of nW waves (the workspace

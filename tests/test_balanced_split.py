@@ -5,16 +5,18 @@ KV head) stream and cuts them into chunks by a guided schedule that depends
 only on the tile count T, the grid size nW and a floor (two rounds of the
 decode's tile ring, 8 to 20 tiles): nW chunks of C1 = max(1, 4A/5) tiles, nW
 of C2 = max(A/7, F), then chunks of C3 = max(A/16, F), with A = T / nW and
-F = max(floor, 4).  Inside a chunk a piece of a stream is a
-segment: a whole stream writes its output, any other segment is the first
-(slot 0) or last (slot 1) of its chunk.  The reduce finds the chunks of a
-stream with chunk_of() and reads slot 1 of the first one when the stream
-starts inside it.  These tests replay the same integer formulas (written
-again here from that description) and check what the two kernels rely on:
-chunks tile [0, T) without gaps or empty chunks, chunk_of inverts the chunk
-starts, the chunk count stays under the workspace bound 5 nW + 8, at most two
-partial segments per chunk, in the slots the reduce reads, and the pieces of
-every split stream cover it exactly once."""
+F = max(floor, 4).  A cut that falls inside a stream moves to the nearer
+end of that stream when it lies within a quarter of the smaller of the two
+chunks the cut separates.  Inside a chunk a piece of a stream is a segment: a whole
+stream writes its output, any other segment is the first (slot 0) or last
+(slot 1) of its chunk.  The decode records each stream's first chunk (and
+whether its piece there is slot 1) and last chunk, and the reduce reads
+them.  These tests replay the same integer formulas (written again here
+from that description) and check what the two kernels rely on: chunks tile
+[0, T) without gaps or empty chunks, the chunk count stays under the
+workspace bound 5 nW + 8, at most two partial segments per chunk, in the
+slots the reduce reads, and the pieces of every split stream cover it
+exactly once."""
 import numpy as np
 import pytest
 
@@ -47,12 +49,27 @@ def chunk_begin(q, c):
     return min(b, q["T"])
 
 
-def chunk_of(q, x):
-    if x < q["e1"]:
-        return x // q["C1"]
-    if x < q["e2"]:
-        return q["nW"] + (x - q["e1"]) // q["C2"]
-    return 2 * q["nW"] + (x - q["e2"]) // q["C3"]
+def chunk_start(q, c, strm):
+    """chunk_begin moved to the nearer end of the stream it falls in, when
+    that end is within a quarter of the smaller neighbouring chunk."""
+    b = chunk_begin(q, c)
+    if c <= 0 or c >= q["chunks"]:
+        return b
+    d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) // 4
+    for g0, g1 in strm:
+        if g0 <= b < g1:
+            r = b - g0
+            if r <= d:
+                return g0
+            if g1 - b <= d:
+                return g1
+            return b
+    return b
+
+
+def chunk_holding(starts, x):
+    """The chunk c with starts[c] <= x < starts[c + 1]."""
+    return int(np.searchsorted(starts, x, side="right")) - 1
 
 
 def streams(lens, Hkv):
@@ -88,11 +105,16 @@ def test_split_properties(lens, Hkv, nW, floor):
     if T == 0:
         assert q["chunks"] == 0
         return
-    starts = [chunk_begin(q, c) for c in range(q["chunks"] + 1)]
+    plain = [chunk_begin(q, c) for c in range(q["chunks"] + 1)]
+    starts = [chunk_start(q, c, strm) for c in range(q["chunks"] + 1)]
     assert starts[0] == 0 and starts[-1] == T
-    assert all(starts[c + 1] > starts[c] for c in range(q["chunks"]))     # none empty
+    # none empty: each chunk keeps at least half its tiles
     for c in range(q["chunks"]):
-        assert chunk_of(q, starts[c]) == c and chunk_of(q, starts[c + 1] - 1) == c
+        assert 2 * (starts[c + 1] - starts[c]) >= plain[c + 1] - plain[c] > 0
+    # a moved cut lands on a stream end
+    ends = {g for st in strm for g in st}
+    for c in range(q["chunks"] + 1):
+        assert starts[c] == plain[c] or starts[c] in ends
     # per chunk: middle segments are whole streams; partial ones are first/last
     slot_of = {}
     for c in range(q["chunks"]):
@@ -107,7 +129,7 @@ def test_split_properties(lens, Hkv, nW, floor):
     for i, (g0, g1) in enumerate(strm):
         if g1 == g0:
             continue
-        c0, c1 = chunk_of(q, g0), chunk_of(q, g1 - 1)
+        c0, c1 = chunk_holding(starts, g0), chunk_holding(starts, g1 - 1)
         if c0 == c1:
             assert (i, c0) not in slot_of          # finished by the decode
             continue
