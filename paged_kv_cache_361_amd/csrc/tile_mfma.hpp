@@ -44,6 +44,7 @@
 // 8-bit rounding left in the kernel is the stored output itself.
 #pragma once
 
+#include <cfloat>
 #include <type_traits>
 
 #include "common.hpp"
@@ -228,7 +229,10 @@ struct TileMath {
     __device__ inline void reset(Acc& a) const {
 #pragma unroll
         for (int n = 0; n < NT; n++) a.o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        a.m = -INFINITY;
+        // below every score, but finite: a column that has seen nothing
+        // yet (masked rows score -inf) gets weights exp2(-inf - m) = 0, not
+        // the NaN of -inf - -inf
+        a.m = -FLT_MAX;
         a.l = 0.0f;
     }
 
@@ -298,7 +302,7 @@ struct TileMath {
     // as for issue(); rows past it get no weight.  CAUSAL: the B columns are
     // query tokens as well as heads, and column lane%16 also drops the rows
     // past clim (its own limit within the tile); a column can then have
-    // seen no token yet, so weights of dropped rows are forced to zero.
+    // seen no token yet, which the finite starting max of reset() covers.
     // MASK = false: the caller knows that every column it keeps sees every
     // row of the tile, so no limit is applied (the same result, fewer
     // vector instructions).
@@ -398,9 +402,7 @@ struct TileMath {
         }
         float pz[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            pz[r] = (CAUSAL && MASK && z[r] == -INFINITY) ? 0.0f
-                                                          : __builtin_amdgcn_exp2f(z[r] - a.m);
+        for (int r = 0; r < 4; r++) pz[r] = __builtin_amdgcn_exp2f(z[r] - a.m);
         a.l += (pz[0] + pz[1]) + (pz[2] + pz[3]);
 
         // ---- weights as the A operand ----
