@@ -59,16 +59,18 @@ def chunk_floor(cache_dtype: str, bs: int, D: int) -> int:
     return 2 * depth
 
 
-def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int):
+def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int, tile_tokens=None):
     """The balanced split's pieces, replayed on the host: the streams
     (sequence, KV head) of 16-token tiles laid end to end and cut into chunks
     by the guided schedule (nW chunks of max(1, 4A/5) tiles, nW of
     max(A/7, F), then max(A/16, F), A = T / nW, F = max(floor, 4)), each cut
     inside a stream moved to the nearer end of that stream when it lies
-    within a quarter of the smaller neighbouring chunk.  Returns (number of
-    streams spread over several chunks, partial entries they write per query
-    head)."""
-    nt = -(-np.maximum(lens.astype(np.int64), 0) // 16)
+    within a quarter of the smaller neighbouring chunk.  tile_tokens: each
+    sequence's tile (mixed block sizes: 8 for 8-token blocks), default 16.
+    Returns (number of streams spread over several chunks, partial entries
+    they write per query head)."""
+    tt = 16 if tile_tokens is None else np.asarray(tile_tokens, np.int64)
+    nt = -(-np.maximum(lens.astype(np.int64), 0) // tt)
     T = int(nt.sum()) * Hkv
     if T == 0:
         return 0, 0
@@ -105,7 +107,7 @@ def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int):
     return int(split.sum()), int((c1 - c0 + 1)[split].sum())
 
 
-def decode_bytes(c, P: int, nW: int = 0) -> dict:
+def decode_bytes(c, P: int, nW: int = 0, tile_tokens=None, floor_bs=None) -> dict:
     """Algorithmic bytes one decode launch (and its reduce) must move: each KV
     head's rows once per group, Q in, O out, the table entries used, the
     lengths, and for split-K the partials written once and read once."""
@@ -122,8 +124,8 @@ def decode_bytes(c, P: int, nW: int = 0) -> dict:
     elif P < 0:
         # a split (sequence, KV head) stream writes one entry per piece for each
         # query head of its group; its G output rows come from the reduce
-        split_streams, entries = balanced_split(L, c.Hkv, nW,
-                                                chunk_floor(c.cache_dtype, c.bs, c.D))
+        split_streams, entries = balanced_split(
+            L, c.Hkv, nW, chunk_floor(c.cache_dtype, floor_bs or c.bs, c.D), tile_tokens)
         n_multi = split_streams / c.Hkv          # in units of whole sequences
         partials = entries * c.G * (c.D + 2) * 4
     # decode: K/V, Q, O of sequences it finishes, table, lengths, partials out
@@ -638,7 +640,7 @@ def bench_mixed(args) -> int:
     log("generating workload %s ..." % args.workload)
     mc = workloads.mixed_block_sizes()
     c = mc.case
-    P = 512 if args.partition is None else args.partition
+    P = -1 if args.partition is None else args.partition      # the balanced split
 
     def dev(a, d):
         if d == "bf16":
@@ -686,7 +688,10 @@ def bench_mixed(args) -> int:
     t_total = time.perf_counter() - t0
     dec_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     red_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    b = decode_bytes(c, P)
+    nW = int(ws[:16].cpu().numpy().view(np.int32)[1]) if P < 0 else 0
+    # the balanced walk takes 8-token tiles for 8-token blocks and the ring
+    # of 16-token blocks
+    b = decode_bytes(c, P, nW, tile_tokens=np.where(mc.seq_bs == 8, 8, 16), floor_bs=16)
     L = c.seq_lens.astype(np.int64)
     # table entries: one per block of each sequence's own size, plus the sizes
     table_fix = 4 * int((-(-L // mc.seq_bs.astype(np.int64))).sum()) + 4 * c.S \

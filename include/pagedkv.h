@@ -272,12 +272,14 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* query, pkv_dtype q
  *   page_size and num_blocks = num_pages).
  *
  * What is computed, the other arguments, partition_size (P > 0: a multiple
- * of 32; the partials then go to the workspace of
- * pkv_decode_workspace_bytes with the same sizes and P, and
- * pkv_paged_attention_reduce merges them) and the errors are as for
+ * of 32; PKV_PARTITION_BALANCED: the balanced split, each sequence walked
+ * over its own block size, 8-token blocks in 8-token tiles; either way the
+ * partials go to the workspace of pkv_decode_workspace_bytes with the same
+ * sizes and partition_size, and pkv_paged_attention_reduce with that
+ * partition_size merges them) and the errors are as for
  * pkv_paged_attention_decode with block_size = page_size and num_blocks =
  * num_pages, for the matrix-core type combinations (f16/bf16 query;
- * f16/bf16/fp8 cache; head_dim 64 or 128; G <= 16; no balanced split).
+ * f16/bf16/fp8 cache; head_dim 64 or 128; G <= 16).
  * Also PKV_ERR_NULL for a NULL seq_block_sizes ([num_seqs] int32, device);
  * PKV_ERR_SHAPE for a pool smaller than 32 tokens or P not a multiple of 32.
  * Preconditions: each bs_s is 8, 16 or 32 and at least page_size (other

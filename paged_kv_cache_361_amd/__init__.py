@@ -221,8 +221,9 @@ def paged_attention_decode_mixed(out: torch.Tensor, query: torch.Tensor,
     """Decode over a pool of pages (caches [num_pages, page, Hkv, D]) whose
     sequences have blocks of seq_block_sizes[s] tokens (8, 16 or 32; int32
     [S]), each that many / page consecutive pages from the page the table
-    names.  partition_size P > 0 (a multiple of 32): call
-    paged_attention_reduce next, as for paged_attention_decode."""
+    names.  partition_size P > 0 (a multiple of 32) or PARTITION_BALANCED:
+    call paged_attention_reduce next with the same partition_size, as for
+    paged_attention_decode."""
     S, Hq, D = query.shape
     NP, page, Hkv, _ = k_cache.shape
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

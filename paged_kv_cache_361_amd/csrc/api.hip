@@ -433,9 +433,10 @@ int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_d
                                      size_t workspace_bytes, hipStream_t stream) {
     if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_DTYPE;
     if (!valid_decode_types(q_dtype, cache_dtype)) return PKV_ERR_DTYPE;
+    const bool balanced = partition_size == PKV_PARTITION_BALANCED;
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         page_size <= 0 || num_pages <= 0 || max_blocks_per_seq <= 0 || max_seq_len <= 0 ||
-        partition_size < 0)
+        (partition_size < 0 && !balanced))
         return PKV_ERR_SHAPE;
     if (num_q_heads % num_kv_heads != 0) return PKV_ERR_SHAPE;
     if (num_kv_heads > 4096) return PKV_ERR_SHAPE;
@@ -489,17 +490,31 @@ int pkv_paged_attention_decode_mixed(void* out, const void* query, pkv_dtype q_d
     const float ks = cache_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f;
     p.scale_log2 = scale * ks * kLog2e;
     p.v_scale = cache_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
-    if (partition_size > 0) {
+    if (partition_size != 0) {
         WsLayout w;
         if (!ws_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
                        partition_size, &w))
             return PKV_ERR_SHAPE;
         if (!workspace || workspace_bytes < w.bytes) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
-        p.P_max = w.P_max;
+        p.P_max = balanced ? 1 : w.P_max;
+        p.ws_hdr = (int32_t*)workspace;
+        p.ws_pre = (int32_t*)((char*)workspace + w.off_pre);
         p.ws_m = (float*)((char*)workspace + w.off_m);
         p.ws_l = (float*)((char*)workspace + w.off_l);
         p.ws_o = (float*)((char*)workspace + w.off_o);
+    }
+    if (balanced) {
+        // the balanced split's walk over each sequence's own block size
+        // (8-token tiles for 8-token blocks); pkv_paged_attention_reduce
+        // merges the pieces as after a uniform pool
+        const int64_t tiles = (int64_t)num_seqs * num_kv_heads * ((p.len_cap + 7) / 8);
+        if (tiles > ((int64_t)1 << 31) - 1) return PKV_ERR_SHAPE;
+        if (num_seqs > kBalancedMaxSeqs) return PKV_ERR_UNSUPPORTED;
+        p.P = 0;
+        p.nW = balanced_grid_waves(q_dtype, cache_dtype, head_dim, 16);
+        p.epoch = next_call_number();
+        return launch_status(launch_decode_balanced(q_dtype, cache_dtype, p, stream));
     }
     const int64_t units = (int64_t)num_seqs * p.P_max * num_kv_heads;
     if (units > ((int64_t)1 << 31) - 64) return PKV_ERR_SHAPE;

@@ -97,7 +97,23 @@ __device__ inline int counter_rebase(unsigned long long* ctr, uint32_t epoch) {
     return __builtin_amdgcn_readfirstlane(k);
 }
 
-__device__ inline int seq_tiles(int L) { return L > 0 ? (L + 15) >> 4 : 0; }
+// Tiles of a sequence of L tokens in tiles of 2^ts tokens (ts = 4: 16-token
+// tiles; ts = 3: the 8-token tiles of 8-token blocks with mixed block sizes).
+__device__ inline int seq_tiles(int L, int ts = 4) { return L > 0 ? (L + (1 << ts) - 1) >> ts : 0; }
+
+// Mixed block sizes: a sequence's geometry, packed in one LDS word: log2 of
+// its block size (low byte) and of its tile (next byte).  A block of 8
+// tokens takes 8-token tiles (rows 8-15 of the 16-row matrix-core tile
+// dead), so that every tile lies inside one block; 16- and 32-token blocks
+// take 16-token tiles.  Uniform pools pass the pool's block size.
+__device__ inline int geo_pack(int shift, int ts) { return shift | (ts << 8); }
+__device__ inline int geo_shift(int g) { return g & 255; }
+__device__ inline int geo_ts(int g) { return g >> 8; }
+// The same in 3 bits (block shift 3..5, tile shift 3..4), kept in a span's
+// key above the sequence and head (no extra scalar register per span).
+__device__ inline int geo_code(int g) { return (geo_shift(g) - 3) | ((geo_ts(g) - 3) << 2); }
+__device__ inline int code_shift(int c) { return (c & 3) + 3; }
+__device__ inline int code_ts(int c) { return (c >> 2) + 3; }
 
 // A copy of a loaded value made by an instruction the compiler cannot see
 // through, so that it waits for that one load here.  Used on rare paths
@@ -114,8 +130,11 @@ __device__ inline int settled(int x) {
 
 // Every workgroup computes the batch's tile prefix in LDS from the lengths:
 // len[s] = clamped length of sequence s, pre[s] = tiles of the streams of
-// all sequences before s (pre[S] = T).
-__device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
+// all sequences before s (pre[S] = T).  MIXED: geo[s] = the sequence's
+// geometry (its block size from p.seq_bs, as decode_mixed_kernel reads it),
+// and its length is also clamped to what its table can hold.
+template <bool MIXED>
+__device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len, int* geo) {
     __shared__ int wave_sum[kWaves];
     constexpr int NT = 64 * kWaves;
     const int tid = threadIdx.x;
@@ -124,14 +143,23 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
     // lengths into LDS with coalesced loads, then a scan over contiguous
     // ranges of `per` sequences per thread
 #pragma unroll 4
-    for (int s = tid; s < p.S; s += NT) len[s] = min(p.lens[s], p.len_cap);
+    for (int s = tid; s < p.S; s += NT) {
+        int L = min(p.lens[s], p.len_cap);
+        if constexpr (MIXED) {
+            const int bs = p.seq_bs[s];
+            const int shift = bs >= 32 ? 5 : max(bs >= 16 ? 4 : 3, p.page_shift);
+            geo[s] = geo_pack(shift, shift == 3 ? 3 : 4);
+            L = min(L, p.max_blocks << shift);
+        }
+        len[s] = L;
+    }
     __syncthreads();
     const int per = (p.S + NT - 1) / NT;
     const int s0 = tid * per;
     int n = 0;
     for (int i = 0; i < per; i++) {
         const int s = s0 + i;
-        if (s < p.S) n += seq_tiles(len[s]) * p.Hkv;
+        if (s < p.S) n += seq_tiles(len[s], MIXED ? geo_ts(geo[s]) : 4) * p.Hkv;
     }
     const int incl = wave_incl_scan(n);
     if (lane == 63) wave_sum[wv] = incl;
@@ -147,7 +175,7 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
         const int s = s0 + i;
         if (s < p.S) {
             pre[s] = run;
-            run += seq_tiles(len[s]) * p.Hkv;
+            run += seq_tiles(len[s], MIXED ? geo_ts(geo[s]) : 4) * p.Hkv;
         }
     }
     if (tid == 0) pre[p.S] = total;
@@ -165,7 +193,8 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len) {
 // tiles), chunk 0 starts at 0 and the last ends at T; the reduce reads each
 // stream's chunks from what the decode records, so it needs no copy of this
 // rule.
-__device__ inline int chunk_start(const Sched& q, int c, const int* pre, const int* len, int S) {
+__device__ inline int chunk_start(const Sched& q, int c, const int* pre, const int* len,
+                                   const int* geo, int S) {
     const int b = chunk_begin(q, c);
     if (c <= 0 || c >= q.chunks) return b;
     const int d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) / 4;
@@ -176,7 +205,8 @@ __device__ inline int chunk_start(const Sched& q, int c, const int* pre, const i
         if (__builtin_amdgcn_readfirstlane(pre[mid]) <= b) lo = mid;
         else hi = mid;
     }
-    const int nt = seq_tiles(__builtin_amdgcn_readfirstlane(len[lo]));
+    const int ts = geo ? geo_ts(__builtin_amdgcn_readfirstlane(geo[lo])) : 4;
+    const int nt = seq_tiles(__builtin_amdgcn_readfirstlane(len[lo]), ts);
     const int r = (b - __builtin_amdgcn_readfirstlane(pre[lo])) % nt;
     if (r <= d) return b - r;
     if (nt - r <= d) return b + nt - r;
@@ -192,30 +222,35 @@ enum : int { kFirst = 1, kLast = 2, kComplete = 4, kSlot1 = 8, kStart = 16, kEnd
 // window starting at block wb, inside chunk `chunk`.  Wave-uniform; kept
 // small because three of them live in scalar registers.
 struct Span {
-    int key;           // s << 12 | h
+    int key;           // geometry code (mixed block sizes) << 25 | s << 12 | h
     int L, t0, t1, wb, chunk;
     int flags;         // kFirst: first span of its segment; kLast: last;
                        // kComplete: the segment is the whole stream;
                        // kSlot1: not the first segment of its chunk;
                        // (last span) kStart: the segment starts the stream,
                        // kEnd: it ends it
-    __device__ int s() const { return key >> 12; }
+    template <bool MIXED>
+    __device__ int seq() const { return MIXED ? (key >> 12) & 0x1FFF : key >> 12; }
+    __device__ int s() const { return (key >> 12) & 0x1FFF; }
     __device__ int h() const { return key & 4095; }
+    __device__ int code() const { return key >> 25; }
 };
 
 // Wave-uniform walk over one chunk, span by span.  pre and len are the LDS
-// copies of the tile prefix and of the clamped lengths.
+// copies of the tile prefix and of the clamped lengths; geo those of the
+// sequences' geometries (nullptr: every sequence has geometry `g0`).
 struct Walk {
     int s, h, tile;    // next tile: stream (s, h), tile index
     int L;             // clamped length of sequence s
+    int g;             // its geometry (geo_pack)
     int rem;           // tiles of the chunk not yet walked
     int chunk;
     int wf;            // 1: the current segment continues in the next span;
                        // 2: it started at tile 0; 4: a segment already ended
                        // in this chunk
 
-    __device__ inline void start(const int* pre, const int* len, int S, int c, int x0,
-                                 int x1) {
+    __device__ inline void start(const int* pre, const int* len, const int* geo, int g0, int S,
+                                 int c, int x0, int x1) {
         // the sequence whose streams hold tile x0: pre[s] <= x0 < pre[s + 1]
         int lo = 0, hi = S;
         while (hi - lo > 1) {
@@ -225,7 +260,8 @@ struct Walk {
         }
         s = lo;
         L = __builtin_amdgcn_readfirstlane(len[s]);
-        const int nt = seq_tiles(L);
+        g = geo ? __builtin_amdgcn_readfirstlane(geo[s]) : g0;
+        const int nt = seq_tiles(L, geo ? geo_ts(g) : 4);
         const int off = x0 - __builtin_amdgcn_readfirstlane(pre[s]);
         h = off / nt;
         tile = off % nt;
@@ -234,9 +270,10 @@ struct Walk {
         wf = 0;
     }
 
-    __device__ inline bool next(const int* len, int S, int Hkv, int bs_shift, Span& o) {
+    __device__ inline bool next(const int* len, const int* geo, int S, int Hkv, int bs_shift,
+                                Span& o) {
         if (rem <= 0) return false;
-        int nt = seq_tiles(L);
+        int nt = seq_tiles(L, geo ? geo_ts(g) : 4);
         while (tile >= nt) {               // stream exhausted: move on
             tile = 0;
             wf &= ~1;
@@ -245,7 +282,8 @@ struct Walk {
                 do {
                     if (++s >= S) return false;    // not reached while rem > 0
                     L = __builtin_amdgcn_readfirstlane(len[s]);
-                    nt = seq_tiles(L);
+                    if (geo) g = __builtin_amdgcn_readfirstlane(geo[s]);
+                    nt = seq_tiles(L, geo ? geo_ts(g) : 4);
                 } while (nt == 0);
             }
         }
@@ -255,11 +293,12 @@ struct Walk {
             wf = (wf & 4) | (tile == 0 ? 2 : 0);
         }
         if (wf & 4) f |= kSlot1;
-        o.key = (s << 12) | h;
+        o.key = (s << 12) | h | (geo ? geo_code(g) << 25 : 0);
         o.L = L;
         o.t0 = tile;
-        o.wb = (tile << 4) >> bs_shift;
-        const int wend = ((o.wb + 64) << bs_shift) >> 4;   // first tile past the window
+        const int shift = geo ? geo_shift(g) : bs_shift, ts = geo ? geo_ts(g) : 4;
+        o.wb = (tile << ts) >> shift;
+        const int wend = ((o.wb + 64) << shift) >> ts;     // first tile past the window
         int t1 = min(nt, tile + rem);
         t1 = min(t1, wend);
         o.t1 = t1;
@@ -287,8 +326,12 @@ struct Walk {
 // of decode; the B operand's 16 columns are (query token, head) pairs as in
 // multi_query.hip, each column drops the tokens past its own position, and
 // rows and partial entries are per column (QPG * G of them per chunk slot).
-template <class Q, class C, int D, bool PAIR, int DEPTH, bool MULTI>
+// MIXED: block sizes per sequence over a pool of pages (p.bs tokens each,
+// as decode_mixed_kernel): each sequence walks its own block size, and
+// sequences of 8-token blocks walk 8-token tiles.
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool MULTI, bool MIXED>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeParams p) {
+    static_assert(!(MULTI && MIXED) && !(PAIR && MIXED), "one mode at a time");
     typedef TileMath<Q, C, D, PAIR> TM;
     typedef typename TM::T T;
     typedef typename TM::v8 v8;
@@ -296,11 +339,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     int* pre = lds;                        // [S + 1] tile prefix
     int* len = lds + p.S + 1;              // [S] clamped lengths
     int* qs = lds + 2 * p.S + 1;           // MULTI: [S + 1] query_start
+    int* geo = lds + 2 * p.S + 1;          // MIXED: [S] geometries
     int32_t* hdr = p.ws_hdr;
     if constexpr (MULTI) {
         for (int i = threadIdx.x; i <= p.S; i += 64 * kWaves) qs[i] = p.q_start[i];
     }
-    wg_prefix(p, pre, len);
+    wg_prefix<MIXED>(p, pre, len, geo);
 
     const TM tm;
     const int lane = tm.lane;
@@ -326,6 +370,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     if (w >= q.chunks || w >= p.nW) return;
     const int G = p.G;
     const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
+    const int* geo_s = MIXED ? geo : nullptr;             // per sequence, or
+    const int geo0 = MIXED ? 0 : geo_pack(bs_shift, 4);  // the pool's (unread)
     unsigned long long* counter = (unsigned long long*)(hdr + kHdrCounter);
     const int QPG = MULTI ? 16 / G : 1;    // query tokens per stream
     const int ncol = QPG * G;              // columns (rows) per stream
@@ -372,24 +418,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     // Within a chunk the walk looks one span ahead; it steps into the next
     // chunk only once that chunk's index is at hand.
     Walk pw;
-    pw.start(pre, len, p.S, w, chunk_start(q, w, pre, len, p.S),
-             chunk_start(q, w + 1, pre, len, p.S));
-    auto walk_next = [&](Span& o) { return pw.next(len, p.S, p.Hkv, bs_shift, o); };
+    pw.start(pre, len, geo_s, geo0, p.S, w, chunk_start(q, w, pre, len, geo_s, p.S),
+             chunk_start(q, w + 1, pre, len, geo_s, p.S));
+    auto walk_next = [&](Span& o) { return pw.next(len, geo_s, p.S, p.Hkv, bs_shift, o); };
     auto chunk_next = [&](Span& o) {       // first span of the next chunk
         const int c = take_chunk();
         if (c >= q.chunks) {
             chunks_left = false;
             return false;
         }
-        pw.start(pre, len, p.S, c, chunk_start(q, c, pre, len, p.S),
-                 chunk_start(q, c + 1, pre, len, p.S));
+        pw.start(pre, len, geo_s, geo0, p.S, c, chunk_start(q, c, pre, len, geo_s, p.S),
+                 chunk_start(q, c + 1, pre, len, geo_s, p.S));
         return walk_next(o);               // chunks are never empty
     };
     // Window of 64 block-table entries from block sp.wb; entries at or past
     // ceil(L / bs) are outside the descriptor and read 0 (never touched).
     auto load_window = [&](const Span& sp, bool want) {
-        const int nblk = want ? (sp.L + p.bs - 1) >> bs_shift : 0;
-        const rsrc_t r = make_rsrc((const char*)(p.tables + (size_t)sp.s() * p.max_blocks),
+        int nblk;
+        if constexpr (MIXED) {
+            const int sh = code_shift(sp.code());
+            nblk = want ? (sp.L + (1 << sh) - 1) >> sh : 0;
+        } else {
+            nblk = want ? (sp.L + p.bs - 1) >> bs_shift : 0;
+        }
+        const rsrc_t r = make_rsrc((const char*)(p.tables + (size_t)sp.template seq<MIXED>() * p.max_blocks),
                                    (uint32_t)nblk * 4u);
         return (int)Buf<4>::load(r, (uint32_t)(sp.wb + lane) * 4u);
     };
@@ -403,7 +455,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     int ps_q0 = 0, ps_n = 0;
     // Query rows of the span's group as the B operand (heads past G read 0).
     auto load_query = [&](const Span& sp, bool want, v8 (&qv)[TM::KS]) {
-        size_t first_row = (size_t)sp.s();
+        size_t first_row = (size_t)sp.template seq<MIXED>();
         uint32_t range = (uint32_t)(G * D * sizeof(T));
         uint32_t row = (uint32_t)(tm.j16 * D * sizeof(T));
         if constexpr (MULTI) {
@@ -423,8 +475,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     Span ps, pn;
     walk_next(ps);                         // chunk w is not empty
     if constexpr (MULTI) {
-        ps_q0 = q_first(ps.s());
-        ps_n = q_count(ps.s());
+        ps_q0 = q_first(ps.template seq<MIXED>());
+        ps_n = q_count(ps.template seq<MIXED>());
     }
     v8 qb[TM::KS];                         // query of the consumer's segment
     load_query(ps, true, qb);
@@ -432,7 +484,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     bool has_ps = true;
     bool has_pn = walk_next(pn);
     int win_n = load_window(pn, has_pn);   // window of pn
-    Head hd = make_head<C, D>(p, ps.h());
+    // K/V of the span's stream; MIXED: blocks of the sequence's size, each
+    // (1 << shift) / p.bs consecutive pages from the page its entry names
+    auto head_of = [&](const Span& sp) {
+        Head hd = make_head<C, D>(p, sp.h());
+        if constexpr (MIXED) {
+            const int sh = code_shift(sp.code());
+            hd.bs_shift = sh;
+            hd.rec_bytes = (hd.row_bytes << sh) - (uint32_t)(sp.h() * D * C::kBytes);
+            hd.nb_last = (uint32_t)(p.NB - (1 << (sh - p.page_shift)));
+        }
+        return hd;
+    };
+    Head hd = head_of(ps);
     int prt = ps.t0;
 
     bool want_win = false, want_q = false;  // set when pn / ps change
@@ -449,12 +513,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             if (has_ps) {
                 ps = pn;
                 if constexpr (MULTI) {
-                    ps_q0 = q_first(ps.s());
-                    ps_n = q_count(ps.s());
+                    ps_q0 = q_first(ps.template seq<MIXED>());
+                    ps_n = q_count(ps.template seq<MIXED>());
                 }
                 win = win_n;
                 prt = ps.t0;
-                hd = make_head<C, D>(p, ps.h());
+                hd = head_of(ps);
                 want_q = (ps.flags & kFirst) != 0;
                 has_pn = walk_next(pn);
                 want_win = has_pn;
@@ -503,10 +567,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
 #pragma unroll
     for (int j = 0; j < DEPTH; j++) {
         const int tp = prt + j;
-        tm.issue(hd, tp << 4, tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1, ps.wb, win, tl[j]);
+        if constexpr (MIXED) {
+            const int ts = code_ts(ps.key >> 25);
+            tm.issue(hd, tp << ts, tp < ps.t1 ? min(ps.L - 1 - (tp << ts), (1 << ts) - 1) : -1,
+                     ps.wb, win, tl[j]);
+        } else
+            tm.issue(hd, tp << 4, tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1, ps.wb, win, tl[j]);
     }
     // consumer's span: its stream, length, end tile, chunk and flags
     int c_key = ps.key, c_L = ps.L, c_t1 = ps.t1, c_chunk = ps.chunk, c_flags = ps.flags;
+    int c_ts = MIXED ? code_ts(ps.key >> 25) : 4;   // log2 of the consumer's tile
     int crt = ps.t0;
     // MULTI: this lane's column's last visible token in the consumer's
     // sequence (-1: none)
@@ -529,11 +599,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                     tm.template consume<true>(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j],
                                               c_pc - (tc << 4));
                 else
-                    tm.consume(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j]);
+                    tm.consume(acc, qb, p.scale_log2,
+                               MIXED ? min(c_L - 1 - (tc << c_ts), (1 << c_ts) - 1)
+                                     : c_L - 1 - (tc << 4),
+                               tl[j]);
             }
             const int tp = prt + j;
-            const int plim = has_ps && tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1;
-            tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j]);
+            if constexpr (MIXED) {
+                const int ts = code_ts(ps.key >> 25);
+                const int plim =
+                    has_ps && tp < ps.t1 ? min(ps.L - 1 - (tp << ts), (1 << ts) - 1) : -1;
+                tm.issue(hd, tp << ts, plim, ps.wb, win, tl[j]);
+            } else {
+                const int plim = has_ps && tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1;
+                tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j]);
+            }
         }
         take();
         // Consumer first: finish its span and take the producer's current
@@ -546,7 +626,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                 // the one that ends it the last
                 if (lane == 0 && (c_flags & (kStart | kEnd))) {
                     int32_t* rng = p.ws_pre + p.S + 1 +
-                                   2 * ((c_key >> 12) * p.Hkv + (c_key & 4095));
+                                   2 * ((MIXED ? (c_key >> 12) & 0x1FFF : c_key >> 12) * p.Hkv +
+                                        (c_key & 4095));
                     if (c_flags & kStart)
                         rng[0] = c_chunk | ((c_flags & kSlot1) ? (int32_t)0x80000000 : 0);
                     if (c_flags & kEnd) rng[1] = c_chunk;
@@ -565,7 +646,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                         [&](int c) { return p.ws_l + e0 + c; },
                         [&](int c) { return p.ws_o + (e0 + c) * D; });
                 } else {
-                    const size_t row0 = (size_t)(c_key >> 12) * p.Hq + (size_t)(c_key & 4095) * G;
+                    const size_t row0 =
+                        (size_t)(MIXED ? (c_key >> 12) & 0x1FFF : c_key >> 12) * p.Hq +
+                        (size_t)(c_key & 4095) * G;
                     tm.finish(
                         acc, G, (c_flags & kComplete) != 0, p.v_scale,
                         [&](int head) { return (T*)p.out + (row0 + head) * D; },
@@ -580,6 +663,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             c_t1 = ps.t1;
             c_chunk = ps.chunk;
             c_flags = ps.flags;
+            if constexpr (MIXED) c_ts = code_ts(ps.key >> 25);
             crt = ps.t0;
             if constexpr (MULTI) c_pc = column_limit(c_key >> 12, c_L);
             if (c_flags & kFirst) {
@@ -610,28 +694,30 @@ constexpr int pipeline_depth() {
     return PAIR ? 4 : (D == 64 ? 8 : 6);
 }
 
-inline size_t lds_bytes(int S, bool multi) {
-    return (size_t)((multi ? 3 : 2) * S + (multi ? 2 : 1)) * sizeof(int);
+// prefix and lengths, plus query_start (MULTI) or geometries (MIXED)
+inline size_t lds_bytes(int S, bool wide) {
+    return (size_t)((wide ? 3 : 2) * S + (wide ? 2 : 1)) * sizeof(int);
 }
 
 template <class Q, class C, int D, bool PAIR>
 hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
     const dim3 grid((unsigned)((p.nW + kWaves - 1) / kWaves)), block(64 * kWaves);
     void* args[] = {const_cast<DecodeParams*>(&p)};
+    constexpr int DP = pipeline_depth<C, D, PAIR>();
     const bool multi = p.q_start != nullptr;
+    const bool mixed = p.seq_bs != nullptr;
     const void* k =
-        multi ? reinterpret_cast<const void*>(
-                    decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), true>)
-              : reinterpret_cast<const void*>(
-                    decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false>);
-    return hipLaunchKernel(k, grid, block, args, lds_bytes(p.S, multi), st);
+        multi ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, DP, true, false>)
+        : mixed ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, true>)
+                : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, DP, false, false>);
+    return hipLaunchKernel(k, grid, block, args, lds_bytes(p.S, multi || mixed), st);
 }
 
 template <class Q, class C, int D, bool PAIR>
 int resident_k(int S) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false>,
+            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false, false>,
             64 * kWaves, lds_bytes(S, true)) != hipSuccess)
         return 0;
     // one workgroup per CU = one wavefront per SIMD, also where the
@@ -641,7 +727,7 @@ int resident_k(int S) {
 
 template <class Q, class C>
 hipError_t launch_d(const DecodeParams& p, hipStream_t st) {
-    const bool pair = p.bs == 8;
+    const bool pair = p.bs == 8 && p.seq_bs == nullptr;   // mixed sizes take 8-token tiles
     if (p.D == 64) return pair ? launch_k<Q, C, 64, true>(p, st) : launch_k<Q, C, 64, false>(p, st);
     if (p.D == 128)
         return pair ? launch_k<Q, C, 128, true>(p, st) : launch_k<Q, C, 128, false>(p, st);

@@ -145,3 +145,74 @@ def test_mixed_block_sizes_workload_sampled_rows():
     rows = sorted(s * c.Hq + hq for s in seqs for hq in (0, 5, 18, 31))
     out, _ = run_mixed(mc, 512)
     check(mc, out, oracle_mixed(mc, rows), rows)
+
+
+# ---- the balanced split over mixed block sizes ------------------------------
+BAL = pkv.PARTITION_BALANCED
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mixed_balanced_ragged(dtype):
+    """The balanced split walking each sequence's own block size: 8-token
+    blocks in 8-token tiles, 16 and 32 in 16-token tiles."""
+    mc = case(870, S=40, dtype=dtype, cache=dtype, lmax=1200)
+    out, _ = run_mixed(mc, BAL)
+    check(mc, out, oracle_mixed(mc))
+
+
+def test_mixed_balanced_fp8_and_page_16():
+    mc = case(871, S=30, cache="fp8", lmax=900)
+    out, _ = run_mixed(mc, BAL)
+    check(mc, out, oracle_mixed(mc))
+    mc = case(872, S=30, page=16, sizes=(16, 32), lmax=900)
+    out, _ = run_mixed(mc, BAL)
+    check(mc, out, oracle_mixed(mc))
+
+
+def test_mixed_balanced_small_blocks_and_empty_rows():
+    """Only 8-token blocks (every tile an 8-token one), and a batch with
+    zero-length sequences, whose rows the reduce writes as zeros."""
+    mc = case(873, S=20, sizes=(8,), lmax=400)
+    out, _ = run_mixed(mc, BAL)
+    check(mc, out, oracle_mixed(mc))
+    mc = case(874, S=12, lmax=300)
+    mc.case.seq_lens[[1, 4, 5]] = 0
+    out, _ = run_mixed(mc, BAL)
+    assert np.all(out[[1, 4, 5]] == 0.0)
+    check(mc, out, oracle_mixed(mc))
+
+
+def test_mixed_balanced_equals_the_balanced_decode_on_page_sized_blocks():
+    """Every block one page of 16 tokens: the mixed balanced walk is the
+    uniform pool's, tile for tile and chunk for chunk, so the rows agree bit
+    for bit with the balanced decode on the same pool."""
+    mc = case(875, S=48, page=16, sizes=(16,), lmax=2000)
+    out, d = run_mixed(mc, BAL)
+    c = mc.case
+    ws = pkv.allocate_workspace(c.S, c.Hq, c.Hkv, c.D, c.max_seq_len, BAL)
+    d.out.fill_(float("nan"))
+    pkv.paged_attention_decode(d.out, d.query, d.k_cache, d.v_cache, d.tables, d.lens,
+                               scale=c.scale, max_seq_len=c.max_seq_len, k_scale=c.k_scale,
+                               v_scale=c.v_scale, partition_size=BAL, workspace=ws)
+    pkv.paged_attention_reduce(d.out, ws, d.lens, num_kv_heads=c.Hkv,
+                               max_seq_len=c.max_seq_len, partition_size=BAL)
+    torch.cuda.synchronize()
+    assert np.array_equal(out, from_dev(d.out))
+
+
+def test_mixed_block_sizes_workload_balanced():
+    """The bench's workload (Llama-3-8B decode shape, block size by length)
+    on the balanced split: the oracle on a sample of rows covering every
+    block size, and every row within twice the tolerance of the fixed split
+    at 512."""
+    mc = workloads.mixed_block_sizes()
+    c = mc.case
+    rng = np.random.default_rng(876)
+    seqs = set(rng.choice(c.S, size=24, replace=False).tolist())
+    for b in (8, 16, 32):
+        seqs.update(np.nonzero(mc.seq_bs == b)[0][:3].tolist())
+    rows = sorted(s * c.Hq + hq for s in seqs for hq in (0, 7, 18, 31))
+    out, d = run_mixed(mc, BAL)
+    check(mc, out, oracle_mixed(mc, rows), rows)
+    fixed, _ = run_mixed(mc, 512, d)
+    assert np.all(np.abs(out - fixed) <= 2 * bound(fixed, c.cache_dtype, c.q_dtype))
