@@ -210,8 +210,9 @@ def mixed_args(**kw):
     (dict(out=None), -1), (dict(sbs=None), -1), (dict(tables=None), -1),
     (dict(qdt=7), -3), (dict(qdt=1, cdt=2), -3),
     (dict(S=0), -2), (dict(Hq=30), -2), (dict(max_len=0), -2), (dict(NP=3), -2),
-    (dict(P=16), -2), (dict(P=48), -2), (dict(P=-1), -2),
+    (dict(P=16), -2), (dict(P=48), -2), (dict(P=-2), -2),
     (dict(P=64), -5), (dict(P=64, ws=FAKE, ws_bytes=64), -5),
+    (dict(P=-1), -5), (dict(P=-1, ws=FAKE, ws_bytes=4096), -5),   # balanced, no room
     (dict(qdt=0, cdt=0), -4), (dict(Hq=64, Hkv=2), -4), (dict(D=96), -4), (dict(page=12), -4),
     (dict(out=FAKE + 8), -6), (dict(sbs=FAKE + 2), -6), (dict(max_blocks=(1 << 25) + 1), -2),
 ])
