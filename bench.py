@@ -65,7 +65,8 @@ def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int, tile_tokens=
     by the guided schedule (nW chunks of max(1, 4A/5) tiles, nW of
     max(A/7, F), then max(A/16, F), A = T / nW, F = max(floor, 4)), each cut
     inside a stream moved to the nearer end of that stream when it lies
-    within a quarter of the smaller neighbouring chunk.  tile_tokens: each
+    within an eighth of the smaller neighbouring chunk (a quarter after the
+    first nW chunks).  tile_tokens: each
     sequence's tile (mixed block sizes: 8 for 8-token blocks), default 16.
     Returns (number of streams spread over several chunks, partial entries
     they write per query head)."""
@@ -95,7 +96,7 @@ def balanced_split(lens: np.ndarray, Hkv: int, nW: int, floor: int, tile_tokens=
     # move the inner cuts
     lo_s, hi_s = g0[live], g1[live]
     b = plain[1:-1]
-    d = np.minimum(b - plain[:-2], plain[2:] - b) // 4
+    d = np.minimum(b - plain[:-2], plain[2:] - b) // np.where(c[1:-1] <= nW, 8, 4)
     k = np.searchsorted(lo_s, b, side="right") - 1
     r = b - lo_s[k]
     up = hi_s[k] - b

@@ -183,21 +183,22 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len, int*
 }
 
 // First tile of chunk c: the schedule's chunk_begin, moved to the nearer
-// end of the stream it falls in when that end lies within a quarter of the
-// smaller of the two chunks it separates.  A cut inside a stream costs the
-// stream two partial entries (written here, read by the reduce).  Moving
-// cuts changes the chunks' sizes, which the schedule's balance bears up to
-// about a quarter (MI355X, ragged GQA batch and speculative verification:
-// an eighth, a fifth and a quarter all faster than no moving, 2/5 9%
-// slower on decode).  Chunks stay non-empty (each keeps at least half its
-// tiles), chunk 0 starts at 0 and the last ends at T; the reduce reads each
-// stream's chunks from what the decode records, so it needs no copy of this
-// rule.
+// end of the stream it falls in when that end lies within an eighth of the
+// smaller of the two chunks it separates (a quarter between the later,
+// dynamically taken chunks).  A cut inside a stream costs the stream two
+// partial entries (written here, read by the reduce).  Moving a cut changes
+// two chunks' sizes; the first nW chunks are each wave's fixed share, which
+// bears little of that (MI355X: a quarter there cost the long-context batch
+// 6% and the MHA batch 2%, an eighth nothing), while the later ones are
+// taken as waves free up.  Chunks stay non-empty (each keeps at least half
+// its tiles), chunk 0 starts at 0 and the last ends at T; the reduce reads
+// each stream's chunks from what the decode records, so it needs no copy of
+// this rule.
 __device__ inline int chunk_start(const Sched& q, int c, const int* pre, const int* len,
                                    const int* geo, int S) {
     const int b = chunk_begin(q, c);
     if (c <= 0 || c >= q.chunks) return b;
-    const int d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) / 4;
+    const int d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) / (c <= q.nW ? 8 : 4);
     if (d <= 0) return b;
     int lo = 0, hi = S;                    // pre[lo] <= b < pre[lo + 1]
     while (hi - lo > 1) {

@@ -6,8 +6,8 @@ only on the tile count T, the grid size nW and a floor (two rounds of the
 decode's tile ring, 8 to 20 tiles): nW chunks of C1 = max(1, 4A/5) tiles, nW
 of C2 = max(A/7, F), then chunks of C3 = max(A/16, F), with A = T / nW and
 F = max(floor, 4).  A cut that falls inside a stream moves to the nearer
-end of that stream when it lies within a quarter of the smaller of the two
-chunks the cut separates.  Inside a chunk a piece of a stream is a segment: a whole
+end of that stream when it lies within an eighth of the smaller of the two
+chunks the cut separates (a quarter for cuts after the first nW chunks).  Inside a chunk a piece of a stream is a segment: a whole
 stream writes its output, any other segment is the first (slot 0) or last
 (slot 1) of its chunk.  The decode records each stream's first chunk (and
 whether its piece there is slot 1) and last chunk, and the reduce reads
@@ -51,11 +51,12 @@ def chunk_begin(q, c):
 
 def chunk_start(q, c, strm):
     """chunk_begin moved to the nearer end of the stream it falls in, when
-    that end is within a quarter of the smaller neighbouring chunk."""
+    that end is within an eighth of the smaller neighbouring chunk (a
+    quarter after the first nW chunks)."""
     b = chunk_begin(q, c)
     if c <= 0 or c >= q["chunks"]:
         return b
-    d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) // 4
+    d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) // (8 if c <= q["nW"] else 4)
     for g0, g1 in strm:
         if g0 <= b < g1:
             r = b - g0

@@ -52,14 +52,14 @@ def test_chunk_floor_is_two_rounds_of_the_ring():
 
 def test_balanced_split_replay_counts_split_streams():
     """Two streams of 10 tiles on 2 waves: T = 20, A = 10, C1 = 8, so the
-    schedule cuts at 8 and 16.  The cut at 8 lies 2 tiles before stream 0's
-    end, within a quarter of its chunks (8 tiles each), and moves to 10; the
-    cut at 16 (chunks of 8 and 4 tiles: quarter 1) stays.  Stream 0 is then
-    whole in chunk 0 and stream 1 spans chunks 1-2: 1 split stream, 2
-    entries, whatever the floor (the last chunk is the 4 tiles left)."""
+    schedule cuts at 8 and 16.  Both cuts separate fixed first-phase chunks,
+    which move only within an eighth of the smaller neighbour (1 tile and
+    0): the cut at 8 lies 2 tiles before stream 0's end and stays.  Stream 0
+    spans chunks 0-1, stream 1 chunks 1-2: 2 split streams, 4 entries,
+    whatever the floor (the last chunk is the 4 tiles left)."""
     lens = np.array([160], np.int64)                 # 10 tiles per stream
-    assert bench.balanced_split(lens, 2, 2, 4) == (1, 2)
-    assert bench.balanced_split(lens, 2, 2, 20) == (1, 2)
+    assert bench.balanced_split(lens, 2, 2, 4) == (2, 4)
+    assert bench.balanced_split(lens, 2, 2, 20) == (2, 4)
     assert bench.balanced_split(np.array([0], np.int64), 2, 2, 12) == (0, 0)
 
 
