@@ -133,53 +133,37 @@ __device__ inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt(0xF70 | N);
 }
 
+// The larger of x and the value of the lane 32 away (the other lane of the
+// same query row), as a median with FLT_MAX: fmaxf would first quiet signalling
+// NaNs of values it cannot vouch for, two more instructions, and the scores
+// here are finite or -inf.
+__device__ inline float row_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), FLT_MAX);
+}
+
 // The value fragments of one 32-key sub-tile: transpose reads (2 per
 // operand; see the address sets in the kernel) from the 4 lane addresses
-// a[ii][rd] (flattened), output tile n at byte offset 256 n.  Written out
-// together with their wait, so that the compiler does not take them for
-// reads of the stage loads still in flight into other buffers (it would
-// wait for all of those first).  r[ii][n][rd] flattened.
-template <int NT>
-__device__ inline void read_v_frags(u32x2 (&r)[4 * NT], const uint32_t (&a)[4]);
-template <>
-__device__ inline void read_v_frags<4>(u32x2 (&r)[16], const uint32_t (&a)[4]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %17\n\t"
-        "ds_read_b64_tr_b16 %2, %16 offset:256\n\t"
-        "ds_read_b64_tr_b16 %3, %17 offset:256\n\t"
-        "ds_read_b64_tr_b16 %4, %16 offset:512\n\t"
-        "ds_read_b64_tr_b16 %5, %17 offset:512\n\t"
-        "ds_read_b64_tr_b16 %6, %16 offset:768\n\t"
-        "ds_read_b64_tr_b16 %7, %17 offset:768\n\t"
-        "ds_read_b64_tr_b16 %8, %18\n\t"
-        "ds_read_b64_tr_b16 %9, %19\n\t"
-        "ds_read_b64_tr_b16 %10, %18 offset:256\n\t"
-        "ds_read_b64_tr_b16 %11, %19 offset:256\n\t"
-        "ds_read_b64_tr_b16 %12, %18 offset:512\n\t"
-        "ds_read_b64_tr_b16 %13, %19 offset:512\n\t"
-        "ds_read_b64_tr_b16 %14, %18 offset:768\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:768\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-        : "memory");
+// a[ii][rd] (flattened) plus off, output tile n 256 n bytes further; r[ii][n][rd]
+// flattened.  Each read goes through a restrict pointer, which gives it the
+// alias-scope information the compiler's wait insertion needs to let it pass
+// the stage loads still in flight into the other buffers (without that it
+// waits for all of them before the first read).  The stage a read takes
+// from is complete by the kernel's own wait and barrier either way.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 tr_read(__attribute__((address_space(3))) s16x4* __restrict__ p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
 }
-template <>
-__device__ inline void read_v_frags<2>(u32x2 (&r)[8], const uint32_t (&a)[4]) {
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:256\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:256\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %11\n\t"
-        "ds_read_b64_tr_b16 %6, %10 offset:256\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:256\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-        : "memory");
+template <int NT>
+__device__ inline void read_v_frags(u32x2 (&r)[4 * NT], const uint32_t (&a)[4], uint32_t off) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+        for (int n = 0; n < NT; n++)
+#pragma unroll
+            for (int rd = 0; rd < 2; rd++)
+                r[ii * 2 * NT + 2 * n + rd] = tr_read(
+                    (__attribute__((address_space(3))) s16x4*)(size_t)(a[2 * ii + rd] + off + 256 * n));
 }
 
 template <class Q, int D>
@@ -388,6 +372,22 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
+    // the sum of the 8 pairs of 16-bit weights in w (one per dot product)
+    auto sum_words = [](const uint32_t (&w)[2][4]) {
+        float t = 0.0f;
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                if constexpr (M::kSplitP)
+                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[ii][q]),
+                                                        bf16x2{(__bf16)1.0f, (__bf16)1.0f}, t, false);
+                else
+                    t = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w[ii][q]),
+                                               f16x2{(_Float16)1.0f, (_Float16)1.0f}, t, false);
+            }
+        return t;
+    };
     auto sub_tile = [&](const char* base, int u, int kb, auto mask) {
         constexpr bool MASK = decltype(mask)::value;
         // all K fragments requested before the first product
@@ -404,13 +404,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         // the value fragments, read while the score products run
         v8 vf[2][SH::kNT];
         {
-            const uint32_t sb = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)base +
-                                (uint32_t)(u * kSub * SH::kRow);
+            const uint32_t sb = (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)base;
             uint32_t a[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) a[i] = sb + (&va[0][0])[i];
             u32x2 r[4 * SH::kNT];
-            read_v_frags<SH::kNT>(r, a);
+            read_v_frags<SH::kNT>(r, a, (uint32_t)(u * kSub * SH::kRow));
 #pragma unroll
             for (int ii = 0; ii < 2; ii++)
 #pragma unroll
@@ -426,8 +425,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
             const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
             mx = fmaxf(mx, (!MASK || key <= lim) ? sc[r] : -INFINITY);
         }
-        mx = swap_max32(mx);
-        const float mxs = mx == -INFINITY ? -INFINITY : mx * sla;
+        mx = row_max(mx);
+        // a row that sees no key of the sub-tile keeps -inf (not -inf * sla)
+        const float mxs = MASK && mx == -INFINITY ? -INFINITY : mx * sla;
         const float m_new = mxs > m + mfma::kTau ? mxs : m;
         if (__any(m_new != m)) {
             const float alpha = m_new == m ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
@@ -438,15 +438,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
         }
         const float nm = -m;
         float pz[16];
-        float ls = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
             const float e = __builtin_amdgcn_exp2f(fmaf(sc[r], sla, nm));
             const int key = kb + 8 * (r >> 2) + 4 * g + (r & 3);
             pz[r] = (!MASK || key <= lim) ? e : 0.0f;
-            ls += pz[r];
         }
-        l += ls;
         // element e of the operand of step ii is score register 8 ii + e
         // (keys 4g.. and 8 + 4g.. of the step, the order of the value reads)
         uint32_t hw[2][4];
@@ -460,6 +457,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
                 else
                     hw[ii][q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
             }
+        // The running sum takes the 16-bit weights themselves, the numbers
+        // the value products see, two per dot product with (1, 1): the
+        // output is then a weighted mean with exactly its own weights.
+        l += sum_words(hw);
 #pragma unroll
         for (int ii = 0; ii < 2; ii++) {
             const v8 hi = __builtin_bit_cast(v8, u32x4{hw[ii][0], hw[ii][1], hw[ii][2], hw[ii][3]});
@@ -477,6 +478,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
             // depend on the other rows of the wave.
             const bool fine = __builtin_amdgcn_exp2f(mxs - m) > 0.125f * l;
             if (__any(fine)) {
+                uint32_t lws[2][4];
 #pragma unroll
                 for (int ii = 0; ii < 2; ii++) {
                     uint32_t lw[4];
@@ -492,7 +494,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
                     const v8 lo = __builtin_bit_cast(v8, u32x4{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
                     for (int n = 0; n < SH::kNT; n++) o[n] = M::mma(vf[ii][n], lo, o[n]);
+                    lws[ii][0] = lw[0], lws[ii][1] = lw[1], lws[ii][2] = lw[2], lws[ii][3] = lw[3];
                 }
+                l += sum_words(lws);        // zero words where the lane is not fine
             }
         }
     };

@@ -13,7 +13,9 @@ below that share a weight ends at most 1/8 of its row's total.
 These tests model that arithmetic on the CPU (no GPU, no library): scores
 from bf16 queries and keys, base-2 weights against a lazily raised
 reference maximum (raised when a step's maximum exceeds it by more than 8),
-a lane's 16 keys of each 32-key step with its own running sum, bf16
+a lane's 16 keys of each 32-key step with its own running sum of the
+16-bit weights it feeds to the products (the kernel sums those words, so
+the output is a weighted mean with exactly its own weights), bf16
 rounding by round-to-nearest-even, the output rounded to bf16, compared
 with float64 softmax attention under the test bound (5e-3, plus half a
 unit in the last place where |ref| >= 1).  They decide that one bf16
@@ -67,17 +69,19 @@ def model(n: int, rows: int, rule: str, rng) -> float:
             if sel.size == 0:
                 continue
             p = np.exp2(step[:, sel] - m[:, None]).astype(np.float32)
-            lanes[g] = lanes[g] + p.astype(np.float64).sum(1)
-            hi = bf16(p)
-            lo = bf16(p - hi)
+            hi = bf16(p).astype(np.float64)
+            lo = bf16(p - bf16(p)).astype(np.float64)
+            # the running sum takes the 16-bit weights the products see
+            lanes[g] = lanes[g] + hi.sum(1)
             if rule == "one":
                 w = hi
             elif rule == "split":
-                w = hi.astype(np.float64) + lo
+                w = hi + lo
             else:
                 fine = pm > lanes[g] / 8
-                w = hi.astype(np.float64) + np.where(fine[:, None], lo, 0.0)
-            o += np.einsum("rn,rnd->rd", w.astype(np.float64), v[:, k0 + sel])
+                w = hi + np.where(fine[:, None], lo, 0.0)
+            lanes[g] = lanes[g] + (w - hi).sum(1)
+            o += np.einsum("rn,rnd->rd", w, v[:, k0 + sel])
     out = bf16((o / (lanes[0] + lanes[1])[:, None]).astype(np.float32)).astype(np.float64)
     return float((np.abs(out - ref) / bound(ref)).max())
 
