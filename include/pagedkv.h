@@ -378,8 +378,11 @@ int pkv_paged_attention_multi(void* out, const void* query, pkv_dtype q_dtype,
  * pkv_multi_workspace_bytes - bytes of workspace pkv_paged_attention_multi
  * needs.  PKV_PARTITION_BALANCED: a 256-byte header, num_seqs + 1 words
  * and 2 * num_seqs * num_q_heads words (the chunk ranges of the streams),
- * then m, l [2 * (5 * 2048 + 8) * 16] and o [same][head_dim] float32 (each
- * part on a 256-byte boundary), whatever the lengths.  P > 0: with rows = num_seqs * max_query_len *
+ * then m, l [2 * (5 * 2048 + 8) * 16] float32 and room for o [same][head_dim]
+ * float32 (each part on a 256-byte boundary), whatever the lengths.  The o
+ * rows are stored compactly in the first half of that room: head_dim f16
+ * values per row, the row's mean scaled by a power of two whose exponent
+ * the low byte of the row's l carries.  P > 0: with rows = num_seqs * max_query_len *
  * num_q_heads and P_max = ceil(max_seq_len / P), m and l [rows][P_max] and
  * o [rows][P_max][head_dim] float32, then [num_seqs * max_query_len] int32
  * context lengths, each part starting on a 256-byte boundary.  0 for

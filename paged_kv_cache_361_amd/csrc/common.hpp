@@ -153,4 +153,23 @@ __device__ inline float strided_max(float x) {
 
 __device__ inline int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// Compact partial entries (the balanced split of multi-query calls, whose
+// split streams leave 16 rows per cut).  A row is stored as D f16 values
+// x_d = (o_d / l) 2^(15 - e), e the frexp exponent of the row's largest
+// |o_d / l| (that value lies in [2^(e-1), 2^e)), so every |x_d| < 2^15
+// keeps 11 significant bits whatever the magnitude of V.  e + 127 rides in
+// the low 8 bits of the stored l, which moves l by less than 2^-15 of
+// itself; the reader takes the sums o_d = x_d 2^(e - 15) l.
+__device__ inline int compact_exponent(float amax) {
+    const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 0;
+    return e < -127 ? -127 : (e > 128 ? 128 : e);
+}
+__device__ inline float compact_l(float l, int e) {
+    return __uint_as_float((__float_as_uint(l) & ~0xFFu) | (uint32_t)(e + 127));
+}
+// the factor that turns a stored x_d back into the sum o_d, from the stored l
+__device__ inline float compact_scale(float l) {
+    return __builtin_ldexpf(l, (int)(__float_as_uint(l) & 0xFFu) - 127 - 15);
+}
+
 }  // namespace pkv

@@ -190,15 +190,19 @@ __device__ inline void wg_prefix(const DecodeParams& p, int* pre, int* len, int*
 // two chunks' sizes; the first nW chunks are each wave's fixed share, which
 // bears little of that (MI355X: a quarter there cost the long-context batch
 // 6% and the MHA batch 2%, an eighth nothing), while the later ones are
-// taken as waves free up.  Chunks stay non-empty (each keeps at least half
+// taken as waves free up.  Verification (MULTI) moves every cut within a
+// quarter: its partial entries hold 16 rows instead of G, four times the
+// bytes per cut stream.  Chunks stay non-empty (each keeps at least half
 // its tiles), chunk 0 starts at 0 and the last ends at T; the reduce reads
 // each stream's chunks from what the decode records, so it needs no copy of
 // this rule.
+template <bool MULTI>
 __device__ inline int chunk_start(const Sched& q, int c, const int* pre, const int* len,
                                    const int* geo, int S) {
     const int b = chunk_begin(q, c);
     if (c <= 0 || c >= q.chunks) return b;
-    const int d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) / (c <= q.nW ? 8 : 4);
+    const int d = min(b - chunk_begin(q, c - 1), chunk_begin(q, c + 1) - b) /
+                  (c <= q.nW && !MULTI ? 8 : 4);
     if (d <= 0) return b;
     int lo = 0, hi = S;                    // pre[lo] <= b < pre[lo + 1]
     while (hi - lo > 1) {
@@ -419,8 +423,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
     // Within a chunk the walk looks one span ahead; it steps into the next
     // chunk only once that chunk's index is at hand.
     Walk pw;
-    pw.start(pre, len, geo_s, geo0, p.S, w, chunk_start(q, w, pre, len, geo_s, p.S),
-             chunk_start(q, w + 1, pre, len, geo_s, p.S));
+    pw.start(pre, len, geo_s, geo0, p.S, w, chunk_start<MULTI>(q, w, pre, len, geo_s, p.S),
+             chunk_start<MULTI>(q, w + 1, pre, len, geo_s, p.S));
     auto walk_next = [&](Span& o) { return pw.next(len, geo_s, p.S, p.Hkv, bs_shift, o); };
     auto chunk_next = [&](Span& o) {       // first span of the next chunk
         const int c = take_chunk();
@@ -428,8 +432,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
             chunks_left = false;
             return false;
         }
-        pw.start(pre, len, geo_s, geo0, p.S, c, chunk_start(q, c, pre, len, geo_s, p.S),
-                 chunk_start(q, c + 1, pre, len, geo_s, p.S));
+        pw.start(pre, len, geo_s, geo0, p.S, c, chunk_start<MULTI>(q, c, pre, len, geo_s, p.S),
+                 chunk_start<MULTI>(q, c + 1, pre, len, geo_s, p.S));
         return walk_next(o);               // chunks are never empty
     };
     // Window of 64 block-table entries from block sp.wb; entries at or past
@@ -638,14 +642,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                     const int cs = c_key >> 12, ch = c_key & 4095;
                     const size_t r0 = (size_t)q_first(cs);
                     const bool complete = (c_flags & kComplete) != 0;
-                    tm.finish_each(
+                    tm.template finish_each<true>(
                         acc, q_count(cs) * G, [&](int) { return complete; }, p.v_scale,
                         [&](int c) {
                             return (T*)p.out + ((r0 + c / G) * p.Hq + (size_t)ch * G + c % G) * D;
                         },
                         [&](int c) { return p.ws_m + e0 + c; },
                         [&](int c) { return p.ws_l + e0 + c; },
-                        [&](int c) { return p.ws_o + (e0 + c) * D; });
+                        [&](int c) { return (_Float16*)p.ws_o + (e0 + c) * D; });
                 } else {
                     const size_t row0 =
                         (size_t)(MIXED ? (c_key >> 12) & 0x1FFF : c_key >> 12) * p.Hq +

@@ -47,17 +47,30 @@ constexpr int waves_per_simd(int WPR) { return WPR > 1 ? 4 : 8; }
 // Waves per workgroup of a kernel serving rows with WPR waves each.
 constexpr int wg_waves(int WPR) { return WPR > 1 ? WPR : kWaves; }
 
+// An entry's CW values of one lane, from its compact form (f16 means x and
+// the stored l; see compact_exponent) back to the sums o = x 2^(e - 15) l.
+template <int CW>
+__device__ inline auto widen_entry(_Float16 __attribute__((ext_vector_type(CW))) h, float l) {
+    typedef float colv __attribute__((ext_vector_type(CW)));
+    const float f = compact_scale(l);
+    colv o;
+#pragma unroll
+    for (int q = 0; q < CW; q++) o[q] = (float)h[q] * f;
+    return o;
+}
+
 // Merges n >= 1 entries into one output row served by WPR > 1 waves (one
 // workgroup).  idx(e) maps entry e to its index in the m/l arrays (o rows at
-// idx * D).  A row whose entries hold no weight (every m = -inf) is written
-// as zeros.
-template <class O, int D, int WPR, class Idx>
+// idx * D; COMPACT: compact rows of D f16 values).  A row whose entries hold
+// no weight (every m = -inf) is written as zeros.
+template <class O, int D, int WPR, bool COMPACT, class Idx>
 __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t row, int sub) {
     static_assert(WPR > 1, "one-wave rows take merge_short");
     constexpr int CW = D / 16;                 // columns per lane
     constexpr int SLOTS = 4 * WPR;             // entry slots per row
     constexpr int NP = WPR;
     typedef float colv __attribute__((ext_vector_type(CW)));
+    typedef _Float16 hcol __attribute__((ext_vector_type(CW)));
     __shared__ colv part_sum[NP][16];
     __shared__ float part_m[NP], part_l[NP];
 
@@ -72,16 +85,19 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
     colv acc = colv{};
     for (int e0 = j; e0 < n; e0 += SLOTS * kBatch) {
         colv o[kBatch];
+        hcol h[kBatch];
         float m[kBatch], l[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; u++) {     // the round's loads, all at once
             const int e = e0 + u * SLOTS;
             o[u] = colv{};                     // entries past n: no weight, no loads
+            h[u] = hcol{};
             m[u] = -INFINITY;
             l[u] = 0.0f;
             if (e < n) {
                 const size_t ie = idx(e);
-                o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+                if constexpr (COMPACT) h[u] = *(const hcol*)((const _Float16*)p.ws_o + ie * D + c * CW);
+                else o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
                 m[u] = p.ws_m[ie];
                 l[u] = p.ws_l[ie];
             }
@@ -90,6 +106,10 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
         // scheduler issues the o loads only once the m values are back, which
         // costs a second memory round trip per round.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (COMPACT) {
+#pragma unroll
+            for (int u = 0; u < kBatch; u++) o[u] = widen_entry<CW>(h[u], l[u]);
+        }
         float bm = m_run;
 #pragma unroll
         for (int u = 0; u < kBatch; u++) {
@@ -153,16 +173,24 @@ __device__ inline void merge_row(const ReduceParams& p, int n, Idx idx, size_t r
 // short rows of a decode batch this is about 1 us faster per call than the
 // running-max merge, which long rows need.  Out-of-range slots read entry 0
 // and get weight 0.
-template <class O, int D, class Idx>
+template <class O, int D, bool COMPACT, class Idx>
 __device__ inline void merge_short(const ReduceParams& p, int n, Idx idx, size_t row) {
     constexpr int CW = D / 16;                 // columns per lane
     constexpr int SLOTS = 4;                   // entry slots per row
     constexpr int U = 4;                       // entries per slot per round
     typedef float colv __attribute__((ext_vector_type(CW)));
+    typedef _Float16 hcol __attribute__((ext_vector_type(CW)));
 
     const int lane = threadIdx.x & 63;
     const int j = lane >> 4;                   // this lane's slot
     const int c = lane & 15;
+    // this lane's columns of entry ie, as sums
+    auto entry = [&](size_t ie) {
+        if constexpr (COMPACT)
+            return widen_entry<CW>(*(const hcol*)((const _Float16*)p.ws_o + ie * D + c * CW), p.ws_l[ie]);
+        else
+            return *(const colv*)(p.ws_o + ie * D + c * CW);
+    };
 
     const size_t i0 = lane < n ? idx(lane) : 0;
     const float m0 = lane < n ? p.ws_m[i0] : -INFINITY;
@@ -173,7 +201,7 @@ __device__ inline void merge_short(const ReduceParams& p, int n, Idx idx, size_t
     for (int u = 0; u < U; u++) {
         const int e = j + u * SLOTS;
         const size_t ie = idx(e < n ? e : 0);
-        o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+        o[u] = entry(ie);
         mo[u] = p.ws_m[ie];
     }
 
@@ -197,7 +225,7 @@ __device__ inline void merge_short(const ReduceParams& p, int n, Idx idx, size_t
             for (int u = 0; u < U; u++) {
                 const int e = e0 + u * SLOTS;
                 const size_t ie = idx(e < n ? e : 0);
-                o[u] = *(const colv*)(p.ws_o + ie * D + c * CW);
+                o[u] = entry(ie);
                 mo[u] = p.ws_m[ie];
             }
         }
@@ -223,10 +251,10 @@ __device__ inline void merge_short(const ReduceParams& p, int n, Idx idx, size_t
 }
 
 // One of the two merges, by the waves a row has.
-template <class O, int D, int WPR, class Idx>
+template <class O, int D, int WPR, bool COMPACT, class Idx>
 __device__ inline void merge(const ReduceParams& p, int n, Idx idx, size_t row, int sub) {
-    if constexpr (WPR == 1) merge_short<O, D>(p, n, idx, row);
-    else merge_row<O, D, WPR>(p, n, idx, row, sub);
+    if constexpr (WPR == 1) merge_short<O, D, COMPACT>(p, n, idx, row);
+    else merge_row<O, D, WPR, COMPACT>(p, n, idx, row, sub);
 }
 
 // ---- fixed partitions -------------------------------------------------------
@@ -246,7 +274,7 @@ void reduce_kernel(ReduceParams p) {
     const int nparts = L > 0 ? (L + p.P - 1) / p.P : 0;
     if (nparts <= 1) return;
     const size_t base = (size_t)row * p.P_max;
-    merge<O, D, WPR>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, sub);
+    merge<O, D, WPR, false>(p, nparts, [&](int k) { return base + (size_t)k; }, (size_t)row, sub);
 }
 
 // ---- balanced split ---------------------------------------------------------
@@ -333,7 +361,7 @@ void reduce_balanced_kernel(ReduceParams p) {
     if (c0 == c1) return;                       // one chunk held it: decode wrote the row
     if (c1 < c0 || c1 >= chunks) return;        // not ranges of this call
     const int slot0 = (int)((uint32_t)r0 >> 31);
-    merge<O, D, WPR>(
+    merge<O, D, WPR, MULTI>(
         p, c1 - c0 + 1,
         [&](int e) {
             const int slot = e == 0 ? slot0 : 0;
@@ -355,6 +383,7 @@ void reduce_group_kernel(ReduceParams p) {
     constexpr int CW = D / 16;                  // output values per lane
     constexpr int U = 4;                        // entries per round
     typedef float colv __attribute__((ext_vector_type(CW)));
+    typedef _Float16 hcol __attribute__((ext_vector_type(CW)));
     const int lane = threadIdx.x & 63;
     const int s = blockIdx.y;
     const int32_t* hdr = p.ws_hdr;
@@ -425,12 +454,14 @@ void reduce_group_kernel(ReduceParams p) {
     float m_run = -INFINITY, l_run = 0.0f;      // reference max (log2 units), sum
     for (int e0 = 0; e0 < n_e; e0 += U) {
         colv o[U];
+        hcol hv[U];
         float m[U], l[U];
 #pragma unroll
         for (int k = 0; k < U; k++) {          // the round's loads, all at once
             const int e = e0 + k < n_e ? e0 + k : n_e - 1;
             const size_t ie = ((size_t)(c0 + e) * 2 + (e == 0 ? slot0 : 0)) * ncol + cc;
-            o[k] = *(const colv*)(p.ws_o + ie * D + c16 * CW);
+            if constexpr (MULTI) hv[k] = *(const hcol*)((const _Float16*)p.ws_o + ie * D + c16 * CW);
+            else o[k] = *(const colv*)(p.ws_o + ie * D + c16 * CW);
             m[k] = p.ws_m[ie];
             l[k] = p.ws_l[ie];
         }
@@ -449,8 +480,14 @@ void reduce_group_kernel(ReduceParams p) {
         for (int k = 0; k < U; k++) {
             const float w = exp2f(m[k] - ref);
             l_run = fmaf(w, l[k], l_run);
+            if constexpr (MULTI) {              // compact entries: sums = x 2^(e-15) l
+                const float f = w * compact_scale(l[k]);
 #pragma unroll
-            for (int q = 0; q < CW; q++) acc[q] = fmaf(w, o[k][q], acc[q]);
+                for (int q = 0; q < CW; q++) acc[q] = fmaf(f, (float)hv[k][q], acc[q]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < CW; q++) acc[q] = fmaf(w, o[k][q], acc[q]);
+            }
         }
         m_run = bm;
     }

@@ -426,8 +426,10 @@ struct TileMath {
     }
 
     // As finish(), with the choice between the output row and the partials
-    // made per column: final_of(head).
-    template <class Final, class OutRow, class MAt, class LAt, class OAt>
+    // made per column: final_of(head).  COMPACT: the partials take half the
+    // bytes (the format of compact_entry); o_at(head) then points to D f16
+    // values.
+    template <bool COMPACT = false, class Final, class OutRow, class MAt, class LAt, class OAt>
     __device__ inline void finish_each(const Acc& a, int G, Final final_of, float v_scale,
                                        OutRow out_row, MAt m_at, LAt l_at, OAt o_at) const {
         const float l_tot = strided_sum<16>(a.l);     // head j16, over all tokens
@@ -443,6 +445,27 @@ struct TileMath {
 #pragma unroll
                 for (int n = 0; n < NT; n++) o[n] = (T)(a.o[n][r] * inv);
                 *(vrow*)(out_row(head) + NT * j16) = o;
+            } else if constexpr (COMPACT) {
+                // the mean o / l of the row's 16 lanes (zeros where l = 0),
+                // scaled by a power of two to the top octave below 2^15
+                const float inv = lh > 0.0f ? v_scale / lh : 0.0f;
+                float x[NT], am = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NT; n++) {
+                    x[n] = a.o[n][r] * inv;
+                    am = fmaxf(am, fabsf(x[n]));
+                }
+                am = group_max<16>(am);
+                const int e = compact_exponent(am);
+                typedef _Float16 hrow __attribute__((ext_vector_type(NT)));
+                hrow h;
+#pragma unroll
+                for (int n = 0; n < NT; n++) h[n] = (_Float16)__builtin_ldexpf(x[n], 15 - e);
+                *(hrow*)(o_at(head) + NT * j16) = h;
+                if (j16 == 0) {
+                    *m_at(head) = mh * kLn2;
+                    *l_at(head) = compact_l(lh, e);
+                }
             } else {
                 if (j16 == 0) {
                     *m_at(head) = mh * kLn2;
