@@ -7,11 +7,13 @@
 // the block table; a token whose position is negative gets a zero row.
 //
 // Work layout.
-//   - A workgroup (one per CU, 8 waves, two per SIMD) serves one (sequence,
-//     KV head) and 256 / G consecutive query tokens; each wave owns 32
-//     query rows, the (token, head) pairs of 32 / G tokens (GQA: the G
-//     heads of a token share the KV head, so every K/V byte a wave reads
-//     feeds G rows).
+//   - An item is one (sequence, KV head) and 256 / G consecutive query
+//     tokens; each wave owns 32 of its query rows, the (token, head) pairs
+//     of 32 / G tokens (GQA: the G heads of a token share the KV head, so
+//     every K/V byte a wave reads feeds G rows).  A workgroup (one per CU,
+//     8 waves, two per SIMD) serves two items one after the other, their
+//     stages in one pipeline, so the second item's first stages load while
+//     the first item's last ones are computed.
 //   - The context the workgroup's last token sees is walked in stages of 64
 //     keys, each wave moving 8 of them (within one block for every block
 //     size).  K and V go straight from memory into one of three LDS buffers
@@ -94,7 +96,7 @@ struct Shape {
     static constexpr int kRow = 2 * D;                 // bytes of one head's K or V row
     static constexpr int kK = kStage * kRow;           // K of a stage
     static constexpr int kBuf = 2 * kK;                // K and V of a stage
-    static constexpr int kLds = kBufs * kBuf + kTbl * 4;
+    static constexpr int kLds = kBufs * kBuf + 2 * kTbl * 4;   // stages, two tables
     static constexpr int kChunks = kRow / 16;          // 16-byte pieces of a row
     static constexpr int kKpl = 64 / kChunks;          // keys of one wave-wide load
     static constexpr int kKpw = kStage / kWaves;       // keys each wave moves per stage
@@ -180,14 +182,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     const int g = lane >> 5;               // lane half
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // workgroup -> (sequence, KV head, group of query tokens).  Workgroups
-    // are dealt to the XCDs in turn (blockIdx % 8), and the (sequence, KV
-    // head) pairs round robin to the XCDs (pair % 8), so each XCD gets a
-    // share of every sequence's work.  Within an XCD, workgroup j (the j-th
-    // dispatched there) takes the j-th longest of the XCD's items (pair,
-    // group), by the keys it reads: the longest-first rule for jobs on
-    // identical machines, which keeps the CUs of the XCD busy to about the
-    // same end.  Items of one pair differ by a group's tokens, so a pair's
+    // workgroup -> two items (sequence, KV head, group of query tokens).
+    // Workgroups are dealt to the XCDs in turn (blockIdx % 8), and the
+    // (sequence, KV head) pairs round robin to the XCDs (pair % 8), so each
+    // XCD gets a share of every sequence's work.  Within an XCD of n items,
+    // workgroup j (the j-th dispatched there) takes the j-th longest item
+    // (by the keys it reads) and then the (n - 1 - j)-th: the longest with
+    // the shortest, which is where the longest-first rule for jobs on
+    // identical machines puts the second item of each CU when n is twice
+    // the CUs.  Items of one pair differ by a group's tokens, so a pair's
     // groups run close together and share the stages in the XCD's L2.
     // Every workgroup ranks the items itself (at most 512 per XCD, one per
     // thread); with more, pair by pair, the longest group first.
@@ -198,10 +201,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     const int xcd = (int)(blockIdx.x % 8);
     const int j = (int)(blockIdx.x / 8);
     const int n_items = (pairs > xcd ? (pairs - xcd + 7) / 8 : 0) * p.max_groups;
-    if (j >= n_items) return;              // whole workgroup
-    int item = j;
+    if (j >= (n_items + 1) / 2) return;    // whole workgroup
+    // the workgroup's two items: ranks j and n_items - 1 - j
+    int itemA = j, itemB = n_items - 1 - j > j ? n_items - 1 - j : -1;
     if (n_items <= 64 * kWaves) {
-        int* key = tbl_lds;                // the table's space, free until filled
+        int* key = tbl_lds;                // the tables' space, free until filled
         int w = -1;
         if (tid < n_items) {
             const int ps = ((tid / p.max_groups) * 8 + xcd) / p.Hkv;
@@ -213,6 +217,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
             }
             key[tid] = w;
         }
+        if (tid == 0) key[kTbl - 2] = -1;
         __syncthreads();
         if (tid < n_items) {
             int rank = 0;
@@ -221,42 +226,63 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
                 rank += (wk > w) | ((wk == w) & (k < tid));
             }
             if (rank == j) key[kTbl - 1] = tid;
+            if (rank == n_items - 1 - j && rank != j) key[kTbl - 2] = tid;
         }
         __syncthreads();
-        item = __builtin_amdgcn_readfirstlane(key[kTbl - 1]);
-        __syncthreads();                   // before the table is filled
+        itemA = __builtin_amdgcn_readfirstlane(key[kTbl - 1]);
+        itemB = __builtin_amdgcn_readfirstlane(key[kTbl - 2]);
+        __syncthreads();                   // before the tables are filled
     }
-    const int pair = (item / p.max_groups) * 8 + xcd;
-    const int grp = p.max_groups - 1 - item % p.max_groups;
-    if (pair >= pairs) return;             // whole workgroup
-    const int h = pair % p.Hkv;
-    const int s = pair / p.Hkv;
-    const int q0 = __builtin_amdgcn_readfirstlane(p.q_start[s]);
-    const int Qn = __builtin_amdgcn_readfirstlane(p.q_start[s + 1]) - q0;
-    const int wg_base = grp * tpg;
-    if (wg_base >= Qn) return;             // whole workgroup
-    int L = __builtin_amdgcn_readfirstlane(p.lens[s]);
-    L = L < p.len_cap ? L : p.len_cap;
-    // keys the workgroup's last query token sees (0: none)
-    const int wg_end = max(0, L - Qn + min(wg_base + tpg, Qn));
+    // An item: (sequence, KV head, group of query tokens), wave-uniform.
+    // nstage = 0 for an item without keys; valid = 0 for one without rows.
+    struct Item {
+        int s, h, q0, Qn, L, wg_base, wg_end, nblk, nstage, tb0, valid;
+    };
+    const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
+    auto make_item = [&](int item) {
+        Item it;
+        it.s = it.h = it.q0 = it.Qn = it.L = it.wg_base = 0;
+        it.wg_end = it.nblk = it.nstage = it.tb0 = it.valid = 0;
+        if (item < 0) return it;
+        const int pair = (item / p.max_groups) * 8 + xcd;
+        const int grp = p.max_groups - 1 - item % p.max_groups;
+        if (pair >= pairs) return it;
+        it.h = pair % p.Hkv;
+        it.s = pair / p.Hkv;
+        it.q0 = __builtin_amdgcn_readfirstlane(p.q_start[it.s]);
+        it.Qn = __builtin_amdgcn_readfirstlane(p.q_start[it.s + 1]) - it.q0;
+        it.wg_base = grp * tpg;
+        if (it.wg_base >= it.Qn) return it;
+        int L = __builtin_amdgcn_readfirstlane(p.lens[it.s]);
+        it.L = L < p.len_cap ? L : p.len_cap;
+        // keys the workgroup's last query token sees (0: none)
+        it.wg_end = max(0, it.L - it.Qn + min(it.wg_base + tpg, it.Qn));
+        it.nblk = it.wg_end > 0 ? ((it.wg_end - 1) >> bs_shift) + 1 : 0;
+        it.nstage = (it.wg_end + kStage - 1) / kStage;
+        it.valid = 1;
+        return it;
+    };
+    Item A = make_item(itemA), B = make_item(itemB);
 
-    // ---- this lane's query row ----
-    const int tok = wg_base + wave * tpw + c / G;   // query token within the sequence
+    // ---- this lane's query row (of the current item) ----
     const int hh = c % G;
-    const bool has_row = tok < Qn;
-    const int pos = L - Qn + tok;                   // its position in the sequence
-    const bool sees = has_row && pos >= 0;
-    // last key this row sees; rows that see nothing read everything (zero
-    // queries, never written), which keeps every row's max finite
-    const int lim = sees ? pos : INT_MAX;
+    int tok = 0, pos = 0, lim = INT_MAX, wlast = -1, wvis = INT_MAX;
+    bool has_row = false, sees = false;
     // Scores enter the exponent as fma(s, |scale'|, -m); a negative scale is
     // carried by the query's sign (exact).
     const float sl2 = p.scale_log2;
     const float sla = fabsf(sl2);
     v8 qf[SH::kQS];
-    {
-        const T* qrow = (const T*)p.q + ((size_t)(q0 + (sees ? tok : 0)) * p.Hq +
-                                         (size_t)h * G + hh) * D;
+    auto setup_rows = [&](const Item& it) {
+        tok = it.wg_base + wave * tpw + c / G;          // query token within the sequence
+        has_row = it.valid && tok < it.Qn;
+        pos = it.L - it.Qn + tok;                       // its position in the sequence
+        sees = has_row && pos >= 0;
+        // last key this row sees; rows that see nothing read everything (zero
+        // queries, never written), which keeps every row's max finite
+        lim = sees ? pos : INT_MAX;
+        const T* qrow = (const T*)p.q + ((size_t)(it.q0 + (sees ? tok : 0)) * p.Hq +
+                                         (size_t)it.h * G + hh) * D;
         const uint32_t flip = sl2 < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
         for (int i = 0; i < SH::kQS; i++) {
@@ -264,30 +290,30 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
             x ^= flip;
             qf[i] = __builtin_bit_cast(v8, x);
         }
-    }
-    // wave-uniform bounds over the rows that see keys: the last key any of
-    // them sees, and the last key all of them see
-    int wlast = sees ? pos : -1;
-    int wvis = sees ? pos : INT_MAX;
+        // wave-uniform bounds over the rows that see keys: the last key any
+        // of them sees, and the last key all of them see
+        int wl = sees ? pos : -1;
+        int wv = sees ? pos : INT_MAX;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        wlast = max(wlast, __shfl_xor(wlast, o, 64));
-        wvis = min(wvis, __shfl_xor(wvis, o, 64));
-    }
-    wlast = __builtin_amdgcn_readfirstlane(wlast);
-    wvis = __builtin_amdgcn_readfirstlane(wvis);
+        for (int o = 1; o < 64; o <<= 1) {
+            wl = max(wl, __shfl_xor(wl, o, 64));
+            wv = min(wv, __shfl_xor(wv, o, 64));
+        }
+        wlast = __builtin_amdgcn_readfirstlane(wl);
+        wvis = __builtin_amdgcn_readfirstlane(wv);
+    };
 
     // ---- block table entries in LDS ----
-    // Entries [tb0, tb0 + kTbl) of the sequence's table; a stage whose
-    // blocks pass the end has the next kTbl loaded first (all waves, at a
-    // stage boundary: rare, a 2048-block span).
-    const int bs_shift = p.bs == 8 ? 3 : (p.bs == 16 ? 4 : 5);
-    const int nblk = wg_end > 0 ? ((wg_end - 1) >> bs_shift) + 1 : 0;
-    const int32_t* table = p.tables + (size_t)s * p.max_blocks;
-    int tb0 = 0;
-    auto fill_table = [&](int b0) {
+    // Entries [tb0, tb0 + kTbl) of each item's table, item A's in the first
+    // kTbl words, B's in the next; a stage whose blocks pass the end has the
+    // next kTbl loaded first (all waves, at a stage boundary: rare, a
+    // 2048-block span).
+    int* tblA = tbl_lds;
+    int* tblB = tbl_lds + kTbl;
+    auto fill_table = [&](int* dst, const Item& it, int b0) {
+        const int32_t* table = p.tables + (size_t)it.s * p.max_blocks;
         for (int i = tid; i < kTbl; i += 64 * kWaves)
-            tbl_lds[i] = b0 + i < nblk ? table[b0 + i] : 0;
+            dst[i] = b0 + i < it.nblk ? table[b0 + i] : 0;
     };
 
     // ---- stage loads ----
@@ -300,16 +326,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     // Keys at or past wg_end take an out-of-range offset and write zeros.
     const uint32_t pool_row = (uint32_t)p.Hkv * SH::kRow;       // bytes between slots
     const uint32_t blk_bytes = (uint32_t)p.bs * pool_row;
-    const uint32_t head_off = (uint32_t)h * SH::kRow;
     const int lj = lane / SH::kChunks;
     const int ch = lane % SH::kChunks;
     // the V slot this lane fills (v_slot inverted): key vk of the block, unit vu
     const int vrem = lane % (4 * SH::kChunks);
     const int vk = 4 * (lane / (4 * SH::kChunks)) + ((vrem >> 2) & 3);
     const int vu = 4 * (vrem >> 4) + (vrem & 3);
-    auto load_stage = [&](int st, int buf) {
+    auto load_stage = [&](const Item& it, const int* tbl, int st, int buf) {
+        const uint32_t head_off = (uint32_t)it.h * SH::kRow;
+        const int wg_end = it.wg_end;
         const int t0 = st * kStage + SH::kKpw * wave;
-        const int e = tbl_lds[min(t0 >> bs_shift, nblk - 1) - tb0];
+        const int e = tbl[min(t0 >> bs_shift, it.nblk - 1) - it.tb0];
         const uint32_t b0 = (uint32_t)__builtin_amdgcn_readfirstlane(e);
         const uint32_t b = b0 < (uint32_t)p.NB ? b0 : (uint32_t)p.NB - 1u;
         const rsrc_t rk = make_rsrc((const char*)p.k + (size_t)b * blk_bytes, blk_bytes);
@@ -502,73 +529,100 @@ __global__ __launch_bounds__(64 * kWaves, 2) void prefill_kernel(DecodeParams p)
     };
 
     // ---- the stage pipeline ----
-    // At the top of stage st the loads of stage st + 2 are issued into
-    // buffer (st + 2) % 3, last read during stage st - 1 (every wave has
-    // passed the barrier that ended it).  At the bottom, the wave waits for
-    // its loads of stage st + 1 (all but the kLoads K and kLoads V loads of
-    // stage st + 2, issued after them, in order) and meets the others: past
-    // that barrier every wave's rows of stage st + 1 are in LDS.
-    const int nstage = (wg_end + kStage - 1) / kStage;
-    fill_table(0);
+    // The stages of item A and then those of item B form one sequence
+    // (global stage gg).  At the top of stage gg the loads of stage gg + 2
+    // are issued into buffer (gg + 2) % 3, last read during stage gg - 1
+    // (every wave has passed the barrier that ended it); so B's first two
+    // stages arrive while A's last two are computed.  At the bottom, the
+    // wave waits for its loads of stage gg + 1 (all but the kLoads K and
+    // kLoads V loads of stage gg + 2, issued after them, in order) and meets
+    // the others: past that barrier every wave's rows of stage gg + 1 are in
+    // LDS.
+    const int NA = A.nstage, NT = A.nstage + B.nstage;
+    // loads of stage st of item X, after the table span holding its blocks
+    // (workgroup-uniform)
+    auto issue_item = [&](Item& X, int* tbl, int st, int buf) {
+        const int last = min(((st + 1) * kStage - 1) >> bs_shift, X.nblk - 1);
+        if (last >= X.tb0 + kTbl) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            X.tb0 = (st * kStage) >> bs_shift;
+            fill_table(tbl, X, X.tb0);
+            __syncthreads();
+        }
+        load_stage(X, tbl, st, buf);
+    };
+    auto issue = [&](int gg) {
+        if (gg < NA) issue_item(A, tblA, gg, gg % kBufs);
+        else if (gg < NT) issue_item(B, tblB, gg - NA, gg % kBufs);
+    };
+    setup_rows(A);
+    fill_table(tblA, A, 0);
+    if (B.valid) fill_table(tblB, B, 0);
     __syncthreads();
-    if (nstage > 0) load_stage(0, 0);
-    if (nstage > 1) load_stage(1, 1);
+    issue(0);
+    issue(1);
     wait_vmcnt<0>();                       // stages 0 and 1 in LDS
     __builtin_amdgcn_s_barrier();
-    // Stages [st0, st1), every sub-tile with the causal limits (MASK) or,
-    // for stages all of whose keys every row of the wave sees, without.
-    // Every stage passes one barrier, so waves that split the stages
-    // differently still meet at each one.
-    auto run_stages = [&](int st0, int st1, auto mask) {
+    // Stages [st0, st1) of the item whose first stage is goff, every
+    // sub-tile with the causal limits (MASK) or, for stages all of whose
+    // keys every row of the wave sees, without.  Every stage passes one
+    // barrier, so waves that split the stages differently still meet at
+    // each one.
+    auto run_stages = [&](int goff, int st0, int st1, auto mask) {
         for (int st = st0; st < st1; st++) {
-            const int sn = st + 2;
-            if (sn < nstage) {
-                // the table span holding stage sn's blocks (workgroup-uniform)
-                const int last = min(((sn + 1) * kStage - 1) >> bs_shift, nblk - 1);
-                if (last >= tb0 + kTbl) {
-                    wait_vmcnt<0>();
-                    __syncthreads();
-                    tb0 = (sn * kStage) >> bs_shift;
-                    fill_table(tb0);
-                    __syncthreads();
-                }
-                load_stage(sn, sn % kBufs);
-            }
-            const char* base = lds + (st % kBufs) * SH::kBuf;
+            const int gg = goff + st;
+            issue(gg + 2);
+            const char* base = lds + (gg % kBufs) * SH::kBuf;
 #pragma unroll
             for (int u = 0; u < kStage / kSub; u++) {
                 const int kb = st * kStage + u * kSub;
                 if (kb <= wlast) sub_tile(base, u, kb, mask);            // wave-uniform
             }
-            // stage st + 1 in LDS: at most the 2 kLoads loads of stage st + 2
-            // may still be in flight
-            if (sn < nstage) wait_vmcnt<2 * SH::kLoads>();
+            // stage gg + 1 in LDS: at most the 2 kLoads loads of stage
+            // gg + 2 may still be in flight
+            if (gg + 2 < NT) wait_vmcnt<2 * SH::kLoads>();
             else wait_vmcnt<0>();
             __builtin_amdgcn_s_barrier();
         }
     };
-    // stage st is seen whole by every row of the wave when st * kStage +
-    // kStage - 1 <= wvis (wvis is INT_MAX for a wave without rows: it
-    // computes nothing and only passes the barriers)
-    const int nfull = (int)min64(nstage, ((int64_t)wvis + 1) / kStage);
-    run_stages(0, nfull, std::false_type{});
-    run_stages(nfull, nstage, std::true_type{});
-
-    // ---- epilogue: normalise and store this lane's row ----
-    if (has_row) {
-        const float l_tot = swap_sum32(l);
-        const float inv = sees && l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        T* orow = (T*)p.out + ((size_t)(q0 + tok) * p.Hq + (size_t)h * G + hh) * D;
-        typedef T t4 __attribute__((ext_vector_type(4)));
+    // normalise and store this lane's row of item `it`
+    auto epilogue = [&](const Item& it) {
+        if (has_row) {
+            const float l_tot = swap_sum32(l);
+            const float inv = sees && l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            T* orow = (T*)p.out + ((size_t)(it.q0 + tok) * p.Hq + (size_t)it.h * G + hh) * D;
+            typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int n = 0; n < SH::kNT; n++)
+            for (int n = 0; n < SH::kNT; n++)
 #pragma unroll
-            for (int rq = 0; rq < 4; rq++) {
-                t4 v;
+                for (int rq = 0; rq < 4; rq++) {
+                    t4 v;
 #pragma unroll
-                for (int e = 0; e < 4; e++) v[e] = (T)(o[n][4 * rq + e] * inv);
-                *(t4*)(orow + 32 * n + 8 * rq + 4 * g) = v;
-            }
+                    for (int e = 0; e < 4; e++) v[e] = (T)(o[n][4 * rq + e] * inv);
+                    *(t4*)(orow + 32 * n + 8 * rq + 4 * g) = v;
+                }
+        }
+    };
+    // stage st of an item is seen whole by every row of the wave when
+    // st * kStage + kStage - 1 <= wvis (wvis is INT_MAX for a wave without
+    // rows: it computes nothing and only passes the barriers)
+    {
+        const int nfull = (int)min64(NA, ((int64_t)wvis + 1) / kStage);
+        run_stages(0, 0, nfull, std::false_type{});
+        run_stages(0, nfull, NA, std::true_type{});
+        epilogue(A);
+    }
+    if (B.valid) {
+        setup_rows(B);
+#pragma unroll
+        for (int n = 0; n < SH::kNT; n++) o[n] = f32x16{};
+        m = -INFINITY;
+        l = 0.0f;
+        const int nfull = (int)min64(B.nstage, ((int64_t)wvis + 1) / kStage);
+        run_stages(NA, 0, nfull, std::false_type{});
+        run_stages(NA, nfull, B.nstage, std::true_type{});
+        epilogue(B);
     }
 }
 
@@ -576,7 +630,8 @@ template <class Q, int D>
 hipError_t launch_dd(const DecodeParams& p, hipStream_t st) {
     typedef Shape<D> SH;
     const long pairs = (long)p.S * p.Hkv;
-    const long wgs = (pairs + 7) / 8 * 8 * p.max_groups;   // per-XCD pairs x groups, x 8
+    const long per_xcd = (pairs + 7) / 8 * p.max_groups;    // items of XCD 0 (the most)
+    const long wgs = 8 * ((per_xcd + 1) / 2);               // two items per workgroup
     void* args[] = {const_cast<DecodeParams*>(&p)};
     return hipLaunchKernel(reinterpret_cast<const void*>(prefill_kernel<Q, D>),
                            dim3((unsigned)wgs), dim3(64 * kWaves), args, SH::kLds, st);
