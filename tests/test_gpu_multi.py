@@ -354,6 +354,25 @@ def test_prefill_tokens_before_the_sequence():
     check(mc, out, oracle_multi(mc))
 
 
+def test_prefill_many_items_per_xcd():
+    """More than 512 items (sequence, KV head, group of 16 query tokens at
+    G = 16) per XCD: the workgroups take them in pair-major order, two each,
+    and an odd count leaves one workgroup a single item (404 streams: 51 on
+    XCDs 0-3, 50 on 4-7, times 13 groups).  The oracle on every head of
+    every 7th query token and the first and last ones of each sequence."""
+    mc = ragged(101, 150, 200, 690, D=64, Hq=64, Hkv=4, lmin=100, lmax=400)
+    c = mc.case
+    assert mc.max_query_len > 12 * 16
+    toks = set()
+    for s in range(c.S):
+        a, b = int(mc.query_start[s]), int(mc.query_start[s + 1])
+        toks.update(range(a, b, 7))
+        toks.update([a, b - 1])
+    rows = sorted(t * c.Hq + hq for t in toks for hq in range(c.Hq))
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc, rows), rows)
+
+
 def test_prefill_f16_head_dim_64():
     mc = ragged(8, 20, 80, 680, dtype="f16", cache="f16", D=64, Hq=8, Hkv=4, lmin=50, lmax=500)
     out, _ = run_multi(mc)
