@@ -277,13 +277,14 @@ def test_balanced_verify_workspace_reused_by_a_smaller_batch():
                   2 * out_rounding(split, c.q_dtype))
 
 
-@pytest.mark.parametrize("shift", [100, -100])
-def test_balanced_verify_value_magnitudes(shift):
+@pytest.mark.parametrize("shift,D", [(100, 128), (-100, 128), (60, 64), (-60, 64)])
+def test_balanced_verify_value_magnitudes(shift, D):
     """The balanced split stores its partial rows as f16 means scaled by a
     power of two whose exponent rides in the row's l: fp8 values under a
     scale of 2^shift times their own (outputs near 2^shift, far outside
     f16's range) match the oracle once both are scaled back by 2^-shift."""
-    mc = ragged(24, 1, 4, 660 + (shift > 0), cache="fp8", lmin=200, lmax=1500)
+    kw = {} if D == 128 else dict(D=64, Hq=16, Hkv=4)
+    mc = ragged(24, 1, 4, 660 + (shift > 0), cache="fp8", lmin=200, lmax=1500, **kw)
     mc.case.v_scale = mc.case.v_scale * 2.0 ** shift
     out, _ = run_balanced(mc)
     ref = oracle_multi(mc)
