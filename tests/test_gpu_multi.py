@@ -355,6 +355,17 @@ def test_prefill_tokens_before_the_sequence():
     check(mc, out, oracle_multi(mc))
 
 
+@pytest.mark.parametrize("G,Hkv", [(1, 8), (2, 4)])
+def test_prefill_small_groups(G, Hkv):
+    """The LDS-staged kernel at G = 1 (a wave's 32 rows are 32 tokens of one
+    head, a workgroup's item 256 tokens) and G = 2, over chunks of 64..300
+    tokens, some longer than their sequence."""
+    mc = ragged(10, 64, 300, 700 + G, Hq=G * Hkv, Hkv=Hkv, lmin=20, lmax=800)
+    assert G * mc.max_query_len >= 64
+    out, _ = run_multi(mc)
+    check(mc, out, oracle_multi(mc))
+
+
 def test_prefill_many_items_per_xcd():
     """More than 512 items (sequence, KV head, group of 16 query tokens at
     G = 16) per XCD: the workgroups take them in pair-major order, two each,
