@@ -142,7 +142,12 @@ def decode_bytes(c, P: int, nW: int = 0, tile_tokens=None, floor_bs=None) -> dic
 
 # Source file each profiled kernel is compiled from.
 KERNEL_SOURCE = {"decode_balanced_kernel": "decode_balanced.hip",
-                 "decode_mfma_kernel": "decode_mfma.hip"}
+                 "decode_mfma_kernel": "decode_mfma.hip",
+                 "reduce_group_kernel": "reduce.hip"}
+# kernels of one call whose counters a workload's record sums: the decode
+# kernel alone, except verification, whose call is the balanced kernel and
+# its grouped reduce
+CALL_KERNELS = {"spec-verify": ("decode_balanced_kernel", "reduce_group_kernel")}
 
 
 def decode_kernel_name(P: int) -> str:
@@ -199,11 +204,24 @@ def traffic_from_profiles(workload: str, launch_bytes: float):
         rec = json.load(open(path)).get(workload)
     except (ValueError, AttributeError):
         return None
-    if not rec or rec.get("kernel") not in KERNEL_SOURCE:
+    if not rec:
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash(rec["kernel"]):
+    kernels = rec.get("kernels") or [rec.get("kernel")]
+    if any(k not in KERNEL_SOURCE for k in kernels):
+        return None
+    if rec.get("kernel_source_hash") != kernels_source_hash(kernels):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def kernels_source_hash(kernels) -> str:
+    """kernel_source_hash of one kernel, or of the sources of several."""
+    if len(kernels) == 1:
+        return kernel_source_hash(kernels[0])
+    h = hashlib.sha256()
+    for k in kernels:
+        h.update(kernel_source_hash(k).encode())
+    return h.hexdigest()[:16]
 
 
 def _counter_means(path: str, kernel: str):
@@ -232,22 +250,30 @@ def record_traffic(args) -> int:
     --copy-calib-mib MiB (that many bytes fetched and written)."""
     if not args.copy_calib_mib:
         raise SystemExit("--record-traffic needs the --copy-calib-mib the runs used")
-    P = DEFAULT_PARTITION[args.workload] if args.partition is None else args.partition
-    kernel = decode_kernel_name(P)
     known_kib = args.copy_calib_mib * 1024.0
-    fetch, fcopy, n = _counter_means(args.record_traffic[0], kernel)
-    write, wcopy, _ = _counter_means(args.record_traffic[1], kernel)
+    if args.workload in CALL_KERNELS:
+        kernels = list(CALL_KERNELS[args.workload])
+    else:
+        P = DEFAULT_PARTITION[args.workload] if args.partition is None else args.partition
+        kernels = [decode_kernel_name(P)]
+    fetch = write = 0.0
+    for k in kernels:
+        f, fcopy, n = _counter_means(args.record_traffic[0], k)
+        w, wcopy, _ = _counter_means(args.record_traffic[1], k)
+        fetch, write = fetch + f, write + w
     fs, wsc = known_kib / fcopy, known_kib / wcopy
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     data = json.load(open(path)) if os.path.exists(path) else {}
     key = traffic_key(args, args.bs)
-    data[key] = {
-        "kernel": kernel, "kernel_source_hash": kernel_source_hash(kernel),
+    rec = {"kernel": kernels[0]} if len(kernels) == 1 else {"kernels": kernels}
+    rec.update({
+        "kernel_source_hash": kernels_source_hash(kernels),
         "hbm_bytes_per_launch": int(round((fetch * fs + write * wsc) * 1024)),
         "fetch_size_kib": round(fetch, 1), "fetch_scale": round(fs, 4),
         "write_size_kib": round(write, 1), "write_scale": round(wsc, 4),
         "dispatches": n,
-    }
+    })
+    data[key] = rec
     with open(path, "w") as f:
         json.dump(data, f, indent=1)
         f.write("\n")
@@ -489,6 +515,12 @@ def bench_multi(args) -> int:
     stream = torch.cuda.current_stream()
     P = MULTI_PARTITION[args.workload] if args.partition is None else args.partition
     ws = pkv.allocate_multi_workspace(c.S, mc.max_query_len, c.Hq, c.D, c.max_seq_len, P)
+    if args.copy_calib_mib:                # a copy of known size, for HBM counter scaling
+        a = torch.empty(args.copy_calib_mib << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     def call(i):
         kc, vc = layers[i % len(layers)]
@@ -517,9 +549,11 @@ def bench_multi(args) -> int:
     if args.workload == "spec-verify":
         metric = "paged multi-query attention: achieved HBM TB/s (% of peak) + query tokens/s/layer"
         value, unit = nbytes / call_s / 1e12, "TB/s"
+        traffic = (traffic_from_profiles(traffic_key(args, c.bs), nbytes)
+                   if args.partition is None else None)
         roof = {"bound": "hbm", "kernel": "paged_attention_multi",
                 "achieved": round(nbytes / call_s / 1e9, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(nbytes / call_s / 1e9 / PEAK_GBPS, 4), "traffic": None}
+                "frac": round(nbytes / call_s / 1e9 / PEAK_GBPS, 4), "traffic": traffic}
     else:
         metric = "paged multi-query attention: achieved TFLOP/s (% of bf16 MFMA peak) + query tokens/s/layer"
         value, unit = flops / call_s / 1e12, "TFLOP/s"
