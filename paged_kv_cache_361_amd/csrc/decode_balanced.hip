@@ -44,6 +44,21 @@
 // of the chunk after its current one (the counter's atomic add) are all
 // requested one step ahead, and the lengths and tile prefix the walk needs
 // are held in LDS, so moving on never drains the ring.
+//
+// K tiles in LDS.  Where the ring's K slots fit beside the prefix arrays
+// (16-byte caches at head_dim 128: 96 KiB per workgroup, so up to about 8,000
+// sequences, 5,400 with query starts or geometries), the K rows go from
+// memory straight into a slot of LDS in row order and are read back in the
+// operand layout (TileMath<..., KLDS>); V stays in registers.  The loads
+// carry no register the compiler could wait on, so the consumer waits with
+// an explicit count before reading slot j: every round issues all DEPTH
+// tiles in ring order (dead tiles read nothing but still count), so once at
+// most the loads of the DEPTH - 1 tiles issued after slot j's are in flight,
+// slot j's are done.  Scheduling barriers keep whole tiles in ring order.
+// On MI355X this took the 40-head MHA layer from 297.7 to 271.2 µs per call
+// (decode + reduce) and the mixed-block-size batch from 253.5 to 251.8; the
+// 8-head GQA layers read alike either way (246.7 against 245.3 µs, long
+// contexts 430.3 against 433.9).
 #include "split_units.hpp"
 #include "tile_mfma.hpp"
 
@@ -124,6 +139,16 @@ __device__ inline int settled(int x) {
     int y;
     asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
     return y;
+}
+
+// Bytes of the kernel's LDS arrays: the tile prefix and the lengths, plus
+// query_start (MULTI) or the geometries (MIXED); LDS-staged K slots start at
+// the next 256-byte boundary.
+__host__ __device__ constexpr size_t lds_bytes(int S, bool wide) {
+    return (size_t)((wide ? 3 : 2) * S + (wide ? 2 : 1)) * sizeof(int);
+}
+__host__ __device__ constexpr size_t ring_offset(int S, bool wide) {
+    return (lds_bytes(S, wide) + 255) & ~(size_t)255;
 }
 
 // ---- tile prefix ----------------------------------------------------------
@@ -334,10 +359,12 @@ struct Walk {
 // MIXED: block sizes per sequence over a pool of pages (p.bs tokens each,
 // as decode_mixed_kernel): each sequence walks its own block size, and
 // sequences of 8-token blocks walk 8-token tiles.
-template <class Q, class C, int D, bool PAIR, int DEPTH, bool MULTI, bool MIXED>
+// KLDS: K tiles staged in LDS (TileMath); the ring's K slots follow the
+// prefix arrays in LDS (ring_offset).
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool MULTI, bool MIXED, bool KLDS>
 __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeParams p) {
     static_assert(!(MULTI && MIXED) && !(PAIR && MIXED), "one mode at a time");
-    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef TileMath<Q, C, D, PAIR, KLDS> TM;
     typedef typename TM::T T;
     typedef typename TM::v8 v8;
     extern __shared__ int lds[];
@@ -569,15 +596,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
 
     // ---- consumer: one round behind, on the producer's previous span ------
     typename TM::Tile tl[DEPTH];
+    // KLDS: this wave's K slots, one per ring buffer
+    lds_t* const kring =
+        (lds_t*)((char*)lds + ring_offset(p.S, MULTI || MIXED)) +
+        (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DEPTH * TM::kKSlot;
+    auto kslot = [&](int j) { return kring + j * TM::kKSlot; };
 #pragma unroll
     for (int j = 0; j < DEPTH; j++) {
         const int tp = prt + j;
         if constexpr (MIXED) {
             const int ts = code_ts(ps.key >> 25);
             tm.issue(hd, tp << ts, tp < ps.t1 ? min(ps.L - 1 - (tp << ts), (1 << ts) - 1) : -1,
-                     ps.wb, win, tl[j]);
+                     ps.wb, win, tl[j], kslot(j));
         } else
-            tm.issue(hd, tp << 4, tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1, ps.wb, win, tl[j]);
+            tm.issue(hd, tp << 4, tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1, ps.wb, win, tl[j],
+                     kslot(j));
+        if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
     }
     // consumer's span: its stream, length, end tile, chunk and flags
     int c_key = ps.key, c_L = ps.L, c_t1 = ps.t1, c_chunk = ps.chunk, c_flags = ps.flags;
@@ -599,26 +633,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
 #pragma unroll
         for (int j = 0; j < DEPTH; j++) {
             const int tc = crt + j;
+            if constexpr (KLDS) {
+                // Slot j's K loads are done once at most the loads of the
+                // DEPTH - 1 tiles issued after them are in flight (every
+                // round issues all DEPTH tiles, dead ones included, in ring
+                // order; the round's requests and the tile's own V loads
+                // only add to the count, so this may wait a little early).
+                vm_wait<(DEPTH - 1) * (TM::KL + 4)>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (j == 0 || tc < c_t1) {
                 if constexpr (MULTI)
                     tm.template consume<true>(acc, qb, p.scale_log2, c_L - 1 - (tc << 4), tl[j],
-                                              c_pc - (tc << 4));
+                                              c_pc - (tc << 4), kslot(j));
                 else
                     tm.consume(acc, qb, p.scale_log2,
                                MIXED ? min(c_L - 1 - (tc << c_ts), (1 << c_ts) - 1)
                                      : c_L - 1 - (tc << 4),
-                               tl[j]);
+                               tl[j], 0, kslot(j));
             }
+            if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
             const int tp = prt + j;
             if constexpr (MIXED) {
                 const int ts = code_ts(ps.key >> 25);
                 const int plim =
                     has_ps && tp < ps.t1 ? min(ps.L - 1 - (tp << ts), (1 << ts) - 1) : -1;
-                tm.issue(hd, tp << ts, plim, ps.wb, win, tl[j]);
+                tm.issue(hd, tp << ts, plim, ps.wb, win, tl[j], kslot(j));
             } else {
                 const int plim = has_ps && tp < ps.t1 ? ps.L - 1 - (tp << 4) : -1;
-                tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j]);
+                tm.issue(hd, tp << 4, plim, ps.wb, win, tl[j], kslot(j));
             }
+            if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
         }
         take();
         // Consumer first: finish its span and take the producer's current
@@ -699,10 +744,8 @@ constexpr int pipeline_depth() {
     return PAIR ? 4 : (D == 64 ? 8 : 6);
 }
 
-// prefix and lengths, plus query_start (MULTI) or geometries (MIXED)
-inline size_t lds_bytes(int S, bool wide) {
-    return (size_t)((wide ? 3 : 2) * S + (wide ? 2 : 1)) * sizeof(int);
-}
+// LDS of one compute unit (gfx950).
+constexpr size_t kLdsPerCu = 160 * 1024;
 
 template <class Q, class C, int D, bool PAIR>
 hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
@@ -711,18 +754,34 @@ hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
     constexpr int DP = pipeline_depth<C, D, PAIR>();
     const bool multi = p.q_start != nullptr;
     const bool mixed = p.seq_bs != nullptr;
-    const void* k =
-        multi ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, DP, true, false>)
-        : mixed ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, true>)
-                : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, PAIR, DP, false, false>);
-    return hipLaunchKernel(k, grid, block, args, lds_bytes(p.S, multi || mixed), st);
+    // K staged in LDS where the ring's slots fit beside the prefix arrays
+    constexpr size_t ring = (size_t)kWaves * DP * TileMath<Q, C, D, false, true>::kKSlot;
+    const size_t lds_k = ring_offset(p.S, multi || mixed) + ring;
+    // (8-token blocks of a uniform pool take the two-block PAIR tile, which
+    // keeps K in registers)
+    const bool klds = !PAIR && lds_k <= kLdsPerCu;
+    const void* k = nullptr;
+    if constexpr (PAIR) {
+        k = multi ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, true, false, false>)
+                  : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, false, false, false>);
+    } else if (multi) {
+        k = klds ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, true, false, true>)
+                 : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, true, false, false>);
+    } else if (mixed) {
+        k = klds ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, true, true>)
+                 : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, true, false>);
+    } else {
+        k = klds ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, false, true>)
+                 : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, false, DP, false, false, false>);
+    }
+    return hipLaunchKernel(k, grid, block, args, klds ? lds_k : lds_bytes(p.S, multi || mixed), st);
 }
 
 template <class Q, class C, int D, bool PAIR>
 int resident_k(int S) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false, false>,
+            &blocks, decode_balanced_kernel<Q, C, D, PAIR, pipeline_depth<C, D, PAIR>(), false, false, false>,
             64 * kWaves, lds_bytes(S, true)) != hipSuccess)
         return 0;
     // one workgroup per CU = one wavefront per SIMD, also where the

@@ -62,6 +62,23 @@ constexpr uint32_t kOOB = 0x80000000u;  // past any descriptor range: reads 0
 constexpr int kStream = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) char lds_t;
+
+// s_waitcnt on the vector-memory count alone (expcnt and lgkmcnt at their
+// maxima): returns once at most N vector-memory instructions of the wave
+// are still in flight.  The count field is 6 bits, split low 4 / high 2.
+template <int N>
+__device__ inline void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// A 16-byte LDS read through a restrict pointer: the compiler then does not
+// treat it as possibly reading what an LDS-direct load still in flight
+// writes, and adds no wait of its own for those loads.
+__device__ inline u32x4 lds_read16(const lds_t* __restrict__ p) {
+    return *(const __attribute__((address_space(3))) u32x4*)p;
+}
 
 // Raw buffer descriptor over [base, base + bytes): stride 0, 32-bit format
 // word of the gfx9 family.
@@ -173,8 +190,16 @@ __device__ inline Head make_head(const DecodeParams& p, int h) {
 }
 
 // PAIR: block size 8, so a 16-token tile spans two blocks.
-template <class Q, class C, int D, bool PAIR>
+// KLDS: the K tile goes from memory straight into LDS, row by row
+// (buffer_load ... lds), and is read back in the operand layout (see
+// issue_as and consume); otherwise K rows load into registers directly in the
+// operand layout.  Row-order loads cover 4 rows x 256 bytes per instruction
+// where the operand layout covers 16 rows x 64 bytes, and on MI355X a read
+// probe of the decode's own tiles streamed the 40-head pool (10 KiB between
+// a head's rows) 16% faster that way, and the 8-head pool 4% faster.
+template <class Q, class C, int D, bool PAIR, bool KLDS = false>
 struct TileMath {
+    static_assert(!(KLDS && PAIR), "LDS-staged K tiles lie in one block");
     typedef Mfma<Q> M;
     typedef typename M::T T;
     typedef typename M::v8 v8;
@@ -187,11 +212,31 @@ struct TileMath {
     static constexpr int VB = NT * EB;             // bytes of one V row slice per lane
     typedef T vrow __attribute__((ext_vector_type(NT)));
     typedef typename Buf<VB>::T vraw;
+    // LDS-staged K: 16-byte pieces per row, rows per load instruction, and
+    // the bytes of one tile's 16 rows
+    static constexpr int KR = D * EB / 16;
+    static constexpr int kRowsPerLoad = 64 / KR;
+    static constexpr int kKSlot = 16 * 16 * KR;
+    static_assert(KL * 1024 == kKSlot, "a tile's K is KL loads of 1 KiB");
 
-    struct Tile {
+    struct TileRegs {
         u32x4 k[KL];
         vraw v[4];
     };
+    struct TileLds {
+        vraw v[4];
+    };
+    typedef std::conditional_t<KLDS, TileLds, TileRegs> Tile;
+
+    // Piece p of K row r is stored at piece p ^ kswz(r) of the row's LDS
+    // slot, so that the 16 rows one operand read touches (one piece each)
+    // fall on distinct banks: r % 16 for rows of 16 or more pieces, r / 2 % 8
+    // for 8 pieces (two rows per 64 banks), r / 4 % 4 for 4 pieces.
+    __device__ static inline int kswz(int r) {
+        if constexpr (KR >= 16) return r & 15;
+        else if constexpr (KR == 8) return (r >> 1) & 7;
+        else return (r >> 2) & 3;
+    }
     // Running state of one (sequence piece, KV head): reference max and this
     // lane's share of the sum for head lane%16, accumulator rows 4*(lane/16)+r.
     struct Acc {
@@ -203,6 +248,10 @@ struct TileMath {
     int lane, g4, j16;
     uint32_t kcol[KL];     // lane-constant byte offsets inside a slot row
     uint32_t vcol;
+    // KLDS: row of load i this lane fills and the byte offset of its piece
+    // in that row; byte offset of operand piece i in the tile's LDS slot
+    int kdr[KLDS ? KL : 1];
+    uint32_t kdp[KLDS ? KL : 1], krd[KLDS ? KL : 1];
 
     __device__ TileMath() {
         lane = threadIdx.x & 63;
@@ -212,6 +261,17 @@ struct TileMath {
         for (int i = 0; i < KL; i++)
             kcol[i] = kFp8 ? (uint32_t)(64 * i + 16 * g4) : (uint32_t)((32 * i + 8 * g4) * EB);
         vcol = (uint32_t)(NT * j16 * EB);
+        if constexpr (KLDS) {
+#pragma unroll
+            for (int i = 0; i < KL; i++) {
+                // load i fills rows kRowsPerLoad i .. with lane-consecutive
+                // 16-byte LDS slots: lane -> (row, slot piece lane % KR)
+                kdr[i] = kRowsPerLoad * i + lane / KR;
+                kdp[i] = 16u * (uint32_t)((lane % KR) ^ kswz(kdr[i]));
+                // the operand wants piece kcol[i] / 16 of row j16
+                krd[i] = (uint32_t)(j16 * 16 * KR) + 16u * (uint32_t)(((int)kcol[i] / 16) ^ kswz(j16));
+            }
+        }
     }
 
     // Query heads of the group as the B operand of the score product; `q`
@@ -242,16 +302,19 @@ struct TileMath {
     // from block wb on (t0's block and, with PAIR, the next one must lie in
     // the window when live).
     __device__ inline void issue(const Head& hd, int t0, int lim, int wb, int win,
-                                 Tile& tl) const {
-        issue_as<PAIR>(hd, t0, lim, wb, win, tl);
+                                 Tile& tl, lds_t* kslot = nullptr) const {
+        issue_as<PAIR>(hd, t0, lim, wb, win, tl, kslot);
     }
 
     // issue() for 8-token blocks (PR) or larger ones, whatever the tile's
     // own PAIR: a kernel whose wavefronts meet both block sizes picks per
     // wavefront.
+    // KLDS: kslot (wave-uniform) receives the tile's K rows, kKSlot bytes;
+    // rows past lim are written as zeros.  The caller waits for the loads
+    // (vm_wait) before consume() reads them.
     template <bool PR>
     __device__ inline void issue_as(const Head& hd, int t0, int lim, int wb, int win,
-                                    Tile& tl) const {
+                                    Tile& tl, lds_t* kslot = nullptr) const {
         uint32_t pa = 0, pb = 0;
         if (lim >= 0) {
             const int blk = (t0 >> hd.bs_shift) - wb;
@@ -264,7 +327,23 @@ struct TileMath {
         }
         const rsrc_t ka = make_rsrc(hd.kbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
         const rsrc_t va = make_rsrc(hd.vbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
-        if constexpr (!PR) {
+        if constexpr (KLDS) {
+            static_assert(!PR, "LDS-staged K tiles lie in one block");
+            const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
+#pragma unroll
+            for (int i = 0; i < KL; i++) {
+                const uint32_t off =
+                    kdr[i] <= lim ? (in_blk + (uint32_t)kdr[i]) * hd.row_bytes + kdp[i] : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ka, (lds_t*)(kslot + 1024 * i), 16, off, 0, 0,
+                                                         kStream);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int tv = 4 * g4 + r;
+                const uint32_t voff = tv <= lim ? (in_blk + (uint32_t)tv) * hd.row_bytes : kOOB;
+                tl.v[r] = Buf<VB>::stream(va, voff + vcol);
+            }
+        } else if constexpr (!PR) {
             const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
             const uint32_t krow = j16 <= lim ? (in_blk + (uint32_t)j16) * hd.row_bytes : kOOB;
 #pragma unroll
@@ -306,10 +385,20 @@ struct TileMath {
     // MASK = false: the caller knows that every column it keeps sees every
     // row of the tile, so no limit is applied (the same result, fewer
     // vector instructions).
+    // KLDS: kslot holds the tile's K rows (the loads complete).
     template <bool CAUSAL = false, bool MASK = true>
     __device__ inline void consume(Acc& a, const v8 (&qb)[KS], float scale_log2, int lim,
-                                   const Tile& cur, int clim = 0) const {
-        const f32x4 sc = scores(qb, cur);
+                                   const Tile& cur, int clim = 0,
+                                   const lds_t* kslot = nullptr) const {
+        u32x4 kf[KL];
+        if constexpr (KLDS) {
+#pragma unroll
+            for (int i = 0; i < KL; i++) kf[i] = lds_read16(kslot + krd[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < KL; i++) kf[i] = cur.k[i];
+        }
+        const f32x4 sc = scores(qb, kf);
         v4 p_hi, p_lo;
         weights<CAUSAL, MASK>(a, sc, scale_log2, lim, clim, p_hi, p_lo);
         vrow vr[4];
@@ -348,22 +437,23 @@ struct TileMath {
         }
     }
 
-    // Scores of the tile's 16 rows against the 16 B columns.
-    __device__ inline f32x4 scores(const v8 (&qb)[KS], const Tile& cur) const {
+    // Scores of the tile's 16 rows (K in the operand layout) against the 16 B
+    // columns.
+    __device__ inline f32x4 scores(const v8 (&qb)[KS], const u32x4 (&k)[KL]) const {
         f32x4 sc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < KL; i++) {
             if constexpr (kFp8) {
-                const v4 a0 = M::from_fp8x4(cur.k[i][0]);
-                const v4 a1 = M::from_fp8x4(cur.k[i][1]);
-                const v4 a2 = M::from_fp8x4(cur.k[i][2]);
-                const v4 a3 = M::from_fp8x4(cur.k[i][3]);
+                const v4 a0 = M::from_fp8x4(k[i][0]);
+                const v4 a1 = M::from_fp8x4(k[i][1]);
+                const v4 a2 = M::from_fp8x4(k[i][2]);
+                const v4 a3 = M::from_fp8x4(k[i][3]);
                 const v8 k0 = v8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
                 const v8 k1 = v8{a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
                 sc = M::qk(k0, qb[2 * i], sc);
                 sc = M::qk(k1, qb[2 * i + 1], sc);
             } else {
-                sc = M::qk(__builtin_bit_cast(v8, cur.k[i]), qb[i], sc);
+                sc = M::qk(__builtin_bit_cast(v8, k[i]), qb[i], sc);
             }
         }
         return sc;
