@@ -495,13 +495,17 @@ def test_balanced_workspace_contents_do_not_matter(fill):
     check(c, from_dev(outs[0]), oracle_run(c))
 
 
-def test_balanced_largest_batch():
+@pytest.mark.parametrize("D", [64, 128])
+def test_balanced_largest_batch(D):
     """8192 sequences, the most the balanced split takes (the lengths and the
     tile prefix fill 64 KiB of LDS; each thread scans 32 sequences), with
-    short ragged lengths including zeros; every row is checked."""
+    short ragged lengths including zeros; every row is checked.  At head_dim
+    64 the K tiles still go through LDS (a 64 KiB ring beside the prefix); at
+    128 the 96 KiB ring no longer fits beside it and the kernel that loads K
+    into registers runs."""
     rng = np.random.default_rng(95)
     lens = rng.integers(0, 40, size=8192)
-    c = workloads.make_case("largest-batch", 95, lens, 8, 2, 64, 16, q_dtype="bf16",
+    c = workloads.make_case("largest-batch", 95, lens, 8, 2, D, 16, q_dtype="bf16",
                             cache_dtype="bf16", max_seq_len=64)
     out = gpu_run(c, "mfma", BAL)
     ref = oracle_run(c)
