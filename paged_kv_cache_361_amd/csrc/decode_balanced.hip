@@ -727,6 +727,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
         producer_advance();
         request();
     }
+    // The ring's last round (dead tiles, zeros) may still be landing in the
+    // K slots: let it land before the workgroup's LDS is handed on.
+    if constexpr (KLDS) vm_wait<0>();
 }
 
 // One wavefront per SIMD, with deep rings.  Two waves on one SIMD do not
