@@ -36,11 +36,16 @@ constexpr int kWaves = 4;
 // flight during the arithmetic; loads are issued unconditionally (dead tiles
 // read zeros).  The unit is walked in windows of 64 table entries (one per
 // lane); a split-K partition of at most 64 blocks is a single window.  PR:
-// 8-token blocks (a tile spans two).
-template <bool PR, int DEPTH, class TM>
+// 8-token blocks (a tile spans two).  KLDS: TM stages K tiles in LDS, slot j
+// of the ring at kring + j * TM::kKSlot; the loads carry no register to wait
+// on, so slot j is read once at most the loads of the DEPTH - 1 tiles issued
+// after it are in flight (every round issues all DEPTH tiles in ring order,
+// dead ones included; scheduling barriers keep whole tiles in that order).
+template <bool PR, int DEPTH, bool KLDS = false, class TM>
 __device__ inline void walk_unit(const TM& tm, const Head& hd, const int32_t* table,
                                  int t_begin, int t_end, const typename TM::v8 (&qb)[TM::KS],
-                                 float scale_log2, typename TM::Acc& acc) {
+                                 float scale_log2, typename TM::Acc& acc,
+                                 lds_t* kring = nullptr) {
     const int lane = tm.lane;
     const int nblk = (t_end + (1 << hd.bs_shift) - 1) >> hd.bs_shift;   // table entries used
     const int wtok = 64 << hd.bs_shift;
@@ -50,15 +55,25 @@ __device__ inline void walk_unit(const TM& tm, const Head& hd, const int32_t* ta
         const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
         typename TM::Tile tl[DEPTH];
 #pragma unroll
-        for (int j = 0; j < DEPTH; j++)
-            tm.template issue_as<PR>(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int j = 0; j < DEPTH; j++) {
+            tm.template issue_as<PR>(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j],
+                                     kring + j * TM::kKSlot);
+            if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
+        }
         for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
 #pragma unroll
             for (int j = 0; j < DEPTH; j++) {
                 const int tj = t0 + 16 * j;
-                if (j == 0 || tj < w1) tm.consume(acc, qb, scale_log2, t_end - 1 - tj, tl[j]);
+                if constexpr (KLDS) {
+                    vm_wait<(DEPTH - 1) * (TM::KL + 4)>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if (j == 0 || tj < w1)
+                    tm.consume(acc, qb, scale_log2, t_end - 1 - tj, tl[j], 0, kring + j * TM::kKSlot);
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
                 const int tn = tj + 16 * DEPTH;
-                tm.template issue_as<PR>(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+                tm.template issue_as<PR>(hd, tn, w1 - 1 - tn, wb, win, tl[j], kring + j * TM::kKSlot);
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -86,9 +101,11 @@ __device__ inline bool select_unit(const DecodeParams& p, int* s_out, int* part_
 }
 
 // DEPTH: tiles whose loads are issued ahead of the arithmetic (the ring).
-template <class Q, class C, int D, bool PAIR, int DEPTH>
+// KLDS: K tiles staged in LDS (TileMath), DEPTH slots per wave.
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool KLDS>
 __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p) {
-    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef TileMath<Q, C, D, PAIR, KLDS> TM;
+    extern __shared__ __attribute__((aligned(16))) char lds_k[];
     typedef typename TM::T T;
     const TM tm;
     const int lane = tm.lane;
@@ -116,8 +133,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
     const Head hd = make_head<C, D>(p, h);
     typename TM::Acc acc;
     tm.reset(acc);
-    walk_unit<PAIR, DEPTH>(tm, hd, p.tables + (size_t)s * p.max_blocks, t_begin, t_end, qb,
-                           p.scale_log2, acc);
+    lds_t* const kring =
+        (lds_t*)lds_k + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DEPTH * TM::kKSlot;
+    walk_unit<PAIR, DEPTH, KLDS>(tm, hd, p.tables + (size_t)s * p.max_blocks, t_begin, t_end, qb,
+                                 p.scale_log2, acc, kring);
 
     const size_t row0 = (size_t)s * p.Hq + (size_t)h * G;
     tm.finish(
@@ -126,6 +145,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
         [&](int head) { return p.ws_m + (row0 + head) * p.P_max + part; },
         [&](int head) { return p.ws_l + (row0 + head) * p.P_max + part; },
         [&](int head) { return p.ws_o + ((row0 + head) * p.P_max + part) * D; });
+    // the ring's last round (dead tiles, zeros) may still be landing in the
+    // K slots: let it land before the workgroup's LDS is handed on
+    if constexpr (KLDS) vm_wait<0>();
 }
 
 // Mixed block sizes ("vLLM 0.5 深度拆解" §1.3: 8, 16 or 32 tokens per
@@ -199,13 +221,20 @@ constexpr int pipeline_depth() {
     return PAIR ? 2 : 4;
 }
 
+// Blocks of 16 or 32 tokens take K tiles staged in LDS (row-order loads,
+// read back in the operand layout; see TileMath): kWaves * 4 slots, 64 KiB
+// per workgroup for 16-bit K at head_dim 128, so two workgroups share a CU.
 template <class Q, class C, int D>
 hipError_t launch_dd(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
     if (p.bs == 8)
-        return launch_kernel(decode_mfma_kernel<Q, C, D, true, pipeline_depth<true>()>, grid,
-                             block, st, p);
-    return launch_kernel(decode_mfma_kernel<Q, C, D, false, pipeline_depth<false>()>, grid,
-                         block, st, p);
+        return launch_kernel(decode_mfma_kernel<Q, C, D, true, pipeline_depth<true>(), false>,
+                             grid, block, st, p);
+    constexpr int DP = pipeline_depth<false>();
+    constexpr size_t lds = (size_t)kWaves * DP * TileMath<Q, C, D, false, true>::kKSlot;
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(decode_mfma_kernel<Q, C, D, false, DP, true>), grid, block,
+        args, lds, st);
 }
 
 template <class Q, class C>
