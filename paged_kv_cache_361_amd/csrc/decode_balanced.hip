@@ -49,7 +49,9 @@
 // (16-byte caches at head_dim 128: 96 KiB per workgroup, so up to about 8,000
 // sequences, 5,400 with query starts or geometries), the K rows go from
 // memory straight into a slot of LDS in row order and are read back in the
-// operand layout (TileMath<..., KLDS>); V stays in registers.  The loads
+// operand layout (TileMath<..., KLDS>); V stays in registers.  A 16-token
+// tile over two 8-token blocks does the same where each row-order load
+// covers rows of one block (at most 8 rows a load).  The loads
 // carry no register the compiler could wait on, so the consumer waits with
 // an explicit count before reading slot j: every round issues all DEPTH
 // tiles in ring order (dead tiles read nothing but still count), so once at
@@ -639,7 +641,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void decode_balanced_kernel(DecodeP
                 // round issues all DEPTH tiles, dead ones included, in ring
                 // order; the round's requests and the tile's own V loads
                 // only add to the count, so this may wait a little early).
-                vm_wait<(DEPTH - 1) * (TM::KL + 4)>();
+                vm_wait<(DEPTH - 1) * TM::kLoadsPerTile>();
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (j == 0 || tc < c_t1) {
@@ -760,11 +762,20 @@ hipError_t launch_k(const DecodeParams& p, hipStream_t st) {
     // K staged in LDS where the ring's slots fit beside the prefix arrays
     constexpr size_t ring = (size_t)kWaves * DP * TileMath<Q, C, D, false, true>::kKSlot;
     const size_t lds_k = ring_offset(p.S, multi || mixed) + ring;
-    // (8-token blocks of a uniform pool take the two-block PAIR tile, which
-    // keeps K in registers)
-    const bool klds = !PAIR && lds_k <= kLdsPerCu;
+    // (8-token blocks of a uniform pool take the two-block PAIR tile; its K
+    // goes through LDS too where each row-order load lies in one block, that
+    // is with at most 8 rows per load)
+    constexpr bool can = !PAIR || 1024 / (D * C::kBytes) <= 8;
+    const bool klds = can && lds_k <= kLdsPerCu;
     const void* k = nullptr;
     if constexpr (PAIR) {
+        if constexpr (can) {
+            if (klds) {
+                k = multi ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, true, false, true>)
+                          : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, false, false, true>);
+                return hipLaunchKernel(k, grid, block, args, lds_k, st);
+            }
+        }
         k = multi ? reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, true, false, false>)
                   : reinterpret_cast<const void*>(decode_balanced_kernel<Q, C, D, true, DP, false, false, false>);
     } else if (multi) {

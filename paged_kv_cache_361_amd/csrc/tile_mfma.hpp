@@ -199,7 +199,6 @@ __device__ inline Head make_head(const DecodeParams& p, int h) {
 // a head's rows) 16% faster that way, and the 8-head pool 4% faster.
 template <class Q, class C, int D, bool PAIR, bool KLDS = false>
 struct TileMath {
-    static_assert(!(KLDS && PAIR), "LDS-staged K tiles lie in one block");
     typedef Mfma<Q> M;
     typedef typename M::T T;
     typedef typename M::v8 v8;
@@ -218,6 +217,10 @@ struct TileMath {
     static constexpr int kRowsPerLoad = 64 / KR;
     static constexpr int kKSlot = 16 * 16 * KR;
     static_assert(KL * 1024 == kKSlot, "a tile's K is KL loads of 1 KiB");
+    // a load of an LDS-staged two-block tile must lie in one block
+    static_assert(!(KLDS && PAIR) || kRowsPerLoad <= 8, "LDS-direct loads within one block");
+    // vector-memory instructions issue() makes per tile
+    static constexpr int kLoadsPerTile = (KLDS ? KL : (PAIR ? 2 : 1) * KL) + (PAIR ? 8 : 4);
 
     struct TileRegs {
         u32x4 k[KL];
@@ -327,8 +330,31 @@ struct TileMath {
         }
         const rsrc_t ka = make_rsrc(hd.kbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
         const rsrc_t va = make_rsrc(hd.vbase + (size_t)pa * hd.blk_bytes, hd.rec_bytes);
-        if constexpr (KLDS) {
-            static_assert(!PR, "LDS-staged K tiles lie in one block");
+        if constexpr (KLDS && PR) {
+            static_assert(PAIR, "the ring's tiles are counted as two-block ones");
+            // 8-token blocks: the tile starts a block, rows 0-7 lie in block
+            // a and rows 8-15 in block b, and each row-order load covers
+            // rows of one block only
+            const rsrc_t kb = make_rsrc(hd.kbase + (size_t)pb * hd.blk_bytes, hd.rec_bytes);
+            const rsrc_t vb = make_rsrc(hd.vbase + (size_t)pb * hd.blk_bytes, hd.rec_bytes);
+#pragma unroll
+            for (int i = 0; i < KL; i++) {
+                const uint32_t off =
+                    kdr[i] <= lim ? (uint32_t)(kdr[i] & 7) * hd.row_bytes + kdp[i] : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(kRowsPerLoad * i >= 8 ? kb : ka,
+                                                         (lds_t*)(kslot + 1024 * i), 16, off, 0, 0,
+                                                         kStream);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int tv = 4 * g4 + r;
+                const uint32_t vo = (uint32_t)(tv & 7) * hd.row_bytes;
+                const uint32_t voa = tv <= lim && tv < 8 ? vo : kOOB;
+                const uint32_t vob = tv <= lim && tv >= 8 ? vo : kOOB;
+                tl.v[r] = Buf<VB>::stream(va, voa + vcol) | Buf<VB>::stream(vb, vob + vcol);
+            }
+        } else if constexpr (KLDS) {
+            static_assert(!PAIR, "the ring's tiles are counted as one-block ones");
             const uint32_t in_blk = (uint32_t)(t0 & ((1 << hd.bs_shift) - 1));
 #pragma unroll
             for (int i = 0; i < KL; i++) {
