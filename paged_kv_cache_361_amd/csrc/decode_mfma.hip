@@ -30,6 +30,10 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 
+// head_dim of a tile math type
+template <class TM>
+__device__ constexpr int D_of() { return TM::NT * 16; }
+
 // Walks tokens [t_begin, t_end) of one unit: DEPTH tiles in flight in a ring
 // of tile buffers unrolled by hand.  Tile j of each round is consumed, then
 // refilled with the tile DEPTH positions ahead, so DEPTH - 1 tiles stay in
@@ -157,13 +161,45 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mfma_kernel(DecodeParams p
 // the table is walked in bs_s-token steps, a block's base is (entry * p.bs)
 // rows in, and its descriptor covers bs_s rows.  Each wavefront runs the
 // 8-token-block loop or the larger-block one for its own sequence.  A block
-// size outside [page, 32] is taken as the nearest of the two.
+// size outside [page, 32] is taken as the nearest of the two.  K tiles go
+// through LDS as in decode_mfma_kernel (on MI355X the mixed-size batch at
+// P = 512 went from 290.9 to 274.5 µs per call).
+// One unit of the mixed-size kernel on the tile math TM: 8-token blocks (PR,
+// a tile spans two) or larger ones, K staged in LDS when KLDS.
+template <bool PR, int DEPTH, bool KLDS, class TM>
+__device__ inline void mixed_unit(const TM& tm, const DecodeParams& p, const Head& hd,
+                                  const int32_t* table, int s, int h, int part, int t_begin,
+                                  int t_end, bool final_out, lds_t* kring) {
+    typedef typename TM::T T;
+    const int G = p.G;
+    T* out = (T*)p.out + ((size_t)s * p.Hq + (size_t)h * G) * D_of<TM>();
+    typename TM::v8 qb[TM::KS];
+    tm.load_q((const T*)p.q + ((size_t)s * p.Hq + (size_t)h * G) * D_of<TM>(), G, qb);
+    typename TM::Acc acc;
+    tm.reset(acc);
+    walk_unit<PR, DEPTH, KLDS>(tm, hd, table, t_begin, t_end, qb, p.scale_log2, acc, kring);
+    const size_t row0 = (size_t)s * p.Hq + (size_t)h * G;
+    constexpr int D = D_of<TM>();
+    tm.finish(
+        acc, G, final_out, p.v_scale,
+        [&](int head) { return out + (size_t)head * D; },
+        [&](int head) { return p.ws_m + (row0 + head) * p.P_max + part; },
+        [&](int head) { return p.ws_l + (row0 + head) * p.P_max + part; },
+        [&](int head) { return p.ws_o + ((row0 + head) * p.P_max + part) * D; });
+    // the ring's last round may still be landing in the K slots
+    if constexpr (KLDS) vm_wait<0>();
+}
+
 template <class Q, class C, int D>
 __global__ __launch_bounds__(64 * kWaves) void decode_mixed_kernel(DecodeParams p) {
-    typedef TileMath<Q, C, D, false> TM;
+    // 16- and 32-token blocks: K staged in LDS (four slots per wave); 8-token
+    // blocks too where each row-order load lies in one block (two slots)
+    typedef TileMath<Q, C, D, false, true> TM;
+    constexpr bool kPairLds = 1024 / (D * C::kBytes) <= 8;
+    typedef TileMath<Q, C, D, true, kPairLds> TM8;
     typedef typename TM::T T;
-    const TM tm;
-    const int lane = tm.lane;
+    extern __shared__ __attribute__((aligned(16))) char lds_k[];
+    const int lane = threadIdx.x & 63;
     int s, part, h;
     if (!select_unit(p, &s, &part, &h)) return;
 
@@ -173,8 +209,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mixed_kernel(DecodeParams 
     int L = p.lens[s];
     L = L < p.len_cap ? L : p.len_cap;
     L = L < (p.max_blocks << shift) ? L : (p.max_blocks << shift);
-    T* out = (T*)p.out + ((size_t)s * p.Hq + (size_t)h * G) * D;
     if (L <= 0) {
+        T* out = (T*)p.out + ((size_t)s * p.Hq + (size_t)h * G) * D;
         for (int i = lane; i < G * D; i += 64) out[i] = (T)0.0f;
         return;
     }
@@ -186,28 +222,20 @@ __global__ __launch_bounds__(64 * kWaves) void decode_mixed_kernel(DecodeParams 
         final_out = (L + p.P - 1) / p.P <= 1;
     }
 
-    typename TM::v8 qb[TM::KS];
-    tm.load_q((const T*)p.q + ((size_t)s * p.Hq + (size_t)h * G) * D, G, qb);
     Head hd = make_head<C, D>(p, h);                  // pages of p.bs tokens
     const uint32_t head_off = (uint32_t)(h * D * C::kBytes);
     hd.bs_shift = shift;
     hd.rec_bytes = (hd.row_bytes << shift) - head_off;
     hd.nb_last = (uint32_t)(p.NB - (1 << (shift - p.page_shift)));
-    typename TM::Acc acc;
-    tm.reset(acc);
     const int32_t* table = p.tables + (size_t)s * p.max_blocks;
+    lds_t* const kring =
+        (lds_t*)lds_k + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 4 * TM::kKSlot;
     if (shift == 3)
-        walk_unit<true, 2>(tm, hd, table, t_begin, t_end, qb, p.scale_log2, acc);
+        mixed_unit<true, 2, kPairLds>(TM8(), p, hd, table, s, h, part, t_begin, t_end, final_out,
+                                      kring);
     else
-        walk_unit<false, 4>(tm, hd, table, t_begin, t_end, qb, p.scale_log2, acc);
-
-    const size_t row0 = (size_t)s * p.Hq + (size_t)h * G;
-    tm.finish(
-        acc, G, final_out, p.v_scale,
-        [&](int head) { return out + (size_t)head * D; },
-        [&](int head) { return p.ws_m + (row0 + head) * p.P_max + part; },
-        [&](int head) { return p.ws_l + (row0 + head) * p.P_max + part; },
-        [&](int head) { return p.ws_o + ((row0 + head) * p.P_max + part) * D; });
+        mixed_unit<false, 4, true>(TM(), p, hd, table, s, h, part, t_begin, t_end, final_out,
+                                   kring);
 }
 
 // Tiles in flight per wavefront.  Four 16-token tiles at head_dim 128 keep
@@ -263,8 +291,16 @@ template <class Q, class C>
 hipError_t launch_mixed_d(const DecodeParams& p, hipStream_t st) {
     const long units = (long)p.S * p.P_max * p.Hkv;
     const dim3 grid((unsigned)((units + kWaves - 1) / kWaves)), block(64 * kWaves);
-    if (p.D == 64) return launch_kernel(decode_mixed_kernel<Q, C, 64>, grid, block, st, p);
-    if (p.D == 128) return launch_kernel(decode_mixed_kernel<Q, C, 128>, grid, block, st, p);
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    // four K slots per wave (the ring of 16- and 32-token blocks)
+    if (p.D == 64)
+        return hipLaunchKernel(reinterpret_cast<const void*>(decode_mixed_kernel<Q, C, 64>), grid,
+                               block, args, (size_t)kWaves * 4 * TileMath<Q, C, 64, false, true>::kKSlot,
+                               st);
+    if (p.D == 128)
+        return hipLaunchKernel(reinterpret_cast<const void*>(decode_mixed_kernel<Q, C, 128>), grid,
+                               block, args, (size_t)kWaves * 4 * TileMath<Q, C, 128, false, true>::kKSlot,
+                               st);
     return hipErrorInvalidValue;
 }
 
