@@ -14,7 +14,9 @@
 // loads feeds every one of them.  Column c drops the tokens past its own
 // position (the causal limit inside the chunk).  A wavefront reads tokens
 // 0 .. (its last query token's position) with the decode kernel's pipeline:
-// windows of 64 table entries, a ring of DEPTH tiles in flight.  Units are
+// windows of 64 table entries, a ring of DEPTH tiles in flight, K tiles
+// staged in LDS in row order (TileMath; on MI355X verification at P = 512
+// went from 364 to 332 µs per call).  Units are
 // numbered with the query group innermost, so the wavefronts that re-read
 // one sequence's K/V for its different groups run side by side and share it
 // through the caches.
@@ -37,9 +39,12 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 
-template <class Q, class C, int D, bool PAIR, int DEPTH, bool SPLIT>
+// KLDS: K tiles staged in LDS, DEPTH slots per wave (TileMath); the ring
+// waits for slot j with an explicit count, as in decode_mfma_kernel.
+template <class Q, class C, int D, bool PAIR, int DEPTH, bool SPLIT, bool KLDS>
 __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p) {
-    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef TileMath<Q, C, D, PAIR, KLDS> TM;
+    extern __shared__ __attribute__((aligned(16))) char lds_k[];
     typedef typename TM::T T;
     typedef typename TM::v8 v8;
     const TM tm;
@@ -114,6 +119,9 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
 
     typename TM::Acc acc;
     tm.reset(acc);
+    lds_t* const kring =
+        (lds_t*)lds_k + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DEPTH * TM::kKSlot;
+    auto kslot = [&](int j) { return kring + j * TM::kKSlot; };
     const int wtok = 64 << hd.bs_shift;
     for (int w0 = t_begin; w0 < t_stop; w0 += wtok) {
         const int w1 = min(t_stop, w0 + wtok);
@@ -121,16 +129,25 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
         const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
         typename TM::Tile tl[DEPTH];
 #pragma unroll
-        for (int j = 0; j < DEPTH; j++)
-            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int j = 0; j < DEPTH; j++) {
+            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j], kslot(j));
+            if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
+        }
         for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
 #pragma unroll
             for (int j = 0; j < DEPTH; j++) {
                 const int tj = t0 + 16 * j;
+                if constexpr (KLDS) {
+                    vm_wait<(DEPTH - 1) * TM::kLoadsPerTile>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (j == 0 || tj < w1)
-                    tm.template consume<true>(acc, qb, p.scale_log2, t_stop - 1 - tj, tl[j], pc - tj);
+                    tm.template consume<true>(acc, qb, p.scale_log2, t_stop - 1 - tj, tl[j], pc - tj,
+                                              kslot(j));
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
                 const int tn = tj + 16 * DEPTH;
-                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j], kslot(j));
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -145,6 +162,8 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
         out_row, [&](int c) { return p.ws_m + row_of(c) * p.P_max + part; },
         [&](int c) { return p.ws_l + row_of(c) * p.P_max + part; },
         [&](int c) { return p.ws_o + (row_of(c) * p.P_max + part) * D; });
+    // the ring's last round may still be landing in the K slots
+    if constexpr (KLDS) vm_wait<0>();
 }
 
 // Long query runs (chunked prefill): every wavefront of the kernel above
@@ -155,9 +174,10 @@ __global__ __launch_bounds__(64 * kWaves) void multi_query_kernel(DecodeParams p
 // tile it loads to all of them: NB times the arithmetic per byte loaded.
 // One pass (no split); one wavefront per SIMD, the accumulators and ring
 // spilling into the accumulation registers.
-template <class Q, class C, int D, bool PAIR, int DEPTH, int NB>
+template <class Q, class C, int D, bool PAIR, int DEPTH, int NB, bool KLDS>
 __global__ __launch_bounds__(64 * kWaves, 1) void multi_query_wide_kernel(DecodeParams p) {
-    typedef TileMath<Q, C, D, PAIR> TM;
+    typedef TileMath<Q, C, D, PAIR, KLDS> TM;
+    extern __shared__ __attribute__((aligned(16))) char lds_k[];
     typedef typename TM::T T;
     typedef typename TM::v8 v8;
     const TM tm;
@@ -214,6 +234,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void multi_query_wide_kernel(Decode
     typename TM::Acc acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) tm.reset(acc[b]);
+    lds_t* const kring =
+        (lds_t*)lds_k + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * DEPTH * TM::kKSlot;
+    auto kslot = [&](int j) { return kring + j * TM::kKSlot; };
     const int wtok = 64 << hd.bs_shift;
     for (int w0 = 0; w0 < t_end; w0 += wtok) {
         const int w1 = min(t_end, w0 + wtok);
@@ -221,20 +244,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void multi_query_wide_kernel(Decode
         const int win = (wb + lane < nblk) ? table[wb + lane] : 0;
         typename TM::Tile tl[DEPTH];
 #pragma unroll
-        for (int j = 0; j < DEPTH; j++)
-            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j]);
+        for (int j = 0; j < DEPTH; j++) {
+            tm.issue(hd, w0 + 16 * j, w1 - 1 - (w0 + 16 * j), wb, win, tl[j], kslot(j));
+            if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
+        }
         for (int t0 = w0; t0 < w1; t0 += 16 * DEPTH) {
 #pragma unroll
             for (int j = 0; j < DEPTH; j++) {
                 const int tj = t0 + 16 * j;
+                if constexpr (KLDS) {
+                    vm_wait<(DEPTH - 1) * TM::kLoadsPerTile>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if (j == 0 || tj < w1) {
 #pragma unroll
                     for (int b = NB - 1; b >= 0; b--)
                         tm.template consume<true>(acc[b], qb[b], p.scale_log2, t_end - 1 - tj,
-                                                  tl[j], pc[b] - tj);
+                                                  tl[j], pc[b] - tj, kslot(j));
                 }
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
                 const int tn = tj + 16 * DEPTH;
-                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j]);
+                tm.issue(hd, tn, w1 - 1 - tn, wb, win, tl[j], kslot(j));
+                if constexpr (KLDS) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -244,6 +275,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void multi_query_wide_kernel(Decode
             acc[b], ncols[b], [&](int) { return true; }, p.v_scale,
             [&](int c) { return out_row(b, c); }, [&](int) { return (float*)nullptr; },
             [&](int) { return (float*)nullptr; }, [&](int) { return (float*)nullptr; });
+    // the ring's last round may still be landing in the K slots
+    if constexpr (KLDS) vm_wait<0>();
 }
 
 // Tiles in flight per wavefront, as in the one-pass decode kernel.
@@ -252,22 +285,45 @@ constexpr int pipeline_depth() {
     return PAIR ? 2 : 4;
 }
 
+// K tiles go through LDS (DEPTH slots per wave), 8-token blocks included
+// where each row-order load covers one block's rows (at most 8 rows a load).
+template <class Q, class C, int D, bool PAIR>
+constexpr bool k_in_lds() {
+    return !PAIR || 1024 / (D * C::kBytes) <= 8;
+}
+template <class Q, class C, int D, bool PAIR>
+constexpr size_t k_ring_bytes() {
+    return (size_t)kWaves * pipeline_depth<PAIR>() * TileMath<Q, C, D, false, true>::kKSlot;
+}
+
+template <class Q, class C, int D, int NB, bool PAIR>
+hipError_t launch_wide_p(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
+    constexpr bool L = k_in_lds<Q, C, D, PAIR>();
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(multi_query_wide_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>(), NB, L>),
+        grid, block, args, L ? k_ring_bytes<Q, C, D, PAIR>() : 0, st);
+}
+
 template <class Q, class C, int D, int NB>
 hipError_t launch_wide(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
-    if (p.bs == 8)
-        return launch_kernel(multi_query_wide_kernel<Q, C, D, true, pipeline_depth<true>(), NB>,
-                             grid, block, st, p);
-    return launch_kernel(multi_query_wide_kernel<Q, C, D, false, pipeline_depth<false>(), NB>,
-                         grid, block, st, p);
+    if (p.bs == 8) return launch_wide_p<Q, C, D, NB, true>(p, grid, block, st);
+    return launch_wide_p<Q, C, D, NB, false>(p, grid, block, st);
+}
+
+template <class Q, class C, int D, bool SPLIT, bool PAIR>
+hipError_t launch_ds_p(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
+    constexpr bool L = k_in_lds<Q, C, D, PAIR>();
+    void* args[] = {const_cast<DecodeParams*>(&p)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(multi_query_kernel<Q, C, D, PAIR, pipeline_depth<PAIR>(), SPLIT, L>),
+        grid, block, args, L ? k_ring_bytes<Q, C, D, PAIR>() : 0, st);
 }
 
 template <class Q, class C, int D, bool SPLIT>
 hipError_t launch_ds(const DecodeParams& p, dim3 grid, dim3 block, hipStream_t st) {
-    if (p.bs == 8)
-        return launch_kernel(multi_query_kernel<Q, C, D, true, pipeline_depth<true>(), SPLIT>,
-                             grid, block, st, p);
-    return launch_kernel(multi_query_kernel<Q, C, D, false, pipeline_depth<false>(), SPLIT>,
-                         grid, block, st, p);
+    if (p.bs == 8) return launch_ds_p<Q, C, D, SPLIT, true>(p, grid, block, st);
+    return launch_ds_p<Q, C, D, SPLIT, false>(p, grid, block, st);
 }
 
 template <class Q, class C, int D>
